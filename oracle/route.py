@@ -49,8 +49,9 @@ class RouteResult:
 
 
 def router_logits(x, w_router, bias=None, score="softmax"):
-    """L = x W_r in fp64; softmax scoring adds the bias into the logit itself."""
-    L = _f64(x) @ _f64(w_router)
+    """L = x W_r^T in fp64 (W_r stored [E, h], one row per expert); softmax scoring adds
+    the bias into the logit itself."""
+    L = _f64(x) @ _f64(w_router).T
     if score == "softmax" and bias is not None:
         L = L + _f64(bias)[None, :]
     return L

@@ -8,7 +8,7 @@ equally distributed) draws; a parity check always hands the oracle the very tens
 the GPU path consumed, copied to the host.
 
 Distributions (the second argument of N(., .) is a variance):
-  x ~ N(0, 1);  W_r ~ N(0, 1/h) in fp32;  expert weights ~ N(0, 1/fan_in);
+  x ~ N(0, 1);  W_r ~ N(0, 1/h) in fp32, stored [E, h];  expert weights ~ N(0, 1/fan_in);
   gauss bias ~ N(0, bias_var) in fp32;  zipf bias b_e = -s * ln(rank_e) with rank_e a
   seeded permutation of 1..E;  uniform keys ~ U(0, 1) in fp32.
 Activations and expert weights are rounded to the workload dtype by torch's cast
@@ -92,7 +92,7 @@ def make_inputs(cfg: MoEConfig, device="cpu", with_weights: bool = True,
         out["w_router"] = None
     else:
         out["x"] = _normal((cfg.T, cfg.h), 1.0, sub_seed(cfg.seed, "x"), device, dt)[:T].contiguous()
-        out["w_router"] = _normal((cfg.h, cfg.E), 1.0 / math.sqrt(cfg.h),
+        out["w_router"] = _normal((cfg.E, cfg.h), 1.0 / math.sqrt(cfg.h),
                                   sub_seed(cfg.seed, "w_router"), device, torch.float32)
     out["bias"] = make_bias(cfg, device)
     if with_weights and cfg.inter > 0:

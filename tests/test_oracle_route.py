@@ -146,13 +146,13 @@ def test_ids_ascending_and_distinct():
 def test_router_logits_triple_loop():
     rng = np.random.default_rng(5)
     x = rng.normal(size=(3, 4))
-    W = rng.normal(size=(4, 5))
+    W = rng.normal(size=(5, 4))          # [E, h]
     L = oracle.router_logits(x, W)
     for t in range(3):
         for e in range(5):
             s = 0.0
             for i in range(4):
-                s += x[t, i] * W[i, e]
+                s += x[t, i] * W[e, i]
             assert abs(L[t, e] - s) < 1e-12
 
 
