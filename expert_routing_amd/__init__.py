@@ -1,0 +1,220 @@
+"""Python binding of libmoe.so, the MI355X MoE-layer forward pass.
+
+Argument marshalling only: every function here takes torch tensors, passes their
+device pointers and the current HIP stream to the C ABI of include/moe.h under the same
+name, and raises MoeError on a non-zero status. All compute runs in the library's HIP
+kernels; there is no fallback. Importing this package fails loudly when the library has
+not been built (python -m expert_routing_amd.build).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m expert_routing_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+SCORE = {"softmax": 0, "sigmoid": 1}
+DTYPE = {"f32": 0, "bf16": 1}
+_TORCH_DTYPE = {0: torch.float32, 1: torch.bfloat16}
+
+
+class Problem(ctypes.Structure):
+    """Mirror of `moe_problem`."""
+    _fields_ = [
+        ("T", ctypes.c_int64),
+        ("h", ctypes.c_int32), ("E", ctypes.c_int32), ("K", ctypes.c_int32),
+        ("score", ctypes.c_int32),
+        ("renorm", ctypes.c_int32),
+        ("n_groups", ctypes.c_int32), ("topk_groups", ctypes.c_int32),
+        ("capacity_factor", ctypes.c_double),
+        ("pad_to_capacity", ctypes.c_int32),
+        ("n_ep", ctypes.c_int32), ("ep_rank", ctypes.c_int32),
+        ("inter", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
+        ("act_dtype", ctypes.c_int32),
+    ]
+
+    def __init__(self, T, h, E, K, score="softmax", renorm=True, n_groups=1, topk_groups=1,
+                 capacity_factor=0.0, pad=False, n_ep=1, ep_rank=0, inter=0, n_shared=0,
+                 shared_inter=0, dtype="bf16"):
+        super().__init__(int(T), int(h), int(E), int(K), SCORE[score], int(bool(renorm)),
+                         int(n_groups), int(topk_groups), float(capacity_factor), int(bool(pad)),
+                         int(n_ep), int(ep_rank), int(inter), int(n_shared), int(shared_inter),
+                         DTYPE[dtype])
+
+    @property
+    def torch_dtype(self):
+        return _TORCH_DTYPE[self.act_dtype]
+
+    @property
+    def E_local(self):
+        return self.E // self.n_ep
+
+
+class Tensors(ctypes.Structure):
+    """Mirror of `moe_tensors`."""
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "x", "w_router", "bias", "w13", "w2", "w13_sh", "w2_sh", "topk_ids", "topk_w",
+        "counts", "offsets", "dest_row", "row_src", "send_bytes", "n_dropped", "xp", "yp",
+        "y_sh", "y")]
+
+
+_P = ctypes.POINTER(Problem)
+_V = ctypes.c_void_p
+_SZ = ctypes.c_size_t
+
+
+def _sig(name, args, res=ctypes.c_int):
+    f = getattr(_lib, name)
+    f.argtypes = args
+    f.restype = res
+    return f
+
+
+_check_problem = _sig("moe_check_problem", [_P])
+_capacity = _sig("moe_capacity", [_P, ctypes.POINTER(ctypes.c_int64)])
+_max_rows = _sig("moe_max_rows", [_P, ctypes.POINTER(ctypes.c_int64)])
+_workspace_bytes = _sig("moe_workspace_bytes", [_P, ctypes.POINTER(ctypes.c_size_t)])
+_status_string = _sig("moe_status_string", [ctypes.c_int], ctypes.c_char_p)
+_route = _sig("moe_route", [_P, _V, _V, _V, _V, _V, _V, _SZ, _V])
+_select = _sig("moe_select", [_P, _V, _V, _V, _V, _V])
+_dispatch = _sig("moe_dispatch", [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _SZ, _V])
+_expert_ffn = _sig("moe_expert_ffn", [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _SZ, _V])
+_combine = _sig("moe_combine", [_P, _V, _V, _V, _V, _V, _V])
+_forward = _sig("moe_forward", [_P, ctypes.POINTER(Tensors), _V, _SZ, _V])
+
+EXPORTED = ["moe_check_problem", "moe_capacity", "moe_max_rows", "moe_workspace_bytes",
+            "moe_status_string", "moe_route", "moe_select", "moe_dispatch", "moe_expert_ffn",
+            "moe_combine", "moe_forward"]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+def status_string(status: int) -> str:
+    return _status_string(int(status)).decode()
+
+
+def _ok(status, where):
+    if status != 0:
+        raise MoeError(status, where)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _ws(ws):
+    return (None, 0) if ws is None else (ws.data_ptr(), ws.numel() * ws.element_size())
+
+
+def check_problem(p: Problem) -> int:
+    return _check_problem(ctypes.byref(p))
+
+
+def capacity(p: Problem) -> int:
+    v = ctypes.c_int64()
+    _ok(_capacity(ctypes.byref(p), ctypes.byref(v)), "moe_capacity")
+    return v.value
+
+
+def max_rows(p: Problem) -> int:
+    v = ctypes.c_int64()
+    _ok(_max_rows(ctypes.byref(p), ctypes.byref(v)), "moe_max_rows")
+    return v.value
+
+
+def workspace_bytes(p: Problem) -> int:
+    v = ctypes.c_size_t()
+    _ok(_workspace_bytes(ctypes.byref(p), ctypes.byref(v)), "moe_workspace_bytes")
+    return v.value
+
+
+def moe_route(p, x, w_router, bias, topk_ids, topk_w, ws, stream=None):
+    wp, wn = _ws(ws)
+    _ok(_route(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(topk_ids),
+               _ptr(topk_w), wp, wn, _stream(stream)), "moe_route")
+
+
+def moe_select(p, logits, bias, topk_ids, topk_w, stream=None):
+    _ok(_select(ctypes.byref(p), _ptr(logits), _ptr(bias), _ptr(topk_ids), _ptr(topk_w),
+                _stream(stream)), "moe_select")
+
+
+def moe_dispatch(p, x, topk_ids, counts, offsets, dest_row, row_src, send_bytes, n_dropped, xp,
+                 ws, stream=None):
+    wp, wn = _ws(ws)
+    _ok(_dispatch(ctypes.byref(p), _ptr(x), _ptr(topk_ids), _ptr(counts), _ptr(offsets),
+                  _ptr(dest_row), _ptr(row_src), _ptr(send_bytes), _ptr(n_dropped), _ptr(xp),
+                  wp, wn, _stream(stream)), "moe_dispatch")
+
+
+def moe_expert_ffn(p, xp, offsets, w13, w2, x, w13_sh, w2_sh, yp, y_sh, ws, stream=None):
+    wp, wn = _ws(ws)
+    _ok(_expert_ffn(ctypes.byref(p), _ptr(xp), _ptr(offsets), _ptr(w13), _ptr(w2), _ptr(x),
+                    _ptr(w13_sh), _ptr(w2_sh), _ptr(yp), _ptr(y_sh), wp, wn, _stream(stream)),
+        "moe_expert_ffn")
+
+
+def moe_combine(p, yp, dest_row, topk_w, y_sh, y, stream=None):
+    _ok(_combine(ctypes.byref(p), _ptr(yp), _ptr(dest_row), _ptr(topk_w), _ptr(y_sh), _ptr(y),
+                 _stream(stream)), "moe_combine")
+
+
+def moe_forward(p, t: dict, ws, stream=None):
+    ts = Tensors(**{k: _ptr(t.get(k)) for k, _ in Tensors._fields_})
+    wp, wn = _ws(ws)
+    _ok(_forward(ctypes.byref(p), ctypes.byref(ts), wp, wn, _stream(stream)), "moe_forward")
+
+
+def alloc_buffers(p: Problem, device="cuda", send=True) -> dict:
+    """Output and intermediate buffers of one layer call, plus its workspace."""
+    T, K, E, El, h = p.T, p.K, p.E, p.E_local, p.h
+    R = max_rows(p)
+    dt = p.torch_dtype
+    i32 = torch.int32
+    b = {
+        "topk_ids": torch.empty((T, K), dtype=i32, device=device),
+        "topk_w": torch.empty((T, K), dtype=torch.float32, device=device),
+        "counts": torch.empty((E,), dtype=i32, device=device),
+        "offsets": torch.empty((El + 1,), dtype=i32, device=device),
+        "dest_row": torch.empty((T, K), dtype=i32, device=device),
+        "row_src": torch.empty((max(R, 1),), dtype=i32, device=device),
+        "send_bytes": (torch.empty((p.n_ep, p.n_ep), dtype=torch.int64, device=device)
+                       if send and T % p.n_ep == 0 else None),
+        "n_dropped": torch.empty((1,), dtype=i32, device=device),
+        "xp": torch.empty((max(R, 1), h), dtype=dt, device=device),
+        "yp": torch.empty((max(R, 1), h), dtype=dt, device=device),
+        "y_sh": (torch.empty((T // p.n_ep, h), dtype=dt, device=device) if p.n_shared else None),
+        "y": torch.empty((T, h), dtype=dt, device=device),
+    }
+    nbytes = workspace_bytes(p)
+    b["ws"] = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=device)
+    return b
+
+
+def problem_from_config(cfg, T=None) -> Problem:
+    """Problem for a workload description with the fields of synth.MoEConfig."""
+    return Problem(T=cfg.T if T is None else T, h=cfg.h, E=cfg.E, K=cfg.K, score=cfg.score,
+                   renorm=cfg.renorm, n_groups=cfg.n_groups, topk_groups=cfg.topk_groups,
+                   capacity_factor=cfg.capacity_factor, pad=cfg.pad, n_ep=cfg.n_ep,
+                   ep_rank=cfg.ep_rank, inter=cfg.inter, n_shared=cfg.n_shared,
+                   shared_inter=cfg.shared_inter, dtype=cfg.dtype)

@@ -1,0 +1,293 @@
+// C ABI: validation, sizing and the five stage entry points. Host code only; the
+// kernels live in route.hip, dispatch.hip, ffn.hip and combine.hip.
+#include <math.h>
+#include <string.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static bool cap_exact(double cf, int64_t T, int K, int E, int64_t* cap) {
+  // cap = ceil(cf * T * K / E) on the exact binary value of cf.
+  if (!(cf > 0.0)) { *cap = -1; return true; }
+  if (!isfinite(cf)) return false;
+  int e2 = 0;
+  double f = frexp(cf, &e2);                       // cf = f * 2^e2, f in [0.5, 1)
+  int64_t m = (int64_t)ldexp(f, 53);               // exact 53-bit integer
+  int sh = e2 - 53;                                 // cf = m * 2^sh
+  unsigned __int128 num = (unsigned __int128)m * (unsigned __int128)T * (unsigned __int128)K;
+  unsigned __int128 den = (unsigned __int128)E;
+  if (sh >= 0) {
+    if (sh > 20) return false;                     // cf >= 2^73: no meaningful cap
+    num <<= sh;                                    // num < 2^108
+  } else {
+    const int r = -sh;
+    // num < 2^88 (m < 2^53, T*K < 2^31, + 2^4 slack); E*2^r < 2^120 for r <= 110
+    if (r > 110) { *cap = (num == 0) ? 0 : 1; return true; }
+    den <<= r;
+  }
+  unsigned __int128 c = (num + den - 1) / den;
+  if (c > (unsigned __int128)INT64_MAX) return false;
+  *cap = (int64_t)c;
+  return true;
+}
+
+int make_dims(const moe_problem* p, Dims* d) {
+  if (!p) return MOE_ERR_INVALID;
+  if (p->T < 0 || p->h <= 0 || p->E < 1 || p->E > 512) return MOE_ERR_INVALID;
+  if (p->K < 1 || p->K > p->E || p->K > 16) return MOE_ERR_INVALID;
+  if (p->score != MOE_SCORE_SOFTMAX && p->score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID;
+  if (p->renorm != 0 && p->renorm != 1) return MOE_ERR_INVALID;
+  if (p->n_ep < 1 || p->E % p->n_ep != 0) return MOE_ERR_INVALID;
+  if (p->ep_rank < 0 || p->ep_rank >= p->n_ep) return MOE_ERR_INVALID;
+  if (p->n_groups < 1 || p->E % p->n_groups != 0) return MOE_ERR_INVALID;
+  if (p->topk_groups < 1 || p->topk_groups > p->n_groups) return MOE_ERR_INVALID;
+  if ((int64_t)p->topk_groups * (p->E / p->n_groups) < p->K) return MOE_ERR_INVALID;
+  if (p->act_dtype != MOE_DTYPE_F32 && p->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID;
+  if (p->n_shared != 0 && p->n_shared != 1) return MOE_ERR_INVALID;
+  if (p->inter < 0 || p->shared_inter < 0) return MOE_ERR_INVALID;
+  if (p->n_shared == 1 && (p->shared_inter <= 0 || p->T % p->n_ep != 0)) return MOE_ERR_INVALID;
+  if (p->pad_to_capacity != 0 && p->pad_to_capacity != 1) return MOE_ERR_INVALID;
+  int64_t cap = -1;
+  if (!cap_exact(p->capacity_factor, p->T, p->K, p->E, &cap)) return MOE_ERR_UNSUPPORTED;
+  if (p->pad_to_capacity && cap < 0) return MOE_ERR_INVALID;
+  const bool bf16 = p->act_dtype == MOE_DTYPE_BF16;
+  if (bf16) {
+    if (p->h % 64 != 0 || p->inter % 64 != 0 || p->shared_inter % 64 != 0)
+      return MOE_ERR_UNSUPPORTED;
+  } else {
+    if (p->h % 4 != 0) return MOE_ERR_UNSUPPORTED;
+  }
+  if (p->T * (int64_t)p->K >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  if (p->n_ep > 1024) return MOE_ERR_UNSUPPORTED;
+  d->T = p->T; d->h = p->h; d->E = p->E; d->K = p->K;
+  d->N = p->n_ep; d->rank = p->ep_rank;
+  d->El = p->E / p->n_ep; d->e0 = p->ep_rank * d->El;
+  d->cap = cap;
+  const int64_t per_tok = p->K < d->El ? p->K : d->El;
+  int64_t rmax = p->T * per_tok;
+  if (cap >= 0) {
+    const int64_t capped = (int64_t)d->El * cap;
+    rmax = p->pad_to_capacity ? capped : (capped < rmax ? capped : rmax);
+  }
+  if (rmax >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  d->R_max = rmax;
+  d->tpr = (p->T % p->n_ep == 0) ? p->T / p->n_ep : 0;
+  d->sh_rows = p->n_shared ? d->tpr : 0;
+  d->s = bf16 ? 2 : 4;
+  d->bf16 = bf16;
+  return MOE_OK;
+}
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const moe_problem* p, const Dims& d) {
+  WsLayout L;
+  size_t off = 0;
+  const size_t n_chunks = (size_t)((d.T + kDispatchChunk - 1) / kDispatchChunk);
+  L.logits = off;       off = align256(off + (size_t)d.T * d.E * 4);
+  L.chunk_counts = off; off = align256(off + n_chunks * d.E * 4);
+  L.chunk_base = off;   off = align256(off + n_chunks * d.E * 4);
+  L.kept = off;         off = align256(off + (size_t)d.E * 4);
+  L.sched = off;        off = align256(off + ffn_sched_bytes(d));
+  const int imax = p->inter > p->shared_inter ? p->inter : p->shared_inter;
+  L.hbuf = off;         off = align256(off + (size_t)(d.R_max + d.sh_rows) * imax * d.s);
+  L.total = off;
+  return L;
+}
+
+static int check_ws(const moe_problem* p, const Dims& d, void* ws, size_t ws_bytes) {
+  if (!ws || ((uintptr_t)ws & 255)) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < ws_layout(p, d).total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_check_problem(const moe_problem* p) {
+  Dims d;
+  return make_dims(p, &d);
+}
+
+int moe_capacity(const moe_problem* p, int64_t* cap) {
+  Dims d;
+  int st = make_dims(p, &d);
+  if (st != MOE_OK) return st;
+  if (!cap) return MOE_ERR_INVALID;
+  *cap = d.cap;
+  return MOE_OK;
+}
+
+int moe_max_rows(const moe_problem* p, int64_t* rows) {
+  Dims d;
+  int st = make_dims(p, &d);
+  if (st != MOE_OK) return st;
+  if (!rows) return MOE_ERR_INVALID;
+  *rows = d.R_max;
+  return MOE_OK;
+}
+
+int moe_workspace_bytes(const moe_problem* p, size_t* bytes) {
+  Dims d;
+  int st = make_dims(p, &d);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID;
+  *bytes = ws_layout(p, d).total;
+  return MOE_OK;
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+    case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"
+
+// Argument checks of each stage (host only, nothing enqueued).
+namespace moe {
+static int v_route(const moe_problem* p, const Dims& d, const void* x, const float* w_router,
+                   const int32_t* ids, const float* w, void* ws, size_t ws_bytes) {
+  if (d.T == 0) return MOE_OK;
+  if (!x || !w_router || !ids || !w) return MOE_ERR_INVALID;
+  return check_ws(p, d, ws, ws_bytes);
+}
+static int v_dispatch(const moe_problem* p, const Dims& d, const void* x, const int32_t* ids,
+                      const int32_t* counts, const int32_t* offsets, const int32_t* dest_row,
+                      const int32_t* row_src, const int64_t* send_bytes, const int32_t* n_dropped,
+                      const void* xp, void* ws, size_t ws_bytes) {
+  if (!counts || !offsets || !n_dropped) return MOE_ERR_INVALID;
+  if (d.T > 0 && (!ids || !dest_row)) return MOE_ERR_INVALID;
+  if (d.R_max > 0 && !row_src) return MOE_ERR_INVALID;
+  if ((x == nullptr) != (xp == nullptr)) return MOE_ERR_INVALID;
+  if (send_bytes && d.tpr == 0 && d.T > 0) return MOE_ERR_INVALID;
+  return check_ws(p, d, ws, ws_bytes);
+}
+static int v_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_t* offsets,
+                 const void* w13, const void* w2, const void* x, const void* w13_sh,
+                 const void* w2_sh, const void* yp, const void* y_sh, void* ws, size_t ws_bytes) {
+  if (p->inter <= 0) return MOE_ERR_INVALID;
+  if (!offsets || !w13 || !w2) return MOE_ERR_INVALID;
+  if (d.R_max > 0 && (!xp || !yp)) return MOE_ERR_INVALID;
+  if (p->n_shared) {
+    if (d.sh_rows > 0 && (!x || !w13_sh || !w2_sh || !y_sh)) return MOE_ERR_INVALID;
+  } else if (w13_sh || w2_sh || y_sh) {
+    return MOE_ERR_INVALID;
+  }
+  return check_ws(p, d, ws, ws_bytes);
+}
+static int v_combine(const moe_problem* p, const Dims& d, const void* yp, const int32_t* dest_row,
+                     const float* w, const void* y_sh, const void* y) {
+  if (d.T == 0) return MOE_OK;
+  if (!dest_row || !w || !y) return MOE_ERR_INVALID;
+  if (d.R_max > 0 && !yp) return MOE_ERR_INVALID;
+  if (y_sh && !p->n_shared) return MOE_ERR_INVALID;
+  if (p->n_shared && d.sh_rows > 0 && !y_sh) return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+}  // namespace moe
+
+extern "C" {
+
+int moe_route(const moe_problem* p, const void* x, const float* w_router, const float* bias,
+              int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = make_dims(p, &d);
+  if (st != MOE_OK) return st;
+  if ((st = v_route(p, d, x, w_router, topk_ids, topk_w, ws, ws_bytes)) != MOE_OK) return st;
+  if (d.T == 0) return MOE_OK;
+  WsLayout L = ws_layout(p, d);
+  return launch_route(p, d, x, w_router, bias, topk_ids, topk_w,
+                      (float*)((char*)ws + L.logits), (hipStream_t)stream);
+}
+
+int moe_select(const moe_problem* p, const float* logits, const float* bias,
+               int32_t* topk_ids, float* topk_w, void* stream) {
+  Dims d;
+  int st = make_dims(p, &d);
+  if (st != MOE_OK) return st;
+  if (d.T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID;
+  return launch_select(p, d, logits, bias, topk_ids, topk_w, (hipStream_t)stream);
+}
+
+int moe_dispatch(const moe_problem* p, const void* x, const int32_t* topk_ids,
+                 int32_t* counts, int32_t* offsets, int32_t* dest_row, int32_t* row_src,
+                 int64_t* send_bytes, int32_t* n_dropped, void* xp,
+                 void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = make_dims(p, &d);
+  if (st != MOE_OK) return st;
+  if ((st = v_dispatch(p, d, x, topk_ids, counts, offsets, dest_row, row_src, send_bytes,
+                       n_dropped, xp, ws, ws_bytes)) != MOE_OK)
+    return st;
+  WsLayout L = ws_layout(p, d);
+  return launch_dispatch(p, d, x, topk_ids, counts, offsets, dest_row, row_src, send_bytes,
+                         n_dropped, xp, (char*)ws, L, (hipStream_t)stream);
+}
+
+int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* offsets,
+                   const void* w13, const void* w2, const void* x, const void* w13_sh,
+                   const void* w2_sh, void* yp, void* y_sh,
+                   void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = make_dims(p, &d);
+  if (st != MOE_OK) return st;
+  if ((st = v_ffn(p, d, xp, offsets, w13, w2, x, w13_sh, w2_sh, yp, y_sh, ws, ws_bytes)) != MOE_OK)
+    return st;
+  WsLayout L = ws_layout(p, d);
+  return launch_ffn(p, d, xp, offsets, w13, w2, x, w13_sh, w2_sh, yp, y_sh, (char*)ws, L,
+                    (hipStream_t)stream);
+}
+
+int moe_combine(const moe_problem* p, const void* yp, const int32_t* dest_row,
+                const float* topk_w, const void* y_sh, void* y, void* stream) {
+  Dims d;
+  int st = make_dims(p, &d);
+  if (st != MOE_OK) return st;
+  if ((st = v_combine(p, d, yp, dest_row, topk_w, y_sh, y)) != MOE_OK) return st;
+  if (d.T == 0) return MOE_OK;
+  return launch_combine(p, d, yp, dest_row, topk_w, y_sh, y, (hipStream_t)stream);
+}
+
+int moe_forward(const moe_problem* p, const moe_tensors* t, void* ws, size_t ws_bytes,
+                void* stream) {
+  if (!t) return MOE_ERR_INVALID;
+  Dims d;
+  int st = make_dims(p, &d);
+  if (st != MOE_OK) return st;
+  if (p->inter <= 0 || (d.T > 0 && !t->x)) return MOE_ERR_INVALID;
+  // Check every stage before the first launch, so an error enqueues nothing.
+  if ((st = v_route(p, d, t->x, t->w_router, t->topk_ids, t->topk_w, ws, ws_bytes)) != MOE_OK ||
+      (st = v_dispatch(p, d, t->x, t->topk_ids, t->counts, t->offsets, t->dest_row, t->row_src,
+                       t->send_bytes, t->n_dropped, t->xp, ws, ws_bytes)) != MOE_OK ||
+      (st = v_ffn(p, d, t->xp, t->offsets, t->w13, t->w2, t->x, t->w13_sh, t->w2_sh, t->yp,
+                  t->y_sh, ws, ws_bytes)) != MOE_OK ||
+      (st = v_combine(p, d, t->yp, t->dest_row, t->topk_w, t->y_sh, t->y)) != MOE_OK)
+    return st;
+  const hipStream_t s = (hipStream_t)stream;
+  const WsLayout L = ws_layout(p, d);
+  char* w = (char*)ws;
+  if (d.T > 0 && (st = launch_route(p, d, t->x, t->w_router, t->bias, t->topk_ids, t->topk_w,
+                                    (float*)(w + L.logits), s)) != MOE_OK)
+    return st;
+  if ((st = launch_dispatch(p, d, t->x, t->topk_ids, t->counts, t->offsets, t->dest_row,
+                            t->row_src, t->send_bytes, t->n_dropped, t->xp, w, L, s)) != MOE_OK)
+    return st;
+  if ((st = launch_ffn(p, d, t->xp, t->offsets, t->w13, t->w2, t->x, t->w13_sh, t->w2_sh, t->yp,
+                       t->y_sh, w, L, s)) != MOE_OK)
+    return st;
+  if (d.T > 0) return launch_combine(p, d, t->yp, t->dest_row, t->topk_w, t->y_sh, t->y, s);
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,449 @@
+// Expert FFN as two grouped GEMMs over the ragged per-expert row blocks:
+//   GEMM1 (gated):  H[r] = silu(A[r] W_g^T) * (A[r] W_u^T)      -> hbuf (act dtype)
+//   GEMM2 (down):   Y[r] = H[r] W_d^T                             -> yp / y_sh
+// Groups are the local experts (rows from `offsets`, read on the device) plus the
+// optional shared expert over this rank's token block. A one-block prep kernel turns
+// the offsets into a tile table; every GEMM block finds its (group, n-tile, m-tile) by
+// binary search, so the host never waits for the routing result.
+//
+// bf16 path: 256 threads (4 waves), MFMA 32x32x16 bf16 with fp32 accumulators, LDS
+// double buffering with register prefetch of the next K slice, XOR-swizzled LDS rows,
+// an LDS-staged epilogue for 16-byte coalesced stores, and an XCD-aware block order
+// (consecutive tiles of one expert land on one XCD's L2).
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int G_MAX = 513;       // local experts (<= 512) + shared expert
+constexpr int G_PAD = 520;
+
+struct FfnGroup {
+  const void* A1;  // [rows][h]
+  const void* B1;  // [2*inter][h]
+  void* C1;        // [rows][inter]  (hbuf)
+  const void* B2;  // [h][inter]
+  void* C2;        // [rows][h]
+  int rows;
+  int inter;
+};
+
+struct FfnSched {
+  int n_groups;
+  int total1;
+  int total2;
+  int pad_;
+  int start1[G_PAD];
+  int start2[G_PAD];
+  FfnGroup g[G_MAX];
+};
+
+// One block of 1024 threads.
+__global__ __launch_bounds__(1024) void ffn_prep(FfnSched* __restrict__ sc,
+                                                 const int32_t* __restrict__ offsets,
+                                                 const char* xp, const char* w13, const char* w2,
+                                                 const char* x, const char* w13_sh,
+                                                 const char* w2_sh, char* hbuf, char* yp,
+                                                 char* y_sh, int El, int has_shared,
+                                                 int64_t sh_rows, int64_t sh_t0, int h, int inter,
+                                                 int sh_inter, int64_t R_max, int s, int BM,
+                                                 int BN1, int BN2) {
+  __shared__ int s1[1024], s2[1024];
+  const int g = threadIdx.x;
+  const int G = El + has_shared;
+  int t1 = 0, t2 = 0;
+  if (g < G) {
+    FfnGroup fg;
+    int rows, I;
+    if (g < El) {
+      const int r0 = offsets[g];
+      rows = offsets[g + 1] - r0;
+      I = inter;
+      fg.A1 = xp + (size_t)r0 * h * s;
+      fg.B1 = w13 + (size_t)g * 2 * inter * h * s;
+      fg.C1 = hbuf + (size_t)r0 * inter * s;
+      fg.B2 = w2 + (size_t)g * h * inter * s;
+      fg.C2 = yp + (size_t)r0 * h * s;
+    } else {
+      rows = (int)sh_rows;
+      I = sh_inter;
+      fg.A1 = x + (size_t)sh_t0 * h * s;
+      fg.B1 = w13_sh;
+      fg.C1 = hbuf + (size_t)R_max * inter * s;
+      fg.B2 = w2_sh;
+      fg.C2 = y_sh;
+    }
+    fg.rows = rows;
+    fg.inter = I;
+    sc->g[g] = fg;
+    const int mt = (rows + BM - 1) / BM;
+    t1 = mt * ((I + BN1 - 1) / BN1);
+    t2 = mt * ((h + BN2 - 1) / BN2);
+  }
+  s1[g] = t1;
+  s2[g] = t2;
+  __syncthreads();
+  for (int st = 1; st < 1024; st <<= 1) {
+    const int a1 = g >= st ? s1[g - st] : 0;
+    const int a2 = g >= st ? s2[g - st] : 0;
+    __syncthreads();
+    s1[g] += a1;
+    s2[g] += a2;
+    __syncthreads();
+  }
+  if (g <= G) {
+    sc->start1[g] = g == 0 ? 0 : s1[g - 1];
+    sc->start2[g] = g == 0 ? 0 : s2[g - 1];
+  }
+  if (g == 0) {
+    sc->n_groups = G;
+    sc->total1 = s1[G - 1];
+    sc->total2 = s2[G - 1];
+  }
+}
+
+// Tile lookup shared by the GEMM kernels. Returns false for blocks with no tile.
+__device__ __forceinline__ bool find_tile(const FfnSched* sc, bool first, int BM, int& g,
+                                          int& m_tile, int& n_tile) {
+  const int total = first ? sc->total1 : sc->total2;
+  const int* start = first ? sc->start1 : sc->start2;
+  const int per = (total + kNumXcd - 1) / kNumXcd;
+  const int xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
+  if (slot >= per) return false;
+  const int L = xcd * per + slot;
+  if (L >= total) return false;
+  int lo = 0, hi = sc->n_groups;          // start[lo] <= L < start[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (start[mid] <= L) lo = mid; else hi = mid;
+  }
+  g = lo;
+  const int rows = sc->g[g].rows;
+  const int mt = (rows + BM - 1) / BM;
+  const int local = L - start[g];
+  m_tile = local % mt;
+  n_tile = local / mt;
+  return true;
+}
+
+__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+
+__device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
+
+// bf16 grouped GEMM. Tile BM x BN (BN counts B rows: for GATED half gate, half up),
+// BK = 64, waves WM x WN.
+template <int BM, int BN, int WM, int WN, bool GATED>
+__global__ __launch_bounds__(256) void ffn_gemm_bf16(const FfnSched* __restrict__ sc, int h) {
+  static_assert(WM * WN == 4, "4 waves");
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  static_assert(TM >= 1 && TN >= 1, "tile");
+  static_assert(!GATED || TN % 2 == 0, "gated needs gate/up pairs");
+  constexpr int BNO = GATED ? BN / 2 : BN;          // output columns per tile
+  constexpr int A_CH = BM * 8 / 256, B_CH = BN * 8 / 256;
+  extern __shared__ uint4 smem[];
+  uint4* As = smem;                 // [2][BM*8]
+  uint4* Bs = smem + 2 * BM * 8;    // [2][BN*8]
+
+  int g, m_tile, n_tile;
+  if (!find_tile(sc, GATED, BM, g, m_tile, n_tile)) return;
+  const FfnGroup fg = sc->g[g];
+  const int rows = fg.rows, I = fg.inter;
+  const bf16_t* A = static_cast<const bf16_t*>(GATED ? fg.A1 : fg.C1);
+  const bf16_t* B = static_cast<const bf16_t*>(GATED ? fg.B1 : fg.B2);
+  bf16_t* C = static_cast<bf16_t*>(GATED ? fg.C1 : fg.C2);
+  const int Kd = GATED ? h : I;         // reduction length = lda = ldb
+  const int Nout = GATED ? I : h;       // output columns = ldc
+  const int m0 = m_tile * BM, n0 = n_tile * BNO;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  // Global source rows of this thread's chunks (clamped into valid memory).
+  const bf16_t* a_src[A_CH];
+  const bf16_t* b_src[B_CH];
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    const int id = tid + i * 256, r = id >> 3, c = id & 7;
+    const int gr = m0 + r < rows ? m0 + r : rows - 1;
+    a_src[i] = A + (size_t)gr * Kd + c * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    const int id = tid + i * 256, r = id >> 3, c = id & 7;
+    int wrow;
+    if (GATED) {
+      const int half = r >= BN / 2;
+      int col = n0 + (half ? r - BN / 2 : r);
+      col = col < I ? col : I - 1;
+      wrow = col + (half ? I : 0);
+    } else {
+      const int col = n0 + r;
+      wrow = col < Nout ? col : Nout - 1;
+    }
+    b_src[i] = B + (size_t)wrow * Kd + c * 8;
+  }
+
+  floatx16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  uint4 ra[A_CH], rb[B_CH];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + k0);
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + k0);
+  };
+  auto lstore = [&](int buf) {
+    uint4* as = As + buf * BM * 8;
+    uint4* bs = Bs + buf * BN * 8;
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int id = tid + i * 256;
+      as[swz(id >> 3, id & 7)] = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      const int id = tid + i * 256;
+      bs[swz(id >> 3, id & 7)] = rb[i];
+    }
+  };
+  // B-tile row of col-tile j of this wave
+  auto brow = [&](int j) {
+    if (GATED) {
+      return j < TN / 2 ? wn * (WTN / 2) + j * 32 : BN / 2 + wn * (WTN / 2) + (j - TN / 2) * 32;
+    }
+    return wn * WTN + j * 32;
+  };
+
+  const int nk = Kd / 64;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * 64);
+    const uint4* as = As + cur * BM * 8;
+    const uint4* bs = Bs + cur * BN * 8;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int c = kk * 2 + (lane >> 5);
+      bf16x8_t af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = __builtin_bit_cast(bf16x8_t, as[swz(wm * WTM + i * 32 + (lane & 31), c)]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bfr[j] = __builtin_bit_cast(bf16x8_t, bs[swz(brow(j) + (lane & 31), c)]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: stage the bf16 tile in LDS, then 16-byte stores.
+  constexpr int PITCH = BNO * 2 + 16;                  // bytes per staged row
+  char* stage = reinterpret_cast<char*>(smem);
+  constexpr int TNO = GATED ? TN / 2 : TN;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TNO; ++j) {
+      const int col = (GATED ? wn * (WTN / 2) : wn * WTN) + j * 32 + (lane & 31);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int row = wm * WTM + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        float v = GATED ? silu(acc[i][j][q]) * acc[i][j + TN / 2][q] : acc[i][j][q];
+        *reinterpret_cast<bf16_t*>(stage + row * PITCH + col * 2) = f32_to_bf16(v);
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int RCH = BNO / 8;                         // 16-byte chunks per row
+  for (int id = tid; id < BM * RCH; id += 256) {
+    const int r = id / RCH, cc = id % RCH;
+    const int gr = m0 + r, gc = n0 + cc * 8;
+    if (gr < rows && gc < Nout)
+      *reinterpret_cast<uint4*>(C + (size_t)gr * Nout + gc) =
+          *reinterpret_cast<const uint4*>(stage + r * PITCH + cc * 16);
+  }
+}
+
+template <int BM, int BN, bool GATED>
+constexpr size_t bf16_lds_bytes() {
+  constexpr size_t ops = 2 * (size_t)(BM + BN) * 8 * 16;
+  constexpr size_t stg = (size_t)BM * ((GATED ? BN / 2 : BN) * 2 + 16);
+  return ops > stg ? ops : stg;
+}
+
+// fp32 grouped GEMM: 64 x 64 tiles (gated: 32 gate + 32 up columns), 4x4 per thread.
+constexpr int F_BM = 64, F_BN = 64, F_BK = 16;
+template <bool GATED>
+__global__ __launch_bounds__(256) void ffn_gemm_f32(const FfnSched* __restrict__ sc, int h) {
+  __shared__ float As[F_BK][F_BM + 4];
+  __shared__ float Bs[F_BK][F_BN + 4];
+  int g, m_tile, n_tile;
+  if (!find_tile(sc, GATED, F_BM, g, m_tile, n_tile)) return;
+  const FfnGroup fg = sc->g[g];
+  const int rows = fg.rows, I = fg.inter;
+  const float* A = static_cast<const float*>(GATED ? fg.A1 : fg.C1);
+  const float* B = static_cast<const float*>(GATED ? fg.B1 : fg.B2);
+  float* C = static_cast<float*>(GATED ? fg.C1 : fg.C2);
+  const int Kd = GATED ? h : I;
+  const int Nout = GATED ? I : h;
+  constexpr int BNO = GATED ? F_BN / 2 : F_BN;
+  const int m0 = m_tile * F_BM, n0 = n_tile * BNO;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < Kd; k0 += F_BK) {
+    for (int id = tid; id < F_BM * F_BK; id += 256) {
+      const int r = id / F_BK, k = id % F_BK, kk = k0 + k;
+      const int gr = m0 + r;
+      As[k][r] = (gr < rows && kk < Kd) ? A[(size_t)gr * Kd + kk] : 0.f;
+      int wrow = -1;
+      if (GATED) {
+        const int half = r >= F_BN / 2;
+        const int col = n0 + (half ? r - F_BN / 2 : r);
+        if (col < I) wrow = col + (half ? I : 0);
+      } else {
+        const int col = n0 + r;
+        if (col < Nout) wrow = col;
+      }
+      Bs[k][r] = (wrow >= 0 && kk < Kd) ? B[(size_t)wrow * Kd + kk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < F_BK; ++k) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[k][ty * 4 + i];
+      if (GATED) {
+        b[0] = Bs[k][tx * 2]; b[1] = Bs[k][tx * 2 + 1];
+        b[2] = Bs[k][F_BN / 2 + tx * 2]; b[3] = Bs[k][F_BN / 2 + tx * 2 + 1];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = Bs[k][tx * 4 + j];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int gr = m0 + ty * 4 + i;
+    if (gr >= rows) continue;
+    if (GATED) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int gc = n0 + tx * 2 + j;
+        if (gc < Nout) C[(size_t)gr * Nout + gc] = silu(acc[i][j]) * acc[i][j + 2];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int gc = n0 + tx * 4 + j;
+        if (gc < Nout) C[(size_t)gr * Nout + gc] = acc[i][j];
+      }
+    }
+  }
+}
+
+// Tile shapes chosen from the expected rows per local expert, T*K/E.
+enum class Tiles { Large, Medium, Small };
+
+template <int BM, int BN, int WM, int WN, bool GATED>
+bool launch_bf16(const FfnSched* sc, int h, int64_t tiles_ub, hipStream_t st) {
+  constexpr size_t lds = bf16_lds_bytes<BM, BN, GATED>();
+  static bool attr_set = false;   // same value for every call and device
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_gemm_bf16<BM, BN, WM, WN, GATED>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return false;
+    attr_set = true;
+  }
+  const int64_t grid = (tiles_ub + kNumXcd - 1) / kNumXcd * kNumXcd;
+  if (grid <= 0) return true;
+  hipLaunchKernelGGL((ffn_gemm_bf16<BM, BN, WM, WN, GATED>), dim3((unsigned)grid), dim3(256),
+                     lds, st, sc, h);
+  return hipGetLastError() == hipSuccess;
+}
+
+}  // namespace
+
+size_t ffn_sched_bytes(const Dims&) { return sizeof(FfnSched); }
+
+int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_t* offsets,
+               const void* w13, const void* w2, const void* x, const void* w13_sh,
+               const void* w2_sh, void* yp, void* y_sh, char* ws, const WsLayout& L,
+               hipStream_t st) {
+  FfnSched* sc = reinterpret_cast<FfnSched*>(ws + L.sched);
+  const int has_sh = (p->n_shared && d.sh_rows > 0) ? 1 : 0;
+  const int64_t sh_t0 = (int64_t)d.rank * d.tpr;
+  Tiles tiles = Tiles::Large;
+  int BM, BN1, BN2;
+  if (d.bf16) {
+    const double per_expert = d.E > 0 ? (double)d.T * d.K / d.E : 0.0;
+    tiles = per_expert >= 384 ? Tiles::Large : (per_expert >= 48 ? Tiles::Medium : Tiles::Small);
+    BM = tiles == Tiles::Large ? 256 : (tiles == Tiles::Medium ? 128 : 32);
+    BN1 = 128;   // output columns of the gated tile (256 B rows: 128 gate + 128 up)
+    BN2 = 256;
+  } else {
+    BM = F_BM; BN1 = F_BN / 2; BN2 = F_BN;
+  }
+  hipLaunchKernelGGL(ffn_prep, dim3(1), dim3(1024), 0, st, sc, offsets,
+                     static_cast<const char*>(xp), static_cast<const char*>(w13),
+                     static_cast<const char*>(w2), static_cast<const char*>(x),
+                     static_cast<const char*>(w13_sh), static_cast<const char*>(w2_sh),
+                     ws + L.hbuf, static_cast<char*>(yp), static_cast<char*>(y_sh), d.El, has_sh,
+                     d.sh_rows, sh_t0, d.h, p->inter, p->shared_inter, d.R_max, d.s, BM, BN1,
+                     BN2);
+  if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
+  // Upper bound on m-tiles: sum_e ceil(rows_e / BM) <= R_max / BM + E_l.
+  const int64_t mt_ub = d.R_max / BM + d.El;
+  const int64_t mt_sh = has_sh ? (d.sh_rows + BM - 1) / BM : 0;
+  const int64_t nt1 = (p->inter + BN1 - 1) / BN1;
+  const int64_t nt1s = has_sh ? (p->shared_inter + BN1 - 1) / BN1 : 0;
+  const int64_t nt2 = (d.h + BN2 - 1) / BN2;
+  const int64_t ub1 = mt_ub * nt1 + mt_sh * nt1s;
+  const int64_t ub2 = (mt_ub + mt_sh) * nt2;
+  bool ok = true;
+  if (d.bf16) {
+    switch (tiles) {
+      case Tiles::Large:
+        ok = launch_bf16<256, 256, 2, 2, true>(sc, d.h, ub1, st) &&
+             launch_bf16<256, 256, 2, 2, false>(sc, d.h, ub2, st);
+        break;
+      case Tiles::Medium:
+        ok = launch_bf16<128, 256, 2, 2, true>(sc, d.h, ub1, st) &&
+             launch_bf16<128, 256, 2, 2, false>(sc, d.h, ub2, st);
+        break;
+      case Tiles::Small:
+        ok = launch_bf16<32, 256, 1, 4, true>(sc, d.h, ub1, st) &&
+             launch_bf16<32, 256, 1, 4, false>(sc, d.h, ub2, st);
+        break;
+    }
+  } else {
+    const int64_t g1 = (ub1 + kNumXcd - 1) / kNumXcd * kNumXcd;
+    const int64_t g2 = (ub2 + kNumXcd - 1) / kNumXcd * kNumXcd;
+    if (g1 > 0)
+      hipLaunchKernelGGL(ffn_gemm_f32<true>, dim3((unsigned)g1), dim3(256), 0, st, sc, d.h);
+    if (g2 > 0)
+      hipLaunchKernelGGL(ffn_gemm_f32<false>, dim3((unsigned)g2), dim3(256), 0, st, sc, d.h);
+    ok = hipGetLastError() == hipSuccess;
+  }
+  return ok ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+}  // namespace moe

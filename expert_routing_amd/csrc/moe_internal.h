@@ -1,0 +1,76 @@
+// Internal declarations shared by the library's HIP sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // raw bf16 storage
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr int kDispatchChunk = 256; // tokens per dispatch block
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// Derived sizes of a validated problem (host side).
+struct Dims {
+  int64_t T;
+  int h, E, K, El, e0, N, rank;
+  int64_t cap;      // -1: no limit
+  int64_t R_max;    // rows of the local buffer
+  int64_t tpr;      // tokens per virtual rank (T / N), 0 when T % N != 0
+  int64_t sh_rows;  // shared-expert rows (T/N or 0)
+  int s;            // activation bytes
+  bool bf16;
+};
+
+// Workspace carve-up (byte offsets from ws, each 256-aligned).
+struct WsLayout {
+  size_t logits;        // [T][E] f32
+  size_t chunk_counts;  // [n_chunks][E] i32
+  size_t chunk_base;    // [n_chunks][E] i32
+  size_t kept;          // [E_l] i32
+  size_t sched;         // ffn tile schedule
+  size_t hbuf;          // [R_max + sh_rows][I_max] act
+  size_t total;
+};
+
+int make_dims(const moe_problem* p, Dims* d);
+WsLayout ws_layout(const moe_problem* p, const Dims& d);
+
+// Stage launchers (arguments already validated; return MOE_OK or MOE_ERR_LAUNCH).
+int launch_route(const moe_problem* p, const Dims& d, const void* x, const float* w_router,
+                 const float* bias, int32_t* ids, float* w, float* logits, hipStream_t st);
+int launch_select(const moe_problem* p, const Dims& d, const float* logits, const float* bias,
+                  int32_t* ids, float* w, hipStream_t st);
+int launch_dispatch(const moe_problem* p, const Dims& d, const void* x, const int32_t* ids,
+                    int32_t* counts, int32_t* offsets, int32_t* dest_row, int32_t* row_src,
+                    int64_t* send_bytes, int32_t* n_dropped, void* xp, char* ws,
+                    const WsLayout& L, hipStream_t st);
+int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_t* offsets,
+               const void* w13, const void* w2, const void* x, const void* w13_sh,
+               const void* w2_sh, void* yp, void* y_sh, char* ws, const WsLayout& L,
+               hipStream_t st);
+int launch_combine(const moe_problem* p, const Dims& d, const void* yp, const int32_t* dest_row,
+                   const float* w, const void* y_sh, void* y, hipStream_t st);
+
+size_t ffn_sched_bytes(const Dims& d);
+
+}  // namespace moe

@@ -1,0 +1,226 @@
+/*
+ * moe.h - C ABI of an MI355X (gfx950) MoE-layer forward pass on one GPU's share of an
+ * expert-parallel (EP) deployment: route -> dispatch -> expert FFN -> combine.
+ *
+ * The four stages are the ones the EP pages list for one MoE layer: the router scores
+ * every expert for every token and keeps the top-K; dispatch regroups the tokens by
+ * destination expert; each expert runs its FFN on the tokens it received; combine
+ * returns the results to token order and sums them with the routing weights
+ * ("总览" (EP chapter overview), section "MoE 路由机制是什么？top-K 怎么用？" and
+ * glossary; "專家並行（Expert Parallelism, EP）", section "技術原理", steps 1-4).
+ * Remote EP ranks appear only as virtual rank ids in the layout: nothing here talks
+ * to another GPU.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *     allocates nothing, keeps no state between calls and never synchronises with the
+ *     host: work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     outputs are valid once that stream has reached the call.
+ *   - Row-major, densely packed arrays; shapes are given in brackets.
+ *     "act" is the activation/expert-weight dtype selected by moe_problem.act_dtype
+ *     (fp32, or bf16 stored as raw 16-bit words). Routing weights are always fp32.
+ *   - Return value: MOE_OK, or a negative status. Arguments are validated on the host
+ *     before anything is enqueued, so an error status means nothing was launched
+ *     (MOE_ERR_LAUNCH excepted: the HIP runtime refused a launch).
+ *   - Workspace: `ws` is device scratch of at least moe_workspace_bytes() bytes,
+ *     256-byte aligned. Calls that run concurrently need distinct workspaces.
+ *   - Values the library leaves undefined are said so per argument; everything else
+ *     is written completely.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = -1,     /* an argument breaks the problem's definition        */
+  MOE_ERR_UNSUPPORTED = -2, /* a valid shape this build does not handle           */
+  MOE_ERR_WORKSPACE = -3,   /* workspace missing, misaligned or too small         */
+  MOE_ERR_LAUNCH = -4       /* the HIP runtime refused a kernel launch            */
+};
+
+enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
+enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
+
+/*
+ * The problem statement of one MoE layer call, in the pages' own quantities: T tokens
+ * of hidden size h, E experts, top-K, a capacity factor, and E/N_EP local experts
+ * ("总览" glossary: top-K, EP 度; "专家并行与 MoE", sections "MoE 结构回顾" and
+ * "Expert Parallelism（EP）": each card holds E/N experts).
+ *
+ *  T            tokens routed in this call (>= 0)
+ *  h            hidden size (> 0)
+ *  E            routed experts in the layer (1..512)
+ *  K            experts per token (1..min(E, 16))
+ *  score        MOE_SCORE_SOFTMAX: key = logit = x.W_r + bias; weights = softmax of
+ *                 the selected logits (= full softmax renormalised over the selection)
+ *               MOE_SCORE_SIGMOID: s = sigmoid(x.W_r); key = s + bias (the bias only
+ *                 steers selection, as aux-loss-free balancing does: "专家并行与 MoE",
+ *                 section "负载均衡"); weights = s over the selection
+ *  renorm       1: selected weights divided by their sum; 0: raw softmax / sigmoid
+ *  n_groups     expert groups for group-limited routing ("总览" glossary "Expert
+ *               group"); groups are contiguous blocks of E/n_groups experts; 1 = off
+ *  topk_groups  groups a token may use (1..n_groups); a group's score is the sum of its
+ *               two largest keys (its only key when a group has one expert)
+ *  capacity_factor  <= 0: no limit. Otherwise cap = ceil(cf * T * K / E), computed
+ *               exactly on the double's value ("專家並行", key parameters: capacity
+ *               factor). Pairs beyond cap are dropped in token order, and a dropped
+ *               pair adds nothing ("专家并行与 MoE": over-capacity tokens skip the
+ *               expert).
+ *  pad_to_capacity  1: every local expert owns exactly cap rows, unused rows zero
+ *               ("专家并行与 MoE", section "负载均衡": drop or pad). Needs a capacity.
+ *  n_ep, ep_rank  virtual EP ranks and the one this GPU plays. Local experts are
+ *               [ep_rank*E/n_ep, (ep_rank+1)*E/n_ep) ("总览", "Dispatch 通信矩阵":
+ *               chip = expert_id / experts-per-chip); token t sits on rank
+ *               t / (T/n_ep) ("总览": 512 tokens over 64 chips, 8 per chip).
+ *  inter        SwiGLU intermediate size of a routed expert (> 0 for the FFN)
+ *  n_shared     0 or 1 shared expert, run on this rank's token block
+ *               [ep_rank*T/n_ep, (ep_rank+1)*T/n_ep) ("总览" glossary "Expert":
+ *               256 routed + 1 shared expert)
+ *  shared_inter SwiGLU intermediate size of the shared expert
+ *  act_dtype    MOE_DTYPE_F32 or MOE_DTYPE_BF16 (activations and expert weights;
+ *               accumulation is fp32 either way)
+ */
+typedef struct moe_problem {
+  int64_t T;
+  int32_t h, E, K;
+  int32_t score;
+  int32_t renorm;
+  int32_t n_groups, topk_groups;
+  double capacity_factor;
+  int32_t pad_to_capacity;
+  int32_t n_ep, ep_rank;
+  int32_t inter, n_shared, shared_inter;
+  int32_t act_dtype;
+} moe_problem;
+
+/* ---- host-only queries (no device work) ---------------------------------------- */
+
+/* MOE_OK if the problem is valid and supported, else the status the calls return.
+ * Invalid: T < 0, h <= 0, E not in 1..512, K not in 1..min(E,16), E % n_ep != 0,
+ * ep_rank outside [0, n_ep), E % n_groups != 0, topk_groups outside 1..n_groups,
+ * topk_groups*E/n_groups < K, padding without a capacity, n_shared not 0/1,
+ * n_shared = 1 with T % n_ep != 0. Unsupported (bf16): h % 64 != 0, inter % 64 != 0,
+ * shared_inter % 64 != 0; (fp32): h % 4 != 0. */
+int moe_check_problem(const moe_problem* p);
+
+/* Capacity per expert in *cap (-1 when there is no limit). */
+int moe_capacity(const moe_problem* p, int64_t* cap);
+
+/* Rows of this rank's expert buffer the caller must allocate for xp / yp / row_src:
+ * T*min(K, E_l) without capacity, E_l*cap padded, min(T*min(K,E_l), E_l*cap) else. */
+int moe_max_rows(const moe_problem* p, int64_t* rows);
+
+/* Workspace bytes that any entry point below needs for this problem. */
+int moe_workspace_bytes(const moe_problem* p, size_t* bytes);
+
+/* Static text for a status code. */
+const char* moe_status_string(int status);
+
+/* ---- stage 1: route --------------------------------------------------------------
+ * Router scores, optional group limit, top-K, weights ("总览" glossary "Router";
+ * "專家並行", "技術原理" step 1). Logits are computed in fp32 (bf16 activations are
+ * exact in fp32; the fp32 router weight enters exactly, as three bf16 parts summed
+ * into fp32 accumulators).
+ *   x         [T][h] act
+ *   w_router  [E][h] fp32 (one row per expert, as a Linear(h, E) weight)
+ *   bias      [E] fp32 or NULL (meaning set by `score`)
+ *   topk_ids  [T][K] int32 out: selected experts, ascending ids; ties between equal
+ *             keys go to the lower expert id (and the lower group id)
+ *   topk_w    [T][K] fp32 out: weights aligned with topk_ids                        */
+int moe_route(const moe_problem* p, const void* x, const float* w_router, const float* bias,
+              int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream);
+
+/* Selection only, from given fp32 logits [T][E] (for example uniform random keys):
+ * the same scoring, group limit, top-K and weights as moe_route after its GEMM.      */
+int moe_select(const moe_problem* p, const float* logits, const float* bias,
+               int32_t* topk_ids, float* topk_w, void* stream);
+
+/* ---- stage 2: dispatch -----------------------------------------------------------
+ * Per-expert histogram, capacity, expert-contiguous permutation of this rank's pairs
+ * and the send-count matrix C[i][j] = n_ij*h*dtype_size of the pairs virtual rank i
+ * routes to rank j ("总览", eq. par-ep-dispatch-matrix). Rows are ordered by (local
+ * expert, token); a pair's rank among its expert's pairs is its token order.
+ *   x          [T][h] act, or NULL for a layout-only call (then xp must be NULL)
+ *   topk_ids   [T][K] int32, each row K distinct ids in [0, E)
+ *   counts     [E] int32 out: pairs per expert before capacity (all experts)
+ *   offsets    [E_l+1] int32 out: first row of each local expert; offsets[E_l] = rows
+ *   dest_row   [T][K] int32 out: row of the pair in this rank's buffer, -1 if the pair
+ *              was dropped or its expert is remote
+ *   row_src    [R_max] int32 out: t*K+k of the row's pair, -1 for pad / unused rows
+ *   send_bytes [n_ep][n_ep] int64 out or NULL; kept pairs only, diagonal included;
+ *              needs T % n_ep == 0
+ *   n_dropped  [1] int32 out: pairs dropped by capacity, over all E experts
+ *   xp         [R_max][h] act out or NULL: xp[r] = x[row_src[r]/K]; pad rows zero;
+ *              rows at or past offsets[E_l] (compact layout) are left undefined      */
+int moe_dispatch(const moe_problem* p, const void* x, const int32_t* topk_ids,
+                 int32_t* counts, int32_t* offsets, int32_t* dest_row, int32_t* row_src,
+                 int64_t* send_bytes, int32_t* n_dropped, void* xp,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* ---- stage 3: expert FFN ---------------------------------------------------------
+ * Every local expert's SwiGLU FFN on its rows as one grouped GEMM pair ("專家並行",
+ * "技術原理" step 3; "MoE 服務的專家並行性": grouped GEMM batching many experts):
+ *   yp = (silu(xp W_g^T) * (xp W_u^T)) W_d^T, fp32 accumulation; the gated product is
+ *   rounded to act once before the down projection.
+ *   xp        [R_max][h] act (rows below offsets[E_l] are read)
+ *   offsets   [E_l+1] int32 (device) as written by moe_dispatch
+ *   w13       [E_l][2*inter][h] act: per expert W_g rows then W_u rows
+ *   w2        [E_l][h][inter] act: per expert W_d
+ *   x, w13_sh, w2_sh   shared expert input [T][h], weights [2*shared_inter][h] and
+ *             [h][shared_inter]; all NULL when n_shared = 0
+ *   yp        [R_max][h] act out: rows below offsets[E_l] written, others undefined
+ *   y_sh      [T/n_ep][h] act out (NULL when n_shared = 0)                           */
+int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* offsets,
+                   const void* w13, const void* w2, const void* x, const void* w13_sh,
+                   const void* w2_sh, void* yp, void* y_sh,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* ---- stage 4: combine ------------------------------------------------------------
+ * y[t] = sum_{k=0..K-1, dest_row[t][k] >= 0} topk_w[t][k] * yp[dest_row[t][k]]
+ *        (+ y_sh[t - t0] for t in this rank's token block when y_sh is not NULL),
+ * accumulated in fp32 in k order, rounded to act once ("專家並行", "技術原理" step 4).
+ * A token with no kept local pair and no shared output gets exact zeros.
+ *   yp [R_max][h] act;  dest_row [T][K];  topk_w [T][K] fp32;
+ *   y_sh [T/n_ep][h] act or NULL;  y [T][h] act out                                */
+int moe_combine(const moe_problem* p, const void* yp, const int32_t* dest_row,
+                const float* topk_w, const void* y_sh, void* y, void* stream);
+
+/* ---- the whole layer -------------------------------------------------------------
+ * route -> dispatch -> expert FFN -> combine on one stream, with every intermediate
+ * kept in caller memory (so each stage's output can be inspected).                   */
+typedef struct moe_tensors {
+  const void* x;            /* [T][h] act                                  */
+  const float* w_router;    /* [E][h] fp32                                 */
+  const float* bias;        /* [E] fp32 or NULL                            */
+  const void* w13;          /* [E_l][2*inter][h] act                       */
+  const void* w2;           /* [E_l][h][inter] act                         */
+  const void* w13_sh;       /* [2*shared_inter][h] act or NULL             */
+  const void* w2_sh;        /* [h][shared_inter] act or NULL               */
+  int32_t* topk_ids;        /* [T][K]                                      */
+  float* topk_w;            /* [T][K]                                      */
+  int32_t* counts;          /* [E]                                         */
+  int32_t* offsets;         /* [E_l+1]                                     */
+  int32_t* dest_row;        /* [T][K]                                      */
+  int32_t* row_src;         /* [R_max]                                     */
+  int64_t* send_bytes;      /* [n_ep][n_ep] or NULL                        */
+  int32_t* n_dropped;       /* [1]                                         */
+  void* xp;                 /* [R_max][h] act                              */
+  void* yp;                 /* [R_max][h] act                              */
+  void* y_sh;               /* [T/n_ep][h] act or NULL                     */
+  void* y;                  /* [T][h] act out                              */
+} moe_tensors;
+
+int moe_forward(const moe_problem* p, const moe_tensors* t, void* ws, size_t ws_bytes,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,132 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the bench times
+(one moe_forward call). Routing and layout are compared in full; the FFN and the layer
+output on sampled rows / tokens that the fp64 oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import volumes as V
+from synth import CONFIGS
+from gpu_cases import (TOL, W_RTOL, cpu_inputs, gpu_inputs, np_, rel_errors, routing_mismatches,
+                       run_forward, run_stages)
+
+pytestmark = pytest.mark.gpu
+
+FULL = ["mixtral_prefill", "dsv3_ep8", "skew_cap1", "skew_nodrop", "dsv3_decode"]
+
+
+def _f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_config(name):
+    cfg = CONFIGS[name]
+    print(f"[case] full {name}", flush=True)
+    inp = gpu_inputs(cfg)
+    p, b = run_forward(cfg, inp)
+    x_c = inp["x"].cpu()
+    wr_c = inp["w_router"].cpu()
+    bias_c = None if inp["bias"] is None else inp["bias"].cpu()
+    # --- route, all tokens
+    rr = oracle.route(K=cfg.K, score=cfg.score, renorm=cfg.renorm, n_groups=cfg.n_groups,
+                      topk_groups=cfg.topk_groups, bias=bias_c, x=x_c, w_router=wr_c)
+    ids = np_(b["topk_ids"]).astype(np.int64)
+    near, other, n_near = routing_mismatches(ids, rr)
+    print(f"[route] {name}: near-tie tokens (gap<1e-4) {n_near}, flipped {len(near)}, "
+          f"other mismatches {len(other)}", flush=True)
+    assert other == []
+    ok = np.ones(cfg.T, bool)
+    ok[near] = False
+    np.testing.assert_allclose(np_(b["topk_w"])[ok], rr.weights[ok], rtol=W_RTOL, atol=1e-7)
+    # --- dispatch, bit-exact against the oracle re-run on the GPU's ids
+    d = oracle.dispatch(ids, E=cfg.E, n_ep=cfg.n_ep, ep_rank=cfg.ep_rank,
+                        capacity_factor=cfg.capacity_factor, pad=cfg.pad, h=cfg.h,
+                        dtype_size=cfg.act_bytes)
+    np.testing.assert_array_equal(np_(b["counts"]), d.counts)
+    np.testing.assert_array_equal(np_(b["offsets"]), d.offsets)
+    np.testing.assert_array_equal(np_(b["dest_row"]), d.dest_row)
+    np.testing.assert_array_equal(np_(b["row_src"])[:d.row_src.shape[0]], d.row_src)
+    assert int(np_(b["n_dropped"])[0]) == d.n_dropped
+    np.testing.assert_array_equal(np_(b["send_bytes"]), d.send_bytes)
+    if d.n_dropped == 0 and cfg.T % cfg.n_ep == 0:
+        assert d.send_bytes.sum() == V.m_total(cfg.T, cfg.K, cfg.h, cfg.act_bytes)
+    # --- xp: bit-exact copies (checked on the device)
+    rs = torch.from_numpy(d.row_src[:d.rows].astype(np.int64)).cuda()
+    live = rs >= 0
+    xp = b["xp"][:d.rows]
+    assert torch.equal(xp[live], inp["x"][rs[live] // cfg.K])
+    assert (xp[~live] == 0).all()
+    # --- FFN on sampled rows: first / last row of a spread of local experts
+    El = cfg.E_local
+    rng = np.random.default_rng(0)
+    experts = [e for e in range(El) if d.offsets[e + 1] > d.offsets[e]]
+    pick = sorted(set(rng.choice(experts, size=min(8, len(experts)), replace=False).tolist()))
+    tmax, tmean = TOL[cfg.dtype]
+    yp = b["yp"]
+    got, ref = [], []
+    for e in pick:
+        lo, hi = int(d.offsets[e]), int(d.offsets[e + 1])
+        rows = sorted({lo, hi - 1, (lo + hi) // 2})
+        w13 = _f64(inp["w13"][e])
+        w2 = _f64(inp["w2"][e])
+        ref.append(oracle.swiglu_ffn(_f64(b["xp"][rows]), w13, w2))
+        got.append(_f64(yp[rows]))
+    mx, mean, _ = rel_errors(np.concatenate(got), np.concatenate(ref))
+    print(f"[ffn] {name}: sampled rows max_rel {mx:.3e} mean_rel {mean:.3e}", flush=True)
+    assert mx <= tmax and mean <= tmean
+    # --- y on sampled tokens, from the oracle's own routing and weights
+    if near:
+        return
+    dref = oracle.dispatch(rr.ids, E=cfg.E, n_ep=cfg.n_ep, ep_rank=cfg.ep_rank,
+                           capacity_factor=cfg.capacity_factor, pad=cfg.pad, h=cfg.h,
+                           dtype_size=cfg.act_bytes)
+    n_tok = 8 if name == "dsv3_decode" else 24
+    toks = sorted(set(rng.choice(cfg.T, size=n_tok, replace=False).tolist()))
+    t0 = cfg.ep_rank * (cfg.T // cfg.n_ep)
+    t1 = t0 + cfg.T // cfg.n_ep
+    if cfg.n_shared:
+        toks = sorted(set(toks) | {t0, t1 - 1, t1})
+    e0 = cfg.ep_rank * El
+    xs = _f64(inp["x"][toks])
+    y_ref = np.zeros((len(toks), cfg.h))
+    by_expert = {}
+    for i, t in enumerate(toks):
+        for k in range(cfg.K):
+            e = int(rr.ids[t, k])
+            if dref.kept[t, k] and e0 <= e < e0 + El:
+                by_expert.setdefault(e - e0, []).append((i, k, t))
+    for el, lst in by_expert.items():
+        out = oracle.swiglu_ffn(xs[[i for i, _, _ in lst]], _f64(inp["w13"][el]),
+                                _f64(inp["w2"][el]))
+        for row, (i, k, t) in zip(out, lst):
+            y_ref[i] += rr.weights[t, k] * row
+    if cfg.n_shared:
+        w13s, w2s = _f64(inp["w13_sh"]), _f64(inp["w2_sh"])
+        for i, t in enumerate(toks):
+            if t0 <= t < t1:
+                y_ref[i] += oracle.swiglu_ffn(xs[i:i + 1], w13s, w2s)[0]
+    mx, mean, zexact = rel_errors(_f64(b["y"][toks]), y_ref)
+    print(f"[parity] {name}: sampled y max_rel {mx:.3e} mean_rel {mean:.3e}", flush=True)
+    assert mx <= tmax and mean <= tmean and zexact
+
+
+def test_layout_zero_pairs():
+    """Uniform routing at EP=64, 512 tokens, top-8 of 256: the GPU's send matrix equals
+    the oracle's, and its zero-pair fraction is near the pages' 36%."""
+    cfg = CONFIGS["layout_ep64"]
+    inp = gpu_inputs(cfg)
+    p, b = run_stages(cfg, inp)
+    keys = inp["keys"].cpu()
+    rr = oracle.route(K=cfg.K, score=cfg.score, logits=keys)
+    ids = np_(b["topk_ids"]).astype(np.int64)
+    np.testing.assert_array_equal(ids, rr.ids)
+    d = oracle.dispatch(ids, E=cfg.E, n_ep=cfg.n_ep, h=cfg.h, dtype_size=cfg.act_bytes)
+    send = np_(b["send_bytes"])
+    np.testing.assert_array_equal(send, d.send_bytes)
+    z = V.zero_pair_fraction(send)
+    print(f"[layout] zero-pair fraction {z:.4f} (closed form "
+          f"{V.zero_pair_probability(256, 64, 8, 512):.4f}, pages ~0.36)", flush=True)
+    assert abs(z - 0.36) < 0.02
+    assert send.sum(1).mean() == V.m_per_chip(512, 8, 7168, 2, 64)

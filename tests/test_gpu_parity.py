@@ -1,0 +1,185 @@
+"""GPU parity: every stage of the HIP path against the fp64 oracle, through the C ABI.
+
+Integer outputs (ids, counts, offsets, dest_row, row_src, dropped, send matrix, the xp
+copy) must be bit-exact; layout arrays are compared with the oracle's dispatch re-run on
+the GPU's own ids, so a near-tie flip in routing cannot shift them. Floating-point
+outputs meet the tolerances in gpu_cases (fp32 1e-4; bf16 2e-2 max / 5e-3 mean).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.dispatch import permute
+from synth import CONFIGS
+from gpu_cases import (TOL, W_RTOL, cpu_inputs, gpu_inputs, np_, rel_errors, routing_mismatches,
+                       run_forward, run_stages)
+
+pytestmark = pytest.mark.gpu
+
+# Small problems that span several tiles with ragged tails, compared in full.
+BASE = CONFIGS["mixtral_prefill"]
+SMALL = {
+    "tiny_f32": CONFIGS["tiny_f32"],
+    "f32_shared_ep": CONFIGS["dsv3_ep8"].with_(T=96, h=64, E=16, K=4, n_groups=4, topk_groups=2,
+                                              inter=48, shared_inter=40, n_ep=4, ep_rank=2,
+                                              dtype="f32"),
+    "bf16_ragged": BASE.with_(T=300, h=256, E=8, K=2, inter=320),
+    "bf16_cap_drop": BASE.with_(T=257, h=128, E=8, K=2, inter=192, capacity_factor=0.75),
+    "bf16_cap_pad": BASE.with_(T=200, h=128, E=8, K=3, inter=128, capacity_factor=1.0, pad=True),
+    "bf16_groups_shared": CONFIGS["dsv3_ep8"].with_(T=256, h=512, E=64, K=6, inter=256,
+                                                   shared_inter=192, n_ep=4, ep_rank=1),
+    "bf16_medium": CONFIGS["skew_nodrop"].with_(T=1024, h=256, E=16, K=2, inter=256),
+    "bf16_large_tiles": BASE.with_(T=1100, h=192, E=4, K=2, inter=384),
+    "bf16_decode": CONFIGS["dsv3_decode"].with_(T=8, h=256, E=64, inter=128),
+    "bf16_k_eq_e": BASE.with_(T=70, h=128, E=4, K=4, inter=64),
+    "bf16_one_token": BASE.with_(T=1, h=128, E=8, K=2, inter=64),
+}
+
+
+def check_route(cfg, inp_c, b, allow_near=True):
+    rr = oracle.route(K=cfg.K, score=cfg.score, renorm=cfg.renorm, n_groups=cfg.n_groups,
+                      topk_groups=cfg.topk_groups, bias=inp_c["bias"],
+                      **({"logits": inp_c["keys"]} if cfg.keys == "uniform"
+                         else {"x": inp_c["x"], "w_router": inp_c["w_router"]}))
+    ids = np_(b["topk_ids"]).astype(np.int64)
+    near, other, n_near = routing_mismatches(ids, rr)
+    assert other == [], f"routing mismatches off near-ties: {other[:10]}"
+    if not allow_near:
+        assert near == []
+    ok = np.ones(len(ids), bool)
+    ok[near] = False
+    np.testing.assert_allclose(np_(b["topk_w"])[ok], rr.weights[ok], rtol=W_RTOL, atol=1e-7)
+    return rr, near
+
+
+def check_dispatch(cfg, inp_c, b, ids):
+    d = oracle.dispatch(ids, E=cfg.E, n_ep=cfg.n_ep, ep_rank=cfg.ep_rank,
+                        capacity_factor=cfg.capacity_factor, pad=cfg.pad, h=cfg.h,
+                        dtype_size=cfg.act_bytes)
+    np.testing.assert_array_equal(np_(b["counts"]), d.counts)
+    np.testing.assert_array_equal(np_(b["offsets"]), d.offsets)
+    np.testing.assert_array_equal(np_(b["dest_row"]), d.dest_row)
+    R = d.row_src.shape[0]
+    np.testing.assert_array_equal(np_(b["row_src"])[:R], d.row_src)
+    assert int(np_(b["n_dropped"])[0]) == d.n_dropped
+    if b["send_bytes"] is not None:
+        np.testing.assert_array_equal(np_(b["send_bytes"]), d.send_bytes)
+    return d
+
+
+def check_xp_exact(cfg, b, d):
+    """xp rows are exact copies of x rows (bitwise), pad rows zero: checked on the GPU."""
+    rows = d.rows
+    rs = b["row_src"][:rows].long()
+    live = rs >= 0
+    src_tok = torch.where(live, rs // cfg.K, torch.zeros_like(rs))
+    return live, src_tok, rows
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_layer_full_parity(name):
+    cfg = SMALL[name]
+    print(f"[case] {name} {cfg}", flush=True)
+    inp = gpu_inputs(cfg)
+    p, b = run_stages(cfg, inp)
+    inp_c = cpu_inputs(inp)
+    rr, near = check_route(cfg, inp_c, b)
+    ids = np_(b["topk_ids"]).astype(np.int64)
+    d = check_dispatch(cfg, inp_c, b, ids)
+    # xp: bit-exact row copies; pad rows zero
+    x = inp_c["x"]
+    xp = b["xp"].cpu()
+    for r in range(d.rows):
+        s = d.row_src[r]
+        if s >= 0:
+            assert torch.equal(xp[r], x[s // cfg.K]), r
+        else:
+            assert (xp[r] == 0).all(), r
+    # expert FFN on the GPU's own xp (exact act values) against fp64
+    w13 = inp_c["w13"]
+    w2 = inp_c["w2"]
+    yp_ref = oracle.expert_ffn(xp[:d.rows], d.offsets, w13, w2)
+    mx, mean, zexact = rel_errors(np_(b["yp"])[:d.rows], yp_ref)
+    tmax, tmean = TOL[cfg.dtype]
+    assert mx <= tmax and mean <= tmean and zexact, (mx, mean)
+    # end to end against the oracle's own forward (independent routing and weights)
+    ref = oracle.forward(cfg, inp_c)
+    if near:
+        pytest.skip(f"near-tie tokens {near}: end-to-end compare not defined")
+    if cfg.n_shared:
+        tpr = cfg.T // cfg.n_ep
+        ysh_ref = ref["ysh"]
+        mx, mean, _ = rel_errors(np_(b["y_sh"]), ysh_ref)
+        assert mx <= tmax and mean <= tmean, ("y_sh", mx, mean)
+    mx, mean, zexact = rel_errors(np_(b["y"]), ref["y"])
+    print(f"[parity] {name}: y max_rel {mx:.3e} mean_rel {mean:.3e}", flush=True)
+    assert mx <= tmax and mean <= tmean, (mx, mean)
+    assert zexact
+
+
+@pytest.mark.parametrize("name", ["bf16_ragged", "bf16_groups_shared", "tiny_f32"])
+def test_forward_equals_stages_and_is_deterministic(name):
+    cfg = SMALL[name]
+    inp = gpu_inputs(cfg)
+    _, a = run_stages(cfg, inp)
+    _, f1 = run_forward(cfg, inp)
+    _, f2 = run_forward(cfg, inp)
+    for k in ("topk_ids", "topk_w", "counts", "offsets", "dest_row", "n_dropped", "y"):
+        assert torch.equal(a[k], f1[k]), k
+        assert torch.equal(f1[k], f2[k]), k
+    if a["y_sh"] is not None:
+        assert torch.equal(a["y_sh"], f1["y_sh"])
+
+
+def test_all_pairs_dropped_or_remote_give_zero_rows():
+    # capacity 1 per expert and 4 ranks: most tokens end with no local kept pair
+    cfg = BASE.with_(T=64, h=128, E=8, K=2, inter=64, capacity_factor=0.0625, n_ep=4,
+                     ep_rank=3)
+    inp = gpu_inputs(cfg)
+    _, b = run_stages(cfg, inp)
+    inp_c = cpu_inputs(inp)
+    ids = np_(b["topk_ids"]).astype(np.int64)
+    d = check_dispatch(cfg, inp_c, b, ids)
+    y = np_(b["y"])
+    empty = (d.dest_row < 0).all(axis=1)
+    assert empty.sum() > 40
+    assert (y[empty] == 0).all()
+
+
+def test_select_from_given_logits_is_exact_on_ties():
+    """moe_select on fp32 logits with forced exact ties: ids bit-exact with the oracle."""
+    import expert_routing_amd as moe
+    g = torch.Generator().manual_seed(0)
+    for (E, K, G, M, score) in [(64, 6, 1, 1, "softmax"), (256, 8, 8, 4, "sigmoid"),
+                                (16, 4, 4, 2, "sigmoid"), (8, 2, 1, 1, "softmax"),
+                                (512, 16, 16, 5, "softmax")]:
+        T = 200
+        L = torch.randint(-3, 4, (T, E), generator=g).float()
+        bias = (torch.randint(-2, 3, (E,), generator=g).float() * 0.25) if score == "sigmoid" else None
+        p = moe.Problem(T=T, h=64, E=E, K=K, score=score, n_groups=G, topk_groups=M)
+        ids = torch.empty((T, K), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+        moe.moe_select(p, L.cuda(), None if bias is None else bias.cuda(), ids, w)
+        torch.cuda.synchronize()
+        rr = oracle.route(K=K, score=score, n_groups=G, topk_groups=M, logits=L, bias=bias)
+        if score == "sigmoid":
+            # sigmoid of equal ints is equal in any precision; keys s+b can tie only exactly
+            pass
+        np.testing.assert_array_equal(ids.cpu().numpy(), rr.ids)
+        np.testing.assert_allclose(w.cpu().numpy(), rr.weights, rtol=W_RTOL, atol=1e-7)
+
+
+def test_renorm_off():
+    import expert_routing_amd as moe
+    for score in ("softmax", "sigmoid"):
+        T, E, K = 64, 32, 4
+        L = torch.randn((T, E), generator=torch.Generator().manual_seed(1))
+        p = moe.Problem(T=T, h=64, E=E, K=K, score=score, renorm=False)
+        ids = torch.empty((T, K), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+        moe.moe_select(p, L.cuda(), None, ids, w)
+        torch.cuda.synchronize()
+        rr = oracle.route(K=K, score=score, renorm=False, logits=L)
+        np.testing.assert_array_equal(ids.cpu().numpy(), rr.ids)
+        np.testing.assert_allclose(w.cpu().numpy(), rr.weights, rtol=W_RTOL, atol=1e-7)
