@@ -130,8 +130,19 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ (r & 7));
 
 __device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer: stride 0, num_records = bytes; reads past the end return zero
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // bf16 grouped GEMM. Tile BM x BN (BN counts B rows: for GATED half gate, half up),
-// BK = 64, waves WM x WN.
+// BK = 64, waves WM x WN. The MFMA takes the weight fragment as its first operand, so
+// a lane's accumulators hold 4 consecutive output columns of one token row.
 template <int BM, int BN, int WM, int WN, bool GATED>
 __global__ __launch_bounds__(256) void ffn_gemm_bf16(const FfnSched* __restrict__ sc, int h) {
   static_assert(WM * WN == 4, "4 waves");
@@ -155,34 +166,35 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(const FfnSched* __restrict_
   const int Kd = GATED ? h : I;         // reduction length = lda = ldb
   const int Nout = GATED ? I : h;       // output columns = ldc
   const int m0 = m_tile * BM, n0 = n_tile * BNO;
+  const uint32_t b_rows = GATED ? 2 * I : h;
+  const __amdgpu_buffer_rsrc_t ra_rs = make_rsrc(A, (uint32_t)rows * Kd * 2);
+  const __amdgpu_buffer_rsrc_t rb_rs = make_rsrc(B, b_rows * (uint32_t)Kd * 2);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
+  const int ld_r = tid >> 3, ld_c = tid & 7;
 
-  // Global source rows of this thread's chunks (clamped into valid memory).
-  const bf16_t* a_src[A_CH];
-  const bf16_t* b_src[B_CH];
+  // Byte offsets of this thread's 16-byte chunks at k = 0. Rows past the group's end
+  // read zeros (buffer bound); gate columns past I are clamped into the gate block.
+  uint32_t a_off[A_CH], b_off[B_CH];
 #pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int id = tid + i * 256, r = id >> 3, c = id & 7;
-    const int gr = m0 + r < rows ? m0 + r : rows - 1;
-    a_src[i] = A + (size_t)gr * Kd + c * 8;
-  }
+  for (int i = 0; i < A_CH; ++i)
+    a_off[i] = ((uint32_t)(m0 + ld_r + 32 * i) * Kd + ld_c * 8) * 2;
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
-    const int id = tid + i * 256, r = id >> 3, c = id & 7;
-    int wrow;
+    const int r = ld_r + 32 * i;
+    uint32_t wrow;
     if (GATED) {
-      const int half = r >= BN / 2;
-      int col = n0 + (half ? r - BN / 2 : r);
+      const bool up = r >= BN / 2;
+      int col = n0 + (up ? r - BN / 2 : r);
       col = col < I ? col : I - 1;
-      wrow = col + (half ? I : 0);
+      wrow = col + (up ? I : 0);
     } else {
-      const int col = n0 + r;
-      wrow = col < Nout ? col : Nout - 1;
+      wrow = n0 + r;
     }
-    b_src[i] = B + (size_t)wrow * Kd + c * 8;
+    b_off[i] = (wrow * (uint32_t)Kd + ld_c * 8) * 2;
   }
+  const int st_base = ld_r * 8 + ld_c;   // swizzle is applied per row below
 
   floatx16 acc[TM][TN];
 #pragma unroll
@@ -193,41 +205,27 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(const FfnSched* __restrict_
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
   uint4 ra[A_CH], rb[B_CH];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + k0);
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + k0);
-  };
-  auto lstore = [&](int buf) {
-    uint4* as = As + buf * BM * 8;
-    uint4* bs = Bs + buf * BN * 8;
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int id = tid + i * 256;
-      as[swz(id >> 3, id & 7)] = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int id = tid + i * 256;
-      bs[swz(id >> 3, id & 7)] = rb[i];
-    }
-  };
-  // B-tile row of col-tile j of this wave
-  auto brow = [&](int j) {
-    if (GATED) {
-      return j < TN / 2 ? wn * (WTN / 2) + j * 32 : BN / 2 + wn * (WTN / 2) + (j - TN / 2) * 32;
-    }
-    return wn * WTN + j * 32;
-  };
-
   const int nk = Kd / 64;
-  gload(0);
-  lstore(0);
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) ra[i] = bload(ra_rs, a_off[i], 0);
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) rb[i] = bload(rb_rs, b_off[i], 0);
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) As[swz(ld_r + 32 * i, ld_c)] = ra[i];
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) Bs[swz(ld_r + 32 * i, ld_c)] = rb[i];
+  (void)st_base;
   __syncthreads();
+
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * 64);
+    if (kt + 1 < nk) {
+      const uint32_t soff = (uint32_t)(kt + 1) * 128;
+#pragma unroll
+      for (int i = 0; i < A_CH; ++i) ra[i] = bload(ra_rs, a_off[i], soff);
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i) rb[i] = bload(rb_rs, b_off[i], soff);
+    }
     const uint4* as = As + cur * BM * 8;
     const uint4* bs = Bs + cur * BN * 8;
 #pragma unroll
@@ -238,32 +236,53 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(const FfnSched* __restrict_
       for (int i = 0; i < TM; ++i)
         af[i] = __builtin_bit_cast(bf16x8_t, as[swz(wm * WTM + i * 32 + (lane & 31), c)]);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = __builtin_bit_cast(bf16x8_t, bs[swz(brow(j) + (lane & 31), c)]);
+      for (int j = 0; j < TN; ++j) {
+        int br;
+        if (GATED)
+          br = j < TN / 2 ? wn * (WTN / 2) + j * 32 : BN / 2 + wn * (WTN / 2) + (j - TN / 2) * 32;
+        else
+          br = wn * WTN + j * 32;
+        bfr[j] = __builtin_bit_cast(bf16x8_t, bs[swz(br + (lane & 31), c)]);
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
+    if (kt + 1 < nk) {
+      uint4* asn = As + (cur ^ 1) * BM * 8;
+      uint4* bsn = Bs + (cur ^ 1) * BN * 8;
+#pragma unroll
+      for (int i = 0; i < A_CH; ++i) asn[swz(ld_r + 32 * i, ld_c)] = ra[i];
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i) bsn[swz(ld_r + 32 * i, ld_c)] = rb[i];
+    }
     __syncthreads();
   }
 
-  // Epilogue: stage the bf16 tile in LDS, then 16-byte stores.
+  // Epilogue. acc[i][j][q]: token row wm*WTM + i*32 + (lane&31); output column
+  // (col-tile base) + 8*(q>>2) + 4*(lane>>5) + (q&3). Stage bf16 in LDS, then 16-byte
+  // row-contiguous stores.
   constexpr int PITCH = BNO * 2 + 16;                  // bytes per staged row
   char* stage = reinterpret_cast<char*>(smem);
   constexpr int TNO = GATED ? TN / 2 : TN;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    const int row = wm * WTM + i * 32 + (lane & 31);
 #pragma unroll
     for (int j = 0; j < TNO; ++j) {
-      const int col = (GATED ? wn * (WTN / 2) : wn * WTN) + j * 32 + (lane & 31);
+      const int cbase = (GATED ? wn * (WTN / 2) : wn * WTN) + j * 32 + 4 * (lane >> 5);
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int row = wm * WTM + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-        float v = GATED ? silu(acc[i][j][q]) * acc[i][j + TN / 2][q] : acc[i][j][q];
-        *reinterpret_cast<bf16_t*>(stage + row * PITCH + col * 2) = f32_to_bf16(v);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int q = q4 * 4 + u;
+          v[u] = GATED ? silu(acc[i][j][q]) * acc[i][j + TN / 2][q] : acc[i][j][q];
+        }
+        bf16x4_t pk = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        *reinterpret_cast<bf16x4_t*>(stage + row * PITCH + (cbase + 8 * q4) * 2) = pk;
       }
     }
   }

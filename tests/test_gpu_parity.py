@@ -148,24 +148,29 @@ def test_all_pairs_dropped_or_remote_give_zero_rows():
 
 
 def test_select_from_given_logits_is_exact_on_ties():
-    """moe_select on fp32 logits with forced exact ties: ids bit-exact with the oracle."""
+    """moe_select on fp32 logits with forced exact ties: ids bit-exact with the oracle.
+
+    Keys are built to be exact in fp32 and fp64 alike, so every tie is a true tie on
+    both sides: softmax keys are small integers; sigmoid logits are +-40 (sigmoid is
+    1.0 or one common tiny value in both precisions) plus biases in steps of 1/4."""
     import expert_routing_amd as moe
     g = torch.Generator().manual_seed(0)
     for (E, K, G, M, score) in [(64, 6, 1, 1, "softmax"), (256, 8, 8, 4, "sigmoid"),
                                 (16, 4, 4, 2, "sigmoid"), (8, 2, 1, 1, "softmax"),
-                                (512, 16, 16, 5, "softmax")]:
+                                (512, 16, 16, 5, "softmax"), (256, 8, 8, 4, "softmax")]:
         T = 200
-        L = torch.randint(-3, 4, (T, E), generator=g).float()
-        bias = (torch.randint(-2, 3, (E,), generator=g).float() * 0.25) if score == "sigmoid" else None
+        if score == "softmax":
+            L = torch.randint(-3, 4, (T, E), generator=g).float()
+            bias = None
+        else:
+            L = torch.randint(0, 2, (T, E), generator=g).float() * 80.0 - 40.0
+            bias = torch.randint(-2, 3, (E,), generator=g).float() * 0.25
         p = moe.Problem(T=T, h=64, E=E, K=K, score=score, n_groups=G, topk_groups=M)
         ids = torch.empty((T, K), dtype=torch.int32, device="cuda")
         w = torch.empty((T, K), dtype=torch.float32, device="cuda")
         moe.moe_select(p, L.cuda(), None if bias is None else bias.cuda(), ids, w)
         torch.cuda.synchronize()
         rr = oracle.route(K=K, score=score, n_groups=G, topk_groups=M, logits=L, bias=bias)
-        if score == "sigmoid":
-            # sigmoid of equal ints is equal in any precision; keys s+b can tie only exactly
-            pass
         np.testing.assert_array_equal(ids.cpu().numpy(), rr.ids)
         np.testing.assert_allclose(w.cpu().numpy(), rr.weights, rtol=W_RTOL, atol=1e-7)
 
