@@ -4,7 +4,7 @@ Argument marshalling only: every function here takes torch tensors, passes their
 device pointers and the current HIP stream to the C ABI of include/moe.h under the same
 name, and raises MoeError on a non-zero status. All compute runs in the library's HIP
 kernels; there is no fallback. Importing this package fails loudly when the library has
-not been built (python -m expert_routing_amd.build).
+not been built (python expert_routing_amd/build.py).
 """
 from __future__ import annotations
 
@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m expert_routing_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python expert_routing_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -89,10 +89,13 @@ _dispatch = _sig("moe_dispatch", [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _S
 _expert_ffn = _sig("moe_expert_ffn", [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _SZ, _V])
 _combine = _sig("moe_combine", [_P, _V, _V, _V, _V, _V, _V])
 _forward = _sig("moe_forward", [_P, ctypes.POINTER(Tensors), _V, _SZ, _V])
+_forward_traced = _sig("moe_forward_traced",
+                       [_P, ctypes.POINTER(Tensors), _V, _SZ, _V, ctypes.POINTER(_V)])
+TRACE_POINTS = ["begin", "route", "dispatch", "ffn_prep", "ffn_gate_up", "ffn_down", "combine"]
 
 EXPORTED = ["moe_check_problem", "moe_capacity", "moe_max_rows", "moe_workspace_bytes",
             "moe_status_string", "moe_route", "moe_select", "moe_dispatch", "moe_expert_ffn",
-            "moe_combine", "moe_forward"]
+            "moe_combine", "moe_forward", "moe_forward_traced"]
 
 
 class MoeError(RuntimeError):
@@ -183,6 +186,43 @@ def moe_forward(p, t: dict, ws, stream=None):
     ts = Tensors(**{k: _ptr(t.get(k)) for k, _ in Tensors._fields_})
     wp, wn = _ws(ws)
     _ok(_forward(ctypes.byref(p), ctypes.byref(ts), wp, wn, _stream(stream)), "moe_forward")
+
+
+def moe_forward_traced(p, t: dict, ws, events, stream=None):
+    """`events`: len(TRACE_POINTS) raw hipEvent_t handles (see HipEvents)."""
+    ts = Tensors(**{k: _ptr(t.get(k)) for k, _ in Tensors._fields_})
+    arr = (_V * len(TRACE_POINTS))(*events)
+    wp, wn = _ws(ws)
+    _ok(_forward_traced(ctypes.byref(p), ctypes.byref(ts), wp, wn, _stream(stream), arr),
+        "moe_forward_traced")
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (timing enabled) from the HIP runtime, for the traced
+    forward; elapsed(a, b) is hipEventElapsedTime in milliseconds."""
+
+    def __init__(self, n):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(_V)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _V, _V]
+        self._hip.hipEventDestroy.argtypes = [_V]
+        self.handles = []
+        for _ in range(n):
+            e = _V()
+            if self._hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles.append(e.value)
+
+    def elapsed(self, a, b):
+        ms = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.handles[a], self.handles[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for h in self.handles:
+            self._hip.hipEventDestroy(h)
+        self.handles = []
 
 
 def alloc_buffers(p: Problem, device="cuda", send=True) -> dict:

@@ -1,6 +1,6 @@
 """Build libmoe.so (all HIP sources, gfx950) in-tree with hipcc.
 
-    python -m expert_routing_amd.build
+    python expert_routing_amd/build.py
 """
 from __future__ import annotations
 

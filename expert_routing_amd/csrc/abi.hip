@@ -259,13 +259,17 @@ int moe_combine(const moe_problem* p, const void* yp, const int32_t* dest_row,
   return launch_combine(p, d, yp, dest_row, topk_w, y_sh, y, (hipStream_t)stream);
 }
 
-int moe_forward(const moe_problem* p, const moe_tensors* t, void* ws, size_t ws_bytes,
-                void* stream) {
+static int forward_impl(const moe_problem* p, const moe_tensors* t, void* ws, size_t ws_bytes,
+                        void* stream, void* const* events) {
   if (!t) return MOE_ERR_INVALID;
   Dims d;
   int st = make_dims(p, &d);
   if (st != MOE_OK) return st;
   if (p->inter <= 0 || (d.T > 0 && !t->x)) return MOE_ERR_INVALID;
+  if (events) {
+    for (int i = 0; i < MOE_TRACE_POINTS; ++i)
+      if (!events[i]) return MOE_ERR_INVALID;
+  }
   // Check every stage before the first launch, so an error enqueues nothing.
   if ((st = v_route(p, d, t->x, t->w_router, t->topk_ids, t->topk_w, ws, ws_bytes)) != MOE_OK ||
       (st = v_dispatch(p, d, t->x, t->topk_ids, t->counts, t->offsets, t->dest_row, t->row_src,
@@ -275,19 +279,40 @@ int moe_forward(const moe_problem* p, const moe_tensors* t, void* ws, size_t ws_
       (st = v_combine(p, d, t->yp, t->dest_row, t->topk_w, t->y_sh, t->y)) != MOE_OK)
     return st;
   const hipStream_t s = (hipStream_t)stream;
+  hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(events);
+  auto mark = [&](int i) {
+    return !ev || hipEventRecord(ev[i], s) == hipSuccess;
+  };
   const WsLayout L = ws_layout(p, d);
   char* w = (char*)ws;
+  if (!mark(MOE_TRACE_BEGIN)) return MOE_ERR_LAUNCH;
   if (d.T > 0 && (st = launch_route(p, d, t->x, t->w_router, t->bias, t->topk_ids, t->topk_w,
                                     (float*)(w + L.logits), s)) != MOE_OK)
     return st;
+  if (!mark(MOE_TRACE_ROUTE)) return MOE_ERR_LAUNCH;
   if ((st = launch_dispatch(p, d, t->x, t->topk_ids, t->counts, t->offsets, t->dest_row,
                             t->row_src, t->send_bytes, t->n_dropped, t->xp, w, L, s)) != MOE_OK)
     return st;
+  if (!mark(MOE_TRACE_DISPATCH)) return MOE_ERR_LAUNCH;
   if ((st = launch_ffn(p, d, t->xp, t->offsets, t->w13, t->w2, t->x, t->w13_sh, t->w2_sh, t->yp,
-                       t->y_sh, w, L, s)) != MOE_OK)
+                       t->y_sh, w, L, s, ev ? ev + MOE_TRACE_FFN_PREP : nullptr)) != MOE_OK)
     return st;
-  if (d.T > 0) return launch_combine(p, d, t->yp, t->dest_row, t->topk_w, t->y_sh, t->y, s);
+  if (d.T > 0 && (st = launch_combine(p, d, t->yp, t->dest_row, t->topk_w, t->y_sh, t->y, s)) !=
+                     MOE_OK)
+    return st;
+  if (!mark(MOE_TRACE_COMBINE)) return MOE_ERR_LAUNCH;
   return MOE_OK;
+}
+
+int moe_forward(const moe_problem* p, const moe_tensors* t, void* ws, size_t ws_bytes,
+                void* stream) {
+  return forward_impl(p, t, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_forward_traced(const moe_problem* p, const moe_tensors* t, void* ws, size_t ws_bytes,
+                       void* stream, void* const* events) {
+  if (!events) return MOE_ERR_INVALID;
+  return forward_impl(p, t, ws, ws_bytes, stream, events);
 }
 
 }  // extern "C"

@@ -140,21 +140,52 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-// bf16 grouped GEMM. Tile BM x BN (BN counts B rows: for GATED half gate, half up),
-// BK = 64, waves WM x WN. The MFMA takes the weight fragment as its first operand, so
-// a lane's accumulators hold 4 consecutive output columns of one token row.
-template <int BM, int BN, int WM, int WN, bool GATED>
-__global__ __launch_bounds__(256) void ffn_gemm_bf16(const FfnSched* __restrict__ sc, int h) {
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Slot of a 16-byte chunk in a 64-byte LDS row: chunk c of row r sits at c ^ row_swz(r).
+// Any 8 aligned consecutive rows (one 128-byte bank sweep) and any 16 aligned consecutive
+// rows (one 256-byte sweep) then put a given chunk in distinct slots, so ds_read_b128
+// fragment reads (lanes = consecutive rows, same chunk) are free of bank conflicts
+// whether the LDS serves 8 or 16 lanes per cycle.
+__device__ __forceinline__ int row_swz(int r) {
+  const int a = (r >> 3) & 1, b = (r >> 2) & 1, c = (r >> 1) & 1;
+  return 2 * (b ^ a) + (c ^ a);
+}
+
+// Workgroup barrier without the memory fence __syncthreads() carries: the fence would
+// wait for every outstanding LDS DMA. Callers wait for the DMA they need with
+// wait_vmcnt first; the "memory" clobber keeps the compiler from moving LDS accesses
+// across the barrier.
+__device__ __forceinline__ void lds_barrier() { __builtin_amdgcn_s_barrier(); }
+
+// s_waitcnt immediate for vmcnt(n) with the other counters left open (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// bf16 grouped GEMM. Block tile BM x BN (BN counts weight rows: for GATED half gate,
+// half up), k-step 32, 4 waves in a WM x WN grid, each wave (BM/WM) x (BN/WN) as 32x32
+// MFMA tiles. Operand tiles stream into a ring of NS LDS stages by buffer->LDS DMA
+// (no register staging), NS-1 steps ahead of the MFMAs. LDS rows are 64 bytes (four
+// 16-byte chunks, swizzled by row_swz). The MFMA takes the weight fragment first, so a
+// lane's accumulators hold 4 consecutive output columns.
+template <int BM, int BN, int WM, int WN, bool GATED, int NS>
+__device__ __forceinline__ void gemm_bf16_body(const FfnSched* __restrict__ sc, int h,
+                                               uint4* __restrict__ smem) {
   static_assert(WM * WN == 4, "4 waves");
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(TM >= 1 && TN >= 1, "tile");
   static_assert(!GATED || TN % 2 == 0, "gated needs gate/up pairs");
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "DMA rows split evenly over 4 waves");
   constexpr int BNO = GATED ? BN / 2 : BN;          // output columns per tile
-  constexpr int A_CH = BM * 8 / 256, B_CH = BN * 8 / 256;
-  extern __shared__ uint4 smem[];
-  uint4* As = smem;                 // [2][BM*8]
-  uint4* Bs = smem + 2 * BM * 8;    // [2][BN*8]
+  constexpr int AI = BM / 64, BI = BN / 64;         // DMA instructions per wave per stage
+  constexpr int LPS = AI + BI;
+  constexpr int A_ST = BM * 4, B_ST = BN * 4;       // uint4 per stage
+  uint4* As = smem;                                 // [NS][BM rows][4 chunks]
+  uint4* Bs = smem + NS * A_ST;                     // [NS][BN rows][4 chunks]
 
   int g, m_tile, n_tile;
   if (!find_tile(sc, GATED, BM, g, m_tile, n_tile)) return;
@@ -172,17 +203,20 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(const FfnSched* __restrict_
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const int ld_r = tid >> 3, ld_c = tid & 7;
 
-  // Byte offsets of this thread's 16-byte chunks at k = 0. Rows past the group's end
-  // read zeros (buffer bound); gate columns past I are clamped into the gate block.
-  uint32_t a_off[A_CH], b_off[B_CH];
+  // DMA: instruction j of this wave fills tile rows 16*(4*j+wave) .. +16; lane L lands
+  // on row +L/4, slot L&3, so it fetches logical chunk (L&3) ^ ((L>>3)&3).
+  const int dr = lane >> 2;
+  const int dc = (lane & 3) ^ row_swz(dr);
+  uint32_t a_off[AI], b_off[BI];
 #pragma unroll
-  for (int i = 0; i < A_CH; ++i)
-    a_off[i] = ((uint32_t)(m0 + ld_r + 32 * i) * Kd + ld_c * 8) * 2;
+  for (int j = 0; j < AI; ++j) {
+    const int r = 16 * (4 * j + wave) + dr;
+    a_off[j] = ((uint32_t)(m0 + r) * Kd + dc * 8) * 2;
+  }
 #pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int r = ld_r + 32 * i;
+  for (int j = 0; j < BI; ++j) {
+    const int r = 16 * (4 * j + wave) + dr;
     uint32_t wrow;
     if (GATED) {
       const bool up = r >= BN / 2;
@@ -192,9 +226,21 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(const FfnSched* __restrict_
     } else {
       wrow = n0 + r;
     }
-    b_off[i] = (wrow * (uint32_t)Kd + ld_c * 8) * 2;
+    b_off[j] = (wrow * (uint32_t)Kd + dc * 8) * 2;
   }
-  const int st_base = ld_r * 8 + ld_c;   // swizzle is applied per row below
+  auto issue = [&](int step, int stage) __attribute__((always_inline)) {
+    const uint32_t soff = (uint32_t)step * 64;
+    uint4* as = As + stage * A_ST;
+    uint4* bs = Bs + stage * B_ST;
+#pragma unroll
+    for (int j = 0; j < AI; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_rs, LDS_PTR(as + 64 * (4 * j + wave)), 16,
+                                               a_off[j], soff, 0, 0);
+#pragma unroll
+    for (int j = 0; j < BI; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_rs, LDS_PTR(bs + 64 * (4 * j + wave)), 16,
+                                               b_off[j], soff, 0, 0);
+  };
 
   floatx16 acc[TM][TN];
 #pragma unroll
@@ -204,62 +250,80 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(const FfnSched* __restrict_
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  uint4 ra[A_CH], rb[B_CH];
-  const int nk = Kd / 64;
+  // Fragment rows (within the tile) and the B row of each col-tile.
+  int arow[TM], brow[TN];
 #pragma unroll
-  for (int i = 0; i < A_CH; ++i) ra[i] = bload(ra_rs, a_off[i], 0);
+  for (int i = 0; i < TM; ++i) arow[i] = wm * WTM + i * 32 + (lane & 31);
 #pragma unroll
-  for (int i = 0; i < B_CH; ++i) rb[i] = bload(rb_rs, b_off[i], 0);
-#pragma unroll
-  for (int i = 0; i < A_CH; ++i) As[swz(ld_r + 32 * i, ld_c)] = ra[i];
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) Bs[swz(ld_r + 32 * i, ld_c)] = rb[i];
-  (void)st_base;
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      const uint32_t soff = (uint32_t)(kt + 1) * 128;
-#pragma unroll
-      for (int i = 0; i < A_CH; ++i) ra[i] = bload(ra_rs, a_off[i], soff);
-#pragma unroll
-      for (int i = 0; i < B_CH; ++i) rb[i] = bload(rb_rs, b_off[i], soff);
-    }
-    const uint4* as = As + cur * BM * 8;
-    const uint4* bs = Bs + cur * BN * 8;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int c = kk * 2 + (lane >> 5);
-      bf16x8_t af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = __builtin_bit_cast(bf16x8_t, as[swz(wm * WTM + i * 32 + (lane & 31), c)]);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        int br;
-        if (GATED)
-          br = j < TN / 2 ? wn * (WTN / 2) + j * 32 : BN / 2 + wn * (WTN / 2) + (j - TN / 2) * 32;
-        else
-          br = wn * WTN + j * 32;
-        bfr[j] = __builtin_bit_cast(bf16x8_t, bs[swz(br + (lane & 31), c)]);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) {
-      uint4* asn = As + (cur ^ 1) * BM * 8;
-      uint4* bsn = Bs + (cur ^ 1) * BN * 8;
-#pragma unroll
-      for (int i = 0; i < A_CH; ++i) asn[swz(ld_r + 32 * i, ld_c)] = ra[i];
-#pragma unroll
-      for (int i = 0; i < B_CH; ++i) bsn[swz(ld_r + 32 * i, ld_c)] = rb[i];
-    }
-    __syncthreads();
+  for (int j = 0; j < TN; ++j) {
+    int br;
+    if (GATED)
+      br = j < TN / 2 ? wn * (WTN / 2) + j * 32 : BN / 2 + wn * (WTN / 2) + (j - TN / 2) * 32;
+    else
+      br = wn * WTN + j * 32;
+    brow[j] = br + (lane & 31);
   }
+  auto frag = [&](const uint4* base, int r, int kk) __attribute__((always_inline)) {
+    const int c = kk * 2 + (lane >> 5);
+    return __builtin_bit_cast(bf16x8_t, base[r * 4 + (c ^ row_swz(r))]);
+  };
+
+  // Software pipeline, one barrier per k32 step, placed mid-step:
+  //   k16 phase 0 of step kt | wait for step kt+1's DMA, barrier | DMA step kt+NS-1
+  //   into the stage step kt-1 used | k16 phase 1 of step kt.
+  // Each phase starts with one MFMA (its fragments were read a phase earlier, so the
+  // compiler's full LDS wait there is free), then reads the next phase's fragments,
+  // then runs its other MFMAs. The barrier is a bare s_barrier: a wave's vmcnt wait
+  // covers its own DMA into LDS and the barrier publishes every wave's
+  // (__syncthreads would add a fence that drains every stage).
+  const int nk = Kd / 32;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s, s);
+  // step 0 must land; the stages issued after it may stay in flight
+  if (nk >= NS - 1) wait_vmcnt<(NS - 2) * LPS>(); else wait_vmcnt<0>();
+  lds_barrier();
+  bf16x8_t a0[TM], b0[TN], a1[TM], b1[TN];
+  auto read_frags = [&](bf16x8_t* a, bf16x8_t* b, int step, int kk) __attribute__((always_inline)) {
+    const uint4* as = As + (step % NS) * A_ST;
+    const uint4* bs = Bs + (step % NS) * B_ST;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[j] = frag(bs, brow[j], kk);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[i] = frag(as, arow[i], kk);
+  };
+  // MFMAs [lo, hi) of one k16 phase, in (i, j) order.
+  auto mfma_range = [&](const bf16x8_t* a, const bf16x8_t* b, int lo, int hi)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < TM * TN; ++t)
+      if (t >= lo && t < hi)
+        acc[t / TN][t % TN] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[t % TN], a[t / TN], acc[t / TN][t % TN],
+                                                    0, 0, 0);
+  };
+  read_frags(a0, b0, 0, 0);
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    mfma_range(a0, b0, 0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(a1, b1, kt, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_range(a0, b0, 1, TM * TN);
+    // step kt+1 must have landed; DMA of steps up to kt+NS-2 may stay in flight
+    if (kt + NS - 2 < nk) wait_vmcnt<(NS - 3) * LPS>(); else wait_vmcnt<0>();
+    lds_barrier();
+    if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_range(a1, b1, 0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(a0, b0, kt + 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_range(a1, b1, 1, TM * TN);
+  }
+  read_frags(a1, b1, nk - 1, 1);
+  mfma_range(a0, b0, 0, TM * TN);
+  mfma_range(a1, b1, 0, TM * TN);
+  __syncthreads();
 
   // Epilogue. acc[i][j][q]: token row wm*WTM + i*32 + (lane&31); output column
   // (col-tile base) + 8*(q>>2) + 4*(lane>>5) + (q&3). Stage bf16 in LDS, then 16-byte
@@ -297,11 +361,23 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(const FfnSched* __restrict_
   }
 }
 
-template <int BM, int BN, bool GATED>
+template <int BM, int BN, bool GATED, int NS>
 constexpr size_t bf16_lds_bytes() {
-  constexpr size_t ops = 2 * (size_t)(BM + BN) * 8 * 16;
+  constexpr size_t ops = (size_t)NS * (BM + BN) * 4 * 16;
   constexpr size_t stg = (size_t)BM * ((GATED ? BN / 2 : BN) * 2 + 16);
   return ops > stg ? ops : stg;
+}
+
+// Two kernel names, so profiles tell the gate/up GEMM from the down projection.
+template <int BM, int BN, int WM, int WN, int NS>
+__global__ __launch_bounds__(256) void ffn_gate_up_bf16(const FfnSched* __restrict__ sc, int h) {
+  __shared__ uint4 smem[bf16_lds_bytes<BM, BN, true, NS>() / 16];
+  gemm_bf16_body<BM, BN, WM, WN, true, NS>(sc, h, smem);
+}
+template <int BM, int BN, int WM, int WN, int NS>
+__global__ __launch_bounds__(256) void ffn_down_bf16(const FfnSched* __restrict__ sc, int h) {
+  __shared__ uint4 smem[bf16_lds_bytes<BM, BN, false, NS>() / 16];
+  gemm_bf16_body<BM, BN, WM, WN, false, NS>(sc, h, smem);
 }
 
 // fp32 grouped GEMM: 64 x 64 tiles (gated: 32 gate + 32 up columns), 4x4 per thread.
@@ -382,20 +458,19 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32(const FfnSched* __restrict__
 // Tile shapes chosen from the expected rows per local expert, T*K/E.
 enum class Tiles { Large, Medium, Small };
 
-template <int BM, int BN, int WM, int WN, bool GATED>
-bool launch_bf16(const FfnSched* sc, int h, int64_t tiles_ub, hipStream_t st) {
-  constexpr size_t lds = bf16_lds_bytes<BM, BN, GATED>();
-  static bool attr_set = false;   // same value for every call and device
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_gemm_bf16<BM, BN, WM, WN, GATED>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return false;
-    attr_set = true;
-  }
-  const int64_t grid = (tiles_ub + kNumXcd - 1) / kNumXcd * kNumXcd;
-  if (grid <= 0) return true;
-  hipLaunchKernelGGL((ffn_gemm_bf16<BM, BN, WM, WN, GATED>), dim3((unsigned)grid), dim3(256),
-                     lds, st, sc, h);
+template <int BM, int BN, int WM, int WN, int NS>
+bool launch_bf16_pair(const FfnSched* sc, int h, int64_t ub1, int64_t ub2, hipStream_t st,
+                      hipEvent_t const* ev) {
+  const int64_t g1 = (ub1 + kNumXcd - 1) / kNumXcd * kNumXcd;
+  const int64_t g2 = (ub2 + kNumXcd - 1) / kNumXcd * kNumXcd;
+  if (g1 > 0)
+    hipLaunchKernelGGL((ffn_gate_up_bf16<BM, BN, WM, WN, NS>), dim3((unsigned)g1), dim3(256), 0,
+                       st, sc, h);
+  if (hipGetLastError() != hipSuccess) return false;
+  if (ev && hipEventRecord(ev[1], st) != hipSuccess) return false;
+  if (g2 > 0)
+    hipLaunchKernelGGL((ffn_down_bf16<BM, BN, WM, WN, NS>), dim3((unsigned)g2), dim3(256), 0, st,
+                       sc, h);
   return hipGetLastError() == hipSuccess;
 }
 
@@ -406,7 +481,7 @@ size_t ffn_sched_bytes(const Dims&) { return sizeof(FfnSched); }
 int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_t* offsets,
                const void* w13, const void* w2, const void* x, const void* w13_sh,
                const void* w2_sh, void* yp, void* y_sh, char* ws, const WsLayout& L,
-               hipStream_t st) {
+               hipStream_t st, hipEvent_t const* ev) {
   FfnSched* sc = reinterpret_cast<FfnSched*>(ws + L.sched);
   const int has_sh = (p->n_shared && d.sh_rows > 0) ? 1 : 0;
   const int64_t sh_t0 = (int64_t)d.rank * d.tpr;
@@ -415,7 +490,7 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
   if (d.bf16) {
     const double per_expert = d.E > 0 ? (double)d.T * d.K / d.E : 0.0;
     tiles = per_expert >= 384 ? Tiles::Large : (per_expert >= 48 ? Tiles::Medium : Tiles::Small);
-    BM = tiles == Tiles::Large ? 256 : (tiles == Tiles::Medium ? 128 : 32);
+    BM = tiles == Tiles::Large ? 256 : (tiles == Tiles::Medium ? 128 : 64);
     BN1 = 128;   // output columns of the gated tile (256 B rows: 128 gate + 128 up)
     BN2 = 256;
   } else {
@@ -429,6 +504,7 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
                      d.sh_rows, sh_t0, d.h, p->inter, p->shared_inter, d.R_max, d.s, BM, BN1,
                      BN2);
   if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
+  if (ev && hipEventRecord(ev[0], st) != hipSuccess) return MOE_ERR_LAUNCH;
   // Upper bound on m-tiles: sum_e ceil(rows_e / BM) <= R_max / BM + E_l.
   const int64_t mt_ub = d.R_max / BM + d.El;
   const int64_t mt_sh = has_sh ? (d.sh_rows + BM - 1) / BM : 0;
@@ -441,16 +517,13 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
   if (d.bf16) {
     switch (tiles) {
       case Tiles::Large:
-        ok = launch_bf16<256, 256, 2, 2, true>(sc, d.h, ub1, st) &&
-             launch_bf16<256, 256, 2, 2, false>(sc, d.h, ub2, st);
+        ok = launch_bf16_pair<256, 256, 2, 2, 4>(sc, d.h, ub1, ub2, st, ev);
         break;
       case Tiles::Medium:
-        ok = launch_bf16<128, 256, 2, 2, true>(sc, d.h, ub1, st) &&
-             launch_bf16<128, 256, 2, 2, false>(sc, d.h, ub2, st);
+        ok = launch_bf16_pair<128, 256, 2, 2, 4>(sc, d.h, ub1, ub2, st, ev);
         break;
       case Tiles::Small:
-        ok = launch_bf16<32, 256, 1, 4, true>(sc, d.h, ub1, st) &&
-             launch_bf16<32, 256, 1, 4, false>(sc, d.h, ub2, st);
+        ok = launch_bf16_pair<64, 256, 1, 4, 4>(sc, d.h, ub1, ub2, st, ev);
         break;
     }
   } else {
@@ -458,10 +531,12 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
     const int64_t g2 = (ub2 + kNumXcd - 1) / kNumXcd * kNumXcd;
     if (g1 > 0)
       hipLaunchKernelGGL(ffn_gemm_f32<true>, dim3((unsigned)g1), dim3(256), 0, st, sc, d.h);
+    if (ev) hipEventRecord(ev[1], st);
     if (g2 > 0)
       hipLaunchKernelGGL(ffn_gemm_f32<false>, dim3((unsigned)g2), dim3(256), 0, st, sc, d.h);
     ok = hipGetLastError() == hipSuccess;
   }
+  if (ok && ev) ok = hipEventRecord(ev[2], st) == hipSuccess;
   return ok ? MOE_OK : MOE_ERR_LAUNCH;
 }
 

@@ -220,6 +220,24 @@ typedef struct moe_tensors {
 int moe_forward(const moe_problem* p, const moe_tensors* t, void* ws, size_t ws_bytes,
                 void* stream);
 
+/* ---- tracing -----------------------------------------------------------------------
+ * moe_forward with timing marks: events[i] (caller-created hipEvent_t handles, all
+ * non-NULL) is recorded on `stream` at trace point i, so the caller can time each
+ * kernel group with hipEventElapsedTime. The work enqueued is identical to
+ * moe_forward's.                                                                     */
+enum moe_trace_point {
+  MOE_TRACE_BEGIN = 0,        /* before the router GEMM                        */
+  MOE_TRACE_ROUTE = 1,        /* after router GEMM + top-K selection           */
+  MOE_TRACE_DISPATCH = 2,     /* after histogram, scan, layout, fill, row copy */
+  MOE_TRACE_FFN_PREP = 3,     /* after the FFN tile-table kernel               */
+  MOE_TRACE_FFN_GATE_UP = 4,  /* after the gate/up grouped GEMM (silu * mul)   */
+  MOE_TRACE_FFN_DOWN = 5,     /* after the down-projection grouped GEMM        */
+  MOE_TRACE_COMBINE = 6,      /* after combine                                 */
+  MOE_TRACE_POINTS = 7
+};
+int moe_forward_traced(const moe_problem* p, const moe_tensors* t, void* ws, size_t ws_bytes,
+                       void* stream, void* const* events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -188,3 +188,22 @@ def test_renorm_off():
         rr = oracle.route(K=K, score=score, renorm=False, logits=L)
         np.testing.assert_array_equal(ids.cpu().numpy(), rr.ids)
         np.testing.assert_allclose(w.cpu().numpy(), rr.weights, rtol=W_RTOL, atol=1e-7)
+
+
+def test_forward_traced_matches_forward():
+    import expert_routing_amd as moe
+    cfg = SMALL["bf16_groups_shared"]
+    inp = gpu_inputs(cfg)
+    p, a = run_forward(cfg, inp)
+    b = moe.alloc_buffers(p, "cuda")
+    t = dict(b)
+    t.update(x=inp["x"], w_router=inp["w_router"], bias=inp["bias"], w13=inp["w13"],
+             w2=inp["w2"], w13_sh=inp["w13_sh"], w2_sh=inp["w2_sh"])
+    ev = moe.HipEvents(len(moe.TRACE_POINTS))
+    moe.moe_forward_traced(p, t, b["ws"], ev.handles)
+    torch.cuda.synchronize()
+    for k in ("topk_ids", "topk_w", "dest_row", "y", "y_sh"):
+        assert torch.equal(a[k], b[k]), k
+    for j in range(1, len(moe.TRACE_POINTS)):
+        assert ev.elapsed(j - 1, j) >= 0.0
+    ev.close()
