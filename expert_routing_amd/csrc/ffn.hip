@@ -142,21 +142,12 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-// Slot of a 16-byte chunk in a 64-byte LDS row: chunk c of row r sits at c ^ row_swz(r).
-// Any 8 aligned consecutive rows (one 128-byte bank sweep) and any 16 aligned consecutive
-// rows (one 256-byte sweep) then put a given chunk in distinct slots, so ds_read_b128
-// fragment reads (lanes = consecutive rows, same chunk) are free of bank conflicts
-// whether the LDS serves 8 or 16 lanes per cycle.
-__device__ __forceinline__ int row_swz(int r) {
-  const int a = (r >> 3) & 1, b = (r >> 2) & 1, c = (r >> 1) & 1;
-  return 2 * (b ^ a) + (c ^ a);
-}
-
-// Workgroup barrier without the memory fence __syncthreads() carries: the fence would
-// wait for every outstanding LDS DMA. Callers wait for the DMA they need with
-// wait_vmcnt first; the "memory" clobber keeps the compiler from moving LDS accesses
-// across the barrier.
-__device__ __forceinline__ void lds_barrier() { __builtin_amdgcn_s_barrier(); }
+// Slot of a 16-byte chunk in a 128-byte LDS row: chunk c of row r sits at
+// c ^ row_swz(r). Any 8 aligned consecutive rows (one 128-byte bank sweep) and any 16
+// aligned consecutive rows (one 256-byte sweep) then hold a given chunk in distinct
+// slots, so ds_read_b128 fragment reads (lanes = consecutive rows, same chunk) are free
+// of bank conflicts whether the LDS serves 8 or 16 lanes per cycle.
+__device__ __forceinline__ int row_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // s_waitcnt immediate for vmcnt(n) with the other counters left open (gfx9 encoding).
 template <int N>
@@ -165,13 +156,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Workgroup barrier without the memory fence __syncthreads() carries (the fence would
+// also wait for LDS DMA still in flight); callers wait for the DMA they need first.
+__device__ __forceinline__ void lds_barrier() { __builtin_amdgcn_s_barrier(); }
+
 // bf16 grouped GEMM. Block tile BM x BN (BN counts weight rows: for GATED half gate,
-// half up), k-step 32, 4 waves in a WM x WN grid, each wave (BM/WM) x (BN/WN) as 32x32
-// MFMA tiles. Operand tiles stream into a ring of NS LDS stages by buffer->LDS DMA
-// (no register staging), NS-1 steps ahead of the MFMAs. LDS rows are 64 bytes (four
-// 16-byte chunks, swizzled by row_swz). The MFMA takes the weight fragment first, so a
-// lane's accumulators hold 4 consecutive output columns.
-template <int BM, int BN, int WM, int WN, bool GATED, int NS>
+// half up), k-step 64, 4 waves in a WM x WN grid, each wave (BM/WM) x (BN/WN) as 32x32
+// MFMA tiles. Operand tiles stream into two LDS stages by buffer->LDS DMA (no register
+// staging) one k-step ahead of the MFMAs. Every DMA request covers whole 128-byte row
+// segments (half-line requests roughly halve what L2 can deliver per CU). The MFMA takes
+// the weight fragment first, so a lane's accumulators hold 4 consecutive output columns.
+template <int BM, int BN, int WM, int WN, bool GATED>
 __device__ __forceinline__ void gemm_bf16_body(const FfnSched* __restrict__ sc, int h,
                                                uint4* __restrict__ smem) {
   static_assert(WM * WN == 4, "4 waves");
@@ -179,13 +174,14 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnSched* __restrict__ sc, 
   constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(TM >= 1 && TN >= 1, "tile");
   static_assert(!GATED || TN % 2 == 0, "gated needs gate/up pairs");
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "DMA rows split evenly over 4 waves");
+  static_assert(BM % 32 == 0 && BN % 32 == 0, "DMA rows split evenly over 4 waves");
   constexpr int BNO = GATED ? BN / 2 : BN;          // output columns per tile
-  constexpr int AI = BM / 64, BI = BN / 64;         // DMA instructions per wave per stage
+  constexpr int AI = BM / 32, BI = BN / 32;         // DMA instructions per wave per stage
   constexpr int LPS = AI + BI;
-  constexpr int A_ST = BM * 4, B_ST = BN * 4;       // uint4 per stage
-  uint4* As = smem;                                 // [NS][BM rows][4 chunks]
-  uint4* Bs = smem + NS * A_ST;                     // [NS][BN rows][4 chunks]
+  constexpr int A_ST = BM * 8, B_ST = BN * 8;       // uint4 per stage
+  constexpr int NMF = TM * TN;                      // MFMAs per k16 phase
+  uint4* As = smem;                                 // [2][BM rows][8 chunks]
+  uint4* Bs = smem + 2 * A_ST;                      // [2][BN rows][8 chunks]
 
   int g, m_tile, n_tile;
   if (!find_tile(sc, GATED, BM, g, m_tile, n_tile)) return;
@@ -201,22 +197,24 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnSched* __restrict__ sc, 
   const __amdgpu_buffer_rsrc_t ra_rs = make_rsrc(A, (uint32_t)rows * Kd * 2);
   const __amdgpu_buffer_rsrc_t rb_rs = make_rsrc(B, b_rows * (uint32_t)Kd * 2);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index as a scalar, so LDS DMA destinations (M0) are computed in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
-  // DMA: instruction j of this wave fills tile rows 16*(4*j+wave) .. +16; lane L lands
-  // on row +L/4, slot L&3, so it fetches logical chunk (L&3) ^ ((L>>3)&3).
-  const int dr = lane >> 2;
-  const int dc = (lane & 3) ^ row_swz(dr);
+  // DMA: instruction j of this wave fills tile rows 8*(4*j+wave) .. +8; lane L lands on
+  // row +L/8, slot L&7, so it fetches logical chunk (L&7) ^ row_swz(row).
+  const int dr = lane >> 3;
+  const int dc = (lane & 7) ^ dr ^ (wave & 1);
   uint32_t a_off[AI], b_off[BI];
 #pragma unroll
   for (int j = 0; j < AI; ++j) {
-    const int r = 16 * (4 * j + wave) + dr;
+    const int r = 8 * (4 * j + wave) + dr;
     a_off[j] = ((uint32_t)(m0 + r) * Kd + dc * 8) * 2;
   }
 #pragma unroll
   for (int j = 0; j < BI; ++j) {
-    const int r = 16 * (4 * j + wave) + dr;
+    const int r = 8 * (4 * j + wave) + dr;
     uint32_t wrow;
     if (GATED) {
       const bool up = r >= BN / 2;
@@ -228,18 +226,17 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnSched* __restrict__ sc, 
     }
     b_off[j] = (wrow * (uint32_t)Kd + dc * 8) * 2;
   }
-  auto issue = [&](int step, int stage) __attribute__((always_inline)) {
-    const uint32_t soff = (uint32_t)step * 64;
-    uint4* as = As + stage * A_ST;
-    uint4* bs = Bs + stage * B_ST;
-#pragma unroll
-    for (int j = 0; j < AI; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_rs, LDS_PTR(as + 64 * (4 * j + wave)), 16,
-                                               a_off[j], soff, 0, 0);
-#pragma unroll
-    for (int j = 0; j < BI; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_rs, LDS_PTR(bs + 64 * (4 * j + wave)), 16,
-                                               b_off[j], soff, 0, 0);
+  // DMA instruction `x` (0 <= x < LPS) of k-step `step` into stage `stage`.
+  auto issue_one = [&](int step, int stage, int x) __attribute__((always_inline)) {
+    const uint32_t soff = (uint32_t)step * 128;
+    if (x < AI) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra_rs, LDS_PTR(As + stage * A_ST + 64 * (4 * x + wave)), 16, a_off[x], soff, 0, 0);
+    } else {
+      const int y = x - AI;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb_rs, LDS_PTR(Bs + stage * B_ST + 64 * (4 * y + wave)), 16, b_off[y], soff, 0, 0);
+    }
   };
 
   floatx16 acc[TM][TN];
@@ -263,66 +260,61 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnSched* __restrict__ sc, 
       br = wn * WTN + j * 32;
     brow[j] = br + (lane & 31);
   }
-  auto frag = [&](const uint4* base, int r, int kk) __attribute__((always_inline)) {
+  bf16x8_t fa[2][TM], fb[2][TN];
+  auto read_frags = [&](int set, int stage, int kk) __attribute__((always_inline)) {
+    const uint4* as = As + stage * A_ST;
+    const uint4* bs = Bs + stage * B_ST;
     const int c = kk * 2 + (lane >> 5);
-    return __builtin_bit_cast(bf16x8_t, base[r * 4 + (c ^ row_swz(r))]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      fb[set][j] = __builtin_bit_cast(bf16x8_t, bs[brow[j] * 8 + (c ^ row_swz(brow[j]))]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      fa[set][i] = __builtin_bit_cast(bf16x8_t, as[arow[i] * 8 + (c ^ row_swz(arow[i]))]);
   };
 
-  // Software pipeline, one barrier per k32 step, placed mid-step:
-  //   k16 phase 0 of step kt | wait for step kt+1's DMA, barrier | DMA step kt+NS-1
-  //   into the stage step kt-1 used | k16 phase 1 of step kt.
-  // Each phase starts with one MFMA (its fragments were read a phase earlier, so the
-  // compiler's full LDS wait there is free), then reads the next phase's fragments,
-  // then runs its other MFMAs. The barrier is a bare s_barrier: a wave's vmcnt wait
-  // covers its own DMA into LDS and the barrier publishes every wave's
-  // (__syncthreads would add a fence that drains every stage).
-  const int nk = Kd / 32;
+  // One k-step: four k16 phases. A phase runs one MFMA (its fragments were read a phase
+  // earlier, so the compiler's full LDS wait there is free), reads the next phase's
+  // fragments, then its other MFMAs. With `dma`, the next k-step's DMA rides along one
+  // instruction per MFMA (never a burst of VMEM issues the wave would block on).
+  auto kstep = [&](int stage, bool dma, int next_step) __attribute__((always_inline)) {
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) issue(s, s);
-  // step 0 must land; the stages issued after it may stay in flight
-  if (nk >= NS - 1) wait_vmcnt<(NS - 2) * LPS>(); else wait_vmcnt<0>();
+    for (int kk = 0; kk < 4; ++kk) {
+      const int cur = kk & 1;
+#pragma unroll
+      for (int t = 0; t < NMF; ++t) {
+        acc[t / TN][t % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            fb[cur][t % TN], fa[cur][t / TN], acc[t / TN][t % TN], 0, 0, 0);
+        const int slot = kk * NMF + t;            // MFMA index within the k-step
+        if (dma && slot >= 1 && slot - 1 < LPS) issue_one(next_step, stage ^ 1, slot - 1);
+        if (t == 0 && kk < 3) {
+          __builtin_amdgcn_sched_barrier(0);
+          read_frags(cur ^ 1, stage, kk + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (dma) {   // instructions left over when the k-step has fewer MFMAs than DMAs
+#pragma unroll
+      for (int x = 4 * NMF - 1; x < LPS; ++x) issue_one(next_step, stage ^ 1, x);
+    }
+  };
+
+  const int nk = Kd / 64;
+#pragma unroll
+  for (int x = 0; x < LPS; ++x) issue_one(0, 0, x);
+  wait_vmcnt<0>();
   lds_barrier();
-  bf16x8_t a0[TM], b0[TN], a1[TM], b1[TN];
-  auto read_frags = [&](bf16x8_t* a, bf16x8_t* b, int step, int kk) __attribute__((always_inline)) {
-    const uint4* as = As + (step % NS) * A_ST;
-    const uint4* bs = Bs + (step % NS) * B_ST;
-#pragma unroll
-    for (int j = 0; j < TN; ++j) b[j] = frag(bs, brow[j], kk);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) a[i] = frag(as, arow[i], kk);
-  };
-  // MFMAs [lo, hi) of one k16 phase, in (i, j) order.
-  auto mfma_range = [&](const bf16x8_t* a, const bf16x8_t* b, int lo, int hi)
-      __attribute__((always_inline)) {
-#pragma unroll
-    for (int t = 0; t < TM * TN; ++t)
-      if (t >= lo && t < hi)
-        acc[t / TN][t % TN] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[t % TN], a[t / TN], acc[t / TN][t % TN],
-                                                    0, 0, 0);
-  };
-  read_frags(a0, b0, 0, 0);
+  read_frags(0, 0, 0);
   for (int kt = 0; kt + 1 < nk; ++kt) {
-    mfma_range(a0, b0, 0, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(a1, b1, kt, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_range(a0, b0, 1, TM * TN);
-    // step kt+1 must have landed; DMA of steps up to kt+NS-2 may stay in flight
-    if (kt + NS - 2 < nk) wait_vmcnt<(NS - 3) * LPS>(); else wait_vmcnt<0>();
+    kstep(kt & 1, true, kt + 1);
+    // k-step kt+1 has landed (this wave's DMA) and every wave is past its reads of
+    // stage kt&1; the barrier publishes the DMA of all waves
+    wait_vmcnt<0>();
     lds_barrier();
-    if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_range(a1, b1, 0, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(a0, b0, kt + 1, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_range(a1, b1, 1, TM * TN);
+    read_frags(0, (kt + 1) & 1, 0);
   }
-  read_frags(a1, b1, nk - 1, 1);
-  mfma_range(a0, b0, 0, TM * TN);
-  mfma_range(a1, b1, 0, TM * TN);
+  kstep((nk - 1) & 1, false, 0);
   __syncthreads();
 
   // Epilogue. acc[i][j][q]: token row wm*WTM + i*32 + (lane&31); output column
@@ -361,23 +353,23 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnSched* __restrict__ sc, 
   }
 }
 
-template <int BM, int BN, bool GATED, int NS>
+template <int BM, int BN, bool GATED>
 constexpr size_t bf16_lds_bytes() {
-  constexpr size_t ops = (size_t)NS * (BM + BN) * 4 * 16;
+  constexpr size_t ops = 2 * (size_t)(BM + BN) * 8 * 16;
   constexpr size_t stg = (size_t)BM * ((GATED ? BN / 2 : BN) * 2 + 16);
   return ops > stg ? ops : stg;
 }
 
 // Two kernel names, so profiles tell the gate/up GEMM from the down projection.
-template <int BM, int BN, int WM, int WN, int NS>
+template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(256) void ffn_gate_up_bf16(const FfnSched* __restrict__ sc, int h) {
-  __shared__ uint4 smem[bf16_lds_bytes<BM, BN, true, NS>() / 16];
-  gemm_bf16_body<BM, BN, WM, WN, true, NS>(sc, h, smem);
+  __shared__ uint4 smem[bf16_lds_bytes<BM, BN, true>() / 16];
+  gemm_bf16_body<BM, BN, WM, WN, true>(sc, h, smem);
 }
-template <int BM, int BN, int WM, int WN, int NS>
+template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(256) void ffn_down_bf16(const FfnSched* __restrict__ sc, int h) {
-  __shared__ uint4 smem[bf16_lds_bytes<BM, BN, false, NS>() / 16];
-  gemm_bf16_body<BM, BN, WM, WN, false, NS>(sc, h, smem);
+  __shared__ uint4 smem[bf16_lds_bytes<BM, BN, false>() / 16];
+  gemm_bf16_body<BM, BN, WM, WN, false>(sc, h, smem);
 }
 
 // fp32 grouped GEMM: 64 x 64 tiles (gated: 32 gate + 32 up columns), 4x4 per thread.
@@ -458,18 +450,18 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32(const FfnSched* __restrict__
 // Tile shapes chosen from the expected rows per local expert, T*K/E.
 enum class Tiles { Large, Medium, Small };
 
-template <int BM, int BN, int WM, int WN, int NS>
+template <int BM, int BN, int WM, int WN>
 bool launch_bf16_pair(const FfnSched* sc, int h, int64_t ub1, int64_t ub2, hipStream_t st,
                       hipEvent_t const* ev) {
   const int64_t g1 = (ub1 + kNumXcd - 1) / kNumXcd * kNumXcd;
   const int64_t g2 = (ub2 + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (g1 > 0)
-    hipLaunchKernelGGL((ffn_gate_up_bf16<BM, BN, WM, WN, NS>), dim3((unsigned)g1), dim3(256), 0,
+    hipLaunchKernelGGL((ffn_gate_up_bf16<BM, BN, WM, WN>), dim3((unsigned)g1), dim3(256), 0,
                        st, sc, h);
   if (hipGetLastError() != hipSuccess) return false;
   if (ev && hipEventRecord(ev[1], st) != hipSuccess) return false;
   if (g2 > 0)
-    hipLaunchKernelGGL((ffn_down_bf16<BM, BN, WM, WN, NS>), dim3((unsigned)g2), dim3(256), 0, st,
+    hipLaunchKernelGGL((ffn_down_bf16<BM, BN, WM, WN>), dim3((unsigned)g2), dim3(256), 0, st,
                        sc, h);
   return hipGetLastError() == hipSuccess;
 }
@@ -490,7 +482,7 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
   if (d.bf16) {
     const double per_expert = d.E > 0 ? (double)d.T * d.K / d.E : 0.0;
     tiles = per_expert >= 384 ? Tiles::Large : (per_expert >= 48 ? Tiles::Medium : Tiles::Small);
-    BM = tiles == Tiles::Large ? 256 : (tiles == Tiles::Medium ? 128 : 64);
+    BM = tiles == Tiles::Large ? 256 : (tiles == Tiles::Medium ? 128 : 32);
     BN1 = 128;   // output columns of the gated tile (256 B rows: 128 gate + 128 up)
     BN2 = 256;
   } else {
@@ -517,13 +509,13 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
   if (d.bf16) {
     switch (tiles) {
       case Tiles::Large:
-        ok = launch_bf16_pair<256, 256, 2, 2, 4>(sc, d.h, ub1, ub2, st, ev);
+        ok = launch_bf16_pair<256, 256, 2, 2>(sc, d.h, ub1, ub2, st, ev);
         break;
       case Tiles::Medium:
-        ok = launch_bf16_pair<128, 256, 2, 2, 4>(sc, d.h, ub1, ub2, st, ev);
+        ok = launch_bf16_pair<128, 256, 2, 2>(sc, d.h, ub1, ub2, st, ev);
         break;
       case Tiles::Small:
-        ok = launch_bf16_pair<64, 256, 1, 4, 4>(sc, d.h, ub1, ub2, st, ev);
+        ok = launch_bf16_pair<32, 256, 1, 4>(sc, d.h, ub1, ub2, st, ev);
         break;
     }
   } else {
