@@ -50,6 +50,51 @@ def _traffic(workload):
     return t.get("hbm_bytes_per_launch")
 
 
+CALIB_BYTES = 512 << 20   # the plain copy that scales rocprofv3's FETCH_SIZE / WRITE_SIZE
+
+
+def summarize_traffic(fetch_csv, write_csv, workload="mixtral_prefill"):
+    """Per-launch HBM bytes of the gate/up GEMM from two rocprofv3 --pmc runs of
+    `bench.py --calibrate-copy` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each
+    scaled by what the same counter reads for the CALIB_BYTES device copy in that run.
+    Writes the JSON that bench.py reports as roofline.traffic."""
+    import csv
+
+    def per_kernel(path, counter):
+        rows = []
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"],
+                                 float(r["Counter_Value"]) * 1024.0))
+        rows.sort()
+        first_gemm = min(d for d, n, _ in rows if "ffn_gate_up" in n)
+        # the calibration copy is the last device copy before the first layer call
+        copies = [v for d, n, v in rows if "copyBuffer" in n and d < first_gemm]
+        vals = {"gate_up": [v for _, n, v in rows if "ffn_gate_up" in n],
+                "down": [v for _, n, v in rows if "ffn_down" in n],
+                "copy": copies[-1:]}
+        return {k: (sum(x) / len(x) if x else None) for k, x in vals.items()}
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    f_scale = f["copy"] / CALIB_BYTES
+    w_scale = w["copy"] / CALIB_BYTES
+    out = {
+        "workload": workload,
+        "source_sha": _ffn_source_sha(),
+        "calibration": {"copy_bytes": CALIB_BYTES, "fetch_counter_bytes": f["copy"],
+                        "write_counter_bytes": w["copy"], "fetch_scale": f_scale,
+                        "write_scale": w_scale},
+        "gate_up": {"fetch_bytes": f["gate_up"] / f_scale, "write_bytes": w["gate_up"] / w_scale},
+        "down": {"fetch_bytes": f["down"] / f_scale, "write_bytes": w["down"] / w_scale},
+    }
+    out["hbm_bytes_per_launch"] = out["gate_up"]["fetch_bytes"] + out["gate_up"]["write_bytes"]
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def cpu_baseline(cfg, inp, n_tokens):
     """The fp64 oracle, untuned, on the first n_tokens tokens of the same workload."""
     import numpy as np
@@ -88,8 +133,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one device copy of a known size (counter calibration)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, workload=args.workload)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
         print(f"bench.py: this build runs one MoE layer on one GPU; --gpus {args.gpus} "
@@ -114,6 +165,12 @@ def main():
     npts = len(moe.TRACE_POINTS)
     ev = moe.HipEvents(npts * args.steps)
 
+    if args.calibrate_copy:
+        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         moe.moe_forward(p, t, b["ws"])
     torch.cuda.synchronize()
