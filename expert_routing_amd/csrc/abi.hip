@@ -76,6 +76,7 @@ int make_dims(const moe_problem* p, Dims* d) {
   d->sh_rows = p->n_shared ? d->tpr : 0;
   d->s = bf16 ? 2 : 4;
   d->bf16 = bf16;
+  d->route_split = route_split(*d);
   return MOE_OK;
 }
 
@@ -85,7 +86,7 @@ WsLayout ws_layout(const moe_problem* p, const Dims& d) {
   WsLayout L;
   size_t off = 0;
   const size_t n_chunks = (size_t)((d.T + kDispatchChunk - 1) / kDispatchChunk);
-  L.logits = off;       off = align256(off + (size_t)d.T * d.E * 4);
+  L.logits = off;       off = align256(off + (size_t)d.route_split * d.T * d.E * 4);
   L.chunk_counts = off; off = align256(off + n_chunks * d.E * 4);
   L.chunk_base = off;   off = align256(off + n_chunks * d.E * 4);
   L.kept = off;         off = align256(off + (size_t)d.E * 4);

@@ -149,6 +149,8 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 // of bank conflicts whether the LDS serves 8 or 16 lanes per cycle.
 __device__ __forceinline__ int row_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
+constexpr int kDmaStride = 2;   // MFMAs per interleaved DMA instruction
+
 // s_waitcnt immediate for vmcnt(n) with the other counters left open (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -276,7 +278,8 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnSched* __restrict__ sc, 
   // One k-step: four k16 phases. A phase runs one MFMA (its fragments were read a phase
   // earlier, so the compiler's full LDS wait there is free), reads the next phase's
   // fragments, then its other MFMAs. With `dma`, the next k-step's DMA rides along one
-  // instruction per MFMA (never a burst of VMEM issues the wave would block on).
+  // instruction every kDmaStride MFMAs: a burst of VMEM issues would block the wave, and
+  // one per MFMA (measured) outruns what the address units accept from four waves.
   auto kstep = [&](int stage, bool dma, int next_step) __attribute__((always_inline)) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -286,7 +289,8 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnSched* __restrict__ sc, 
         acc[t / TN][t % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             fb[cur][t % TN], fa[cur][t / TN], acc[t / TN][t % TN], 0, 0, 0);
         const int slot = kk * NMF + t;            // MFMA index within the k-step
-        if (dma && slot >= 1 && slot - 1 < LPS) issue_one(next_step, stage ^ 1, slot - 1);
+        if (dma && slot >= 1 && (slot - 1) % kDmaStride == 0 && (slot - 1) / kDmaStride < LPS)
+          issue_one(next_step, stage ^ 1, (slot - 1) / kDmaStride);
         if (t == 0 && kk < 3) {
           __builtin_amdgcn_sched_barrier(0);
           read_frags(cur ^ 1, stage, kk + 1);
@@ -294,9 +298,9 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnSched* __restrict__ sc, 
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (dma) {   // instructions left over when the k-step has fewer MFMAs than DMAs
+    if (dma) {   // instructions left over when the k-step has too few MFMAs
 #pragma unroll
-      for (int x = 4 * NMF - 1; x < LPS; ++x) issue_one(next_step, stage ^ 1, x);
+      for (int x = (4 * NMF - 2) / kDmaStride + 1; x < LPS; ++x) issue_one(next_step, stage ^ 1, x);
     }
   };
 

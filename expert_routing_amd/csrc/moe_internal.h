@@ -40,6 +40,7 @@ struct Dims {
   int64_t sh_rows;  // shared-expert rows (T/N or 0)
   int s;            // activation bytes
   bool bf16;
+  int route_split;  // K-slices of the router GEMM (partial logits summed in order)
 };
 
 // Workspace carve-up (byte offsets from ws, each 256-aligned).
@@ -54,6 +55,7 @@ struct WsLayout {
 };
 
 int make_dims(const moe_problem* p, Dims* d);
+int route_split(const Dims& d);   // defined with the router kernels
 WsLayout ws_layout(const moe_problem* p, const Dims& d);
 
 // Stage launchers (arguments already validated; return MOE_OK or MOE_ERR_LAUNCH).

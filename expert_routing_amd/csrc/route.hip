@@ -36,7 +36,7 @@ template <int BE>
 __global__ __launch_bounds__(256) void router_gemm_bf16(const bf16_t* __restrict__ x,
                                                         const float* __restrict__ w,
                                                         float* __restrict__ logits,
-                                                        int T, int h, int E) {
+                                                        int T, int h, int E, int kslice) {
   __shared__ uint4 xs[RT_BM * 8];           // [64 rows][8 chunks]
   __shared__ uint4 wsm[3][BE * 8];          // hi / mid / lo planes, [BE rows][8 chunks]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -47,8 +47,11 @@ __global__ __launch_bounds__(256) void router_gemm_bf16(const bf16_t* __restrict
   floatx4 acc[NEG];
 #pragma unroll
   for (int i = 0; i < NEG; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // K-slice blockIdx.z of the reduction; its partial logits go to slab z
+  const int kb = blockIdx.z * kslice, ke = kb + kslice < h ? kb + kslice : h;
+  logits += (size_t)blockIdx.z * T * E;
 
-  for (int k0 = 0; k0 < h; k0 += RT_BK) {
+  for (int k0 = kb; k0 < ke; k0 += RT_BK) {
     // x tile: 64 rows x 8 chunks = 512 chunks, 2 per thread
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -109,19 +112,21 @@ __global__ __launch_bounds__(256) void router_gemm_bf16(const bf16_t* __restrict
 __global__ __launch_bounds__(256) void router_gemm_f32(const float* __restrict__ x,
                                                        const float* __restrict__ w,
                                                        float* __restrict__ logits,
-                                                       int T, int h, int E) {
+                                                       int T, int h, int E, int kslice) {
   constexpr int BK = 16;
   __shared__ float xs[BK][64 + 4];
   __shared__ float wsm[BK][64 + 4];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
   float acc[4][4] = {};
-  for (int k0 = 0; k0 < h; k0 += BK) {
+  const int kb = blockIdx.z * kslice, ke = kb + kslice < h ? kb + kslice : h;
+  logits += (size_t)blockIdx.z * T * E;
+  for (int k0 = kb; k0 < ke; k0 += BK) {
     for (int id = tid; id < 64 * BK; id += 256) {
       int r = id / BK, k = id % BK;
       int t = t0 + r, e = e0 + r, kk = k0 + k;
-      xs[k][r] = (t < T && kk < h) ? x[(size_t)t * h + kk] : 0.f;
-      wsm[k][r] = (e < E && kk < h) ? w[(size_t)e * h + kk] : 0.f;
+      xs[k][r] = (t < T && kk < ke) ? x[(size_t)t * h + kk] : 0.f;
+      wsm[k][r] = (e < E && kk < ke) ? w[(size_t)e * h + kk] : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(256) void select_topk(const float* __restrict__ log
                                                    int32_t* __restrict__ ids,
                                                    float* __restrict__ wout, int T, int E,
                                                    int K, int score, int renorm, int n_groups,
-                                                   int topk_groups) {
+                                                   int topk_groups, int nsplit) {
   __shared__ float keys_s[SEL_TOK][512];
   __shared__ float gscore_s[SEL_TOK][512];
   __shared__ int gallow_s[SEL_TOK][512];
@@ -174,6 +179,7 @@ __global__ __launch_bounds__(256) void select_topk(const float* __restrict__ log
     float l = -INFINITY, k = -INFINITY, r = 0.f;
     if (active && j < kpl && e < E) {
       l = logits[t * E + e];
+      for (int z = 1; z < nsplit; ++z) l += logits[(size_t)z * T * E + t * E + e];  // in order
       const float b = bias ? bias[e] : 0.f;
       if (score == MOE_SCORE_SOFTMAX) {
         l += b;
@@ -296,37 +302,58 @@ __global__ __launch_bounds__(256) void select_topk(const float* __restrict__ log
 
 }  // namespace
 
-int launch_select(const moe_problem* p, const Dims& d, const float* logits, const float* bias,
-                  int32_t* ids, float* w, hipStream_t st) {
+// K-slices of the router GEMM: enough blocks to fill the chip (about 512), slices of at
+// least 256 along h (a multiple of the 64-wide k-step).
+int route_split(const Dims& d) {
+  const int64_t tiles = ((d.T + RT_BM - 1) / RT_BM) *
+                        ((d.E + 63) / 64 > 0 ? (d.E + 63) / 64 : 1);
+  int s = tiles > 0 ? (int)((512 + tiles - 1) / tiles) : 1;
+  const int smax = d.h / 256 > 1 ? d.h / 256 : 1;
+  s = s < 1 ? 1 : (s > smax ? smax : s);
+  return s;
+}
+
+static int select_with(const moe_problem* p, const Dims& d, const float* logits, int nsplit,
+                       const float* bias, int32_t* ids, float* w, hipStream_t st) {
   const unsigned grid = (unsigned)((d.T + SEL_TOK - 1) / SEL_TOK);
   hipLaunchKernelGGL(select_topk, dim3(grid), dim3(256), 0, st, logits, bias, ids, w,
-                     (int)d.T, d.E, d.K, p->score, p->renorm, p->n_groups, p->topk_groups);
+                     (int)d.T, d.E, d.K, p->score, p->renorm, p->n_groups, p->topk_groups,
+                     nsplit);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+int launch_select(const moe_problem* p, const Dims& d, const float* logits, const float* bias,
+                  int32_t* ids, float* w, hipStream_t st) {
+  return select_with(p, d, logits, 1, bias, ids, w, st);
 }
 
 int launch_route(const moe_problem* p, const Dims& d, const void* x, const float* w_router,
                  const float* bias, int32_t* ids, float* w, float* logits, hipStream_t st) {
   const unsigned gt = (unsigned)((d.T + RT_BM - 1) / RT_BM);
+  const int S = d.route_split;
+  // k-slice length: a multiple of 64 covering h in S slices
+  const int kslice = ((d.h + S - 1) / S + 63) / 64 * 64;
+  const unsigned gz = (unsigned)((d.h + kslice - 1) / kslice);
   if (d.bf16) {
     const int be = d.E <= 16 ? 16 : (d.E <= 32 ? 32 : 64);
-    const dim3 grid(gt, (unsigned)((d.E + be - 1) / be));
+    const dim3 grid(gt, (unsigned)((d.E + be - 1) / be), gz);
     const bf16_t* xb = static_cast<const bf16_t*>(x);
     if (be == 16)
       hipLaunchKernelGGL(router_gemm_bf16<16>, grid, dim3(256), 0, st, xb, w_router, logits,
-                         (int)d.T, d.h, d.E);
+                         (int)d.T, d.h, d.E, kslice);
     else if (be == 32)
       hipLaunchKernelGGL(router_gemm_bf16<32>, grid, dim3(256), 0, st, xb, w_router, logits,
-                         (int)d.T, d.h, d.E);
+                         (int)d.T, d.h, d.E, kslice);
     else
       hipLaunchKernelGGL(router_gemm_bf16<64>, grid, dim3(256), 0, st, xb, w_router, logits,
-                         (int)d.T, d.h, d.E);
+                         (int)d.T, d.h, d.E, kslice);
   } else {
-    const dim3 grid(gt, (unsigned)((d.E + 63) / 64));
+    const dim3 grid(gt, (unsigned)((d.E + 63) / 64), gz);
     hipLaunchKernelGGL(router_gemm_f32, grid, dim3(256), 0, st, static_cast<const float*>(x),
-                       w_router, logits, (int)d.T, d.h, d.E);
+                       w_router, logits, (int)d.T, d.h, d.E, kslice);
   }
   if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
-  return launch_select(p, d, logits, bias, ids, w, st);
+  return select_with(p, d, logits, (int)gz, bias, ids, w, st);
 }
 
 }  // namespace moe
