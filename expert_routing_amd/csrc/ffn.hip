@@ -17,6 +17,8 @@ namespace {
 
 constexpr int G_MAX = 513;       // local experts (<= 512) + shared expert
 constexpr int G_PAD = 520;
+constexpr int kMaxSplit = 4;     // k-slices of a tile in an XCD's last, partial round
+constexpr int kCuPerXcdMax = 32; // MI355X: 256 CUs in 8 XCDs
 
 struct FfnGroup {
   const void* A1;  // [rows][h]
@@ -26,13 +28,19 @@ struct FfnGroup {
   void* C2;        // [rows][h]
   int rows;
   int inter;
+  int mt;     // m-tiles
+  int tall;   // 1: the last m-tile also takes the (short) remainder: BM + tall_extra rows,
+              // split into tall_split narrower tiles per n-tile
 };
 
 struct FfnSched {
   int n_groups;
   int total1;
   int total2;
-  int pad_;
+  int tall_split;
+  int cu_per_xcd;   // CUs of one XCD (one round of blocks there)
+  int split_max;    // 1: no split-K; else the most k-slices a tile may take
+  int pad2_[2];
   int start1[G_PAD];
   int start2[G_PAD];
   FfnGroup g[G_MAX];
@@ -47,7 +55,8 @@ __global__ __launch_bounds__(1024) void ffn_prep(FfnSched* __restrict__ sc,
                                                  char* y_sh, int El, int has_shared,
                                                  int64_t sh_rows, int64_t sh_t0, int h, int inter,
                                                  int sh_inter, int64_t R_max, int s, int BM,
-                                                 int BN1, int BN2) {
+                                                 int tall_extra, int tall_split, int BN1,
+                                                 int BN2, int cu_per_xcd, int split_max) {
   __shared__ int s1[1024], s2[1024];
   const int g = threadIdx.x;
   const int G = El + has_shared;
@@ -73,12 +82,20 @@ __global__ __launch_bounds__(1024) void ffn_prep(FfnSched* __restrict__ sc,
       fg.B2 = w2_sh;
       fg.C2 = y_sh;
     }
+    // A remainder of at most tall_extra rows rides on the expert's last full tile (it
+    // reads the same weights) instead of costing a tile of its own.
+    const int q = rows / BM, r = rows % BM;
+    const int tall = q >= 1 && r > 0 && r <= tall_extra;
+    const int mt = tall ? q : (rows + BM - 1) / BM;
     fg.rows = rows;
     fg.inter = I;
+    fg.mt = mt;
+    fg.tall = tall;
     sc->g[g] = fg;
-    const int mt = (rows + BM - 1) / BM;
-    t1 = mt * ((I + BN1 - 1) / BN1);
-    t2 = mt * ((h + BN2 - 1) / BN2);
+    // per n-tile: mt tiles, or mt - 1 full ones and tall_split tall ones
+    const int per_n = tall ? mt - 1 + tall_split : mt;
+    t1 = per_n * ((I + BN1 - 1) / BN1);
+    t2 = per_n * ((h + BN2 - 1) / BN2);
   }
   s1[g] = t1;
   s2[g] = t2;
@@ -97,32 +114,94 @@ __global__ __launch_bounds__(1024) void ffn_prep(FfnSched* __restrict__ sc,
   }
   if (g == 0) {
     sc->n_groups = G;
+    sc->tall_split = tall_split;
+    sc->cu_per_xcd = cu_per_xcd;
+    sc->split_max = split_max;
     sc->total1 = s1[G - 1];
     sc->total2 = s2[G - 1];
   }
 }
 
-// Tile lookup shared by the GEMM kernels. Returns false for blocks with no tile.
-__device__ __forceinline__ bool find_tile(const FfnSched* sc, bool first, int BM, int& g,
-                                          int& m_tile, int& n_tile) {
+// Tile lookup shared by the GEMM kernels. The tile list is dealt to the XCDs in
+// contiguous ranges (consecutive tiles of an expert share its weights in one L2); an
+// XCD runs its range in rounds of cu_per_xcd blocks. When the last round would leave
+// at least half of the XCD idle, each of its tiles is cut into S k-slices (split-K):
+// the slices store fp32 partial sums that a second kernel adds in slice order.
+struct TileRef {
+  int g, m_tile, n_tile;
+  int tall;     // 0: full tile; 1 + s: part s of the expert's tall last tile
+  int slice;    // k-slice of a split tile, else 0
+  int nslice;   // k-slices of the tile (1: not split)
+  int piece;    // partial-sum slot of a split tile, else -1
+};
+
+struct XcdPlan {
+  int base, cnt;     // the XCD's tiles: [base, base + cnt)
+  int full, rem, S;  // whole rounds, tiles left for the last round, k-slices each
+};
+
+__device__ __forceinline__ XcdPlan xcd_plan(const FfnSched* sc, bool first, int xcd) {
   const int total = first ? sc->total1 : sc->total2;
-  const int* start = first ? sc->start1 : sc->start2;
   const int per = (total + kNumXcd - 1) / kNumXcd;
-  const int xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
-  if (slot >= per) return false;
-  const int L = xcd * per + slot;
-  if (L >= total) return false;
+  XcdPlan q;
+  q.base = xcd * per;
+  q.cnt = max(0, min(per, total - q.base));
+  const int cpx = sc->cu_per_xcd;
+  q.full = q.cnt / cpx * cpx;
+  q.rem = q.cnt - q.full;
+  q.S = 1;
+  if (sc->split_max > 1 && q.rem > 0 && 2 * q.rem <= cpx) q.S = min(sc->split_max, cpx / q.rem);
+  return q;
+}
+
+// Expert, m-tile, n-tile and tall part of tile L.
+__device__ __forceinline__ void locate(const FfnSched* sc, bool first, int L, TileRef& t) {
+  const int* start = first ? sc->start1 : sc->start2;
   int lo = 0, hi = sc->n_groups;          // start[lo] <= L < start[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (start[mid] <= L) lo = mid; else hi = mid;
   }
-  g = lo;
-  const int rows = sc->g[g].rows;
-  const int mt = (rows + BM - 1) / BM;
-  const int local = L - start[g];
-  m_tile = local % mt;
-  n_tile = local / mt;
+  t.g = lo;
+  const int mt = sc->g[lo].mt;
+  const int local = L - start[lo];
+  if (sc->g[lo].tall) {
+    const int per_n = mt - 1 + sc->tall_split;
+    const int w = local % per_n;
+    t.n_tile = local / per_n;
+    t.m_tile = w < mt - 1 ? w : mt - 1;
+    t.tall = w < mt - 1 ? 0 : 1 + w - (mt - 1);
+  } else {
+    t.m_tile = local % mt;
+    t.n_tile = local / mt;
+    t.tall = 0;
+  }
+}
+
+__device__ __forceinline__ bool find_tile(const FfnSched* sc, bool first, TileRef& t) {
+  const int xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
+  const XcdPlan q = xcd_plan(sc, first, xcd);
+  int L;
+  t.slice = 0;
+  t.nslice = 1;
+  t.piece = -1;
+  if (slot < q.full || q.S == 1) {
+    if (slot >= q.cnt) return false;
+    L = q.base + slot;
+  } else {
+    const int p = slot - q.full;
+    if (p >= q.rem * q.S) return false;
+    L = q.base + q.full + p % q.rem;
+    t.slice = p / q.rem;
+    t.nslice = q.S;
+    t.piece = xcd * sc->cu_per_xcd + p;
+  }
+  locate(sc, first, L, t);
+  if (t.tall && t.nslice > 1) {   // tall parts are not split: slice 0 takes all of K
+    if (t.slice > 0) return false;
+    t.nslice = 1;
+    t.piece = -1;
+  }
   return true;
 }
 
@@ -151,6 +230,8 @@ __device__ __forceinline__ int row_swz(int r) { return (r & 7) ^ ((r >> 3) & 1);
 
 constexpr int kDmaStride = 2;   // MFMAs per interleaved DMA instruction
 
+constexpr int kLdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
+
 // s_waitcnt immediate for vmcnt(n) with the other counters left open (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -162,39 +243,90 @@ __device__ __forceinline__ void wait_vmcnt() {
 // also wait for LDS DMA still in flight); callers wait for the DMA they need first.
 __device__ __forceinline__ void lds_barrier() { __builtin_amdgcn_s_barrier(); }
 
+// Epilogue of a bf16 tile. acc[i][j][q]: token row wm*WTM + i*32 + (lane&31); output
+// column (col-tile base) + 8*(q>>2) + 4*(lane>>5) + (q&3). Stages bf16 in LDS (the
+// caller has finished with the operand stages and synchronised), then stores 16-byte
+// row-contiguous chunks. GATED: out = silu(gate) * up, gate col-tiles first.
+template <int BM, int BN, int WM, int WN, bool GATED>
+__device__ __forceinline__ void store_tile(const floatx16 (&acc)[BM / WM / 32][BN / WN / 32],
+                                           const FfnGroup& fg, int m0, int n0, int h,
+                                           uint4* __restrict__ smem) {
+  constexpr int NT = 64 * WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int BNO = GATED ? BN / 2 : BN;
+  constexpr int PITCH = BNO * 2 + 16;                  // bytes per staged row
+  static_assert((size_t)BM * PITCH <= (size_t)kLdsBytes, "staged tile fits the LDS");
+  const int rows = fg.rows;
+  const int Nout = GATED ? fg.inter : h;
+  bf16_t* C = static_cast<bf16_t*>(GATED ? fg.C1 : fg.C2);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  char* stage = reinterpret_cast<char*>(smem);
+  constexpr int TNO = GATED ? TN / 2 : TN;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int row = wm * WTM + i * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < TNO; ++j) {
+      const int cbase = (GATED ? wn * (WTN / 2) : wn * WTN) + j * 32 + 4 * (lane >> 5);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int q = q4 * 4 + u;
+          v[u] = GATED ? silu(acc[i][j][q]) * acc[i][j + TN / 2][q] : acc[i][j][q];
+        }
+        bf16x4_t pk = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        *reinterpret_cast<bf16x4_t*>(stage + row * PITCH + (cbase + 8 * q4) * 2) = pk;
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int RCH = BNO / 8;                         // 16-byte chunks per row
+  for (int id = tid; id < BM * RCH; id += NT) {
+    const int r = id / RCH, cc = id % RCH;
+    const int gr = m0 + r, gc = n0 + cc * 8;
+    if (gr < rows && gc < Nout)
+      *reinterpret_cast<uint4*>(C + (size_t)gr * Nout + gc) =
+          *reinterpret_cast<const uint4*>(stage + r * PITCH + cc * 16);
+  }
+}
+
 // bf16 grouped GEMM. Block tile BM x BN (BN counts weight rows: for GATED half gate,
-// half up), k-step 64, 4 waves in a WM x WN grid, each wave (BM/WM) x (BN/WN) as 32x32
-// MFMA tiles. Operand tiles stream into two LDS stages by buffer->LDS DMA (no register
+// half up), k-step 64, WM x WN waves (4 or 8), each wave (BM/WM) x (BN/WN) as 32x32
+// MFMA tiles. With 8 waves two share each SIMD, so one wave's MFMAs keep the matrix
+// core busy while the other waits to issue its memory instructions. Operand tiles stream into two LDS stages by buffer->LDS DMA (no register
 // staging) one k-step ahead of the MFMAs. Every DMA request covers whole 128-byte row
 // segments (half-line requests roughly halve what L2 can deliver per CU). The MFMA takes
 // the weight fragment first, so a lane's accumulators hold 4 consecutive output columns.
 template <int BM, int BN, int WM, int WN, bool GATED>
-__device__ __forceinline__ void gemm_bf16_body(const FfnSched* __restrict__ sc, int h,
-                                               uint4* __restrict__ smem) {
-  static_assert(WM * WN == 4, "4 waves");
+__device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n0, int h,
+                                               uint4* __restrict__ smem, int slice,
+                                               int nslice, float* __restrict__ part) {
+  constexpr int NW = WM * WN, NT = 64 * NW;
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(TM >= 1 && TN >= 1, "tile");
   static_assert(!GATED || TN % 2 == 0, "gated needs gate/up pairs");
-  static_assert(BM % 32 == 0 && BN % 32 == 0, "DMA rows split evenly over 4 waves");
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "DMA rows split evenly over waves");
   constexpr int BNO = GATED ? BN / 2 : BN;          // output columns per tile
-  constexpr int AI = BM / 32, BI = BN / 32;         // DMA instructions per wave per stage
+  constexpr int AI = BM / (8 * NW), BI = BN / (8 * NW);  // DMA instructions per wave per stage
   constexpr int LPS = AI + BI;
   constexpr int A_ST = BM * 8, B_ST = BN * 8;       // uint4 per stage
   constexpr int NMF = TM * TN;                      // MFMAs per k16 phase
   uint4* As = smem;                                 // [2][BM rows][8 chunks]
   uint4* Bs = smem + 2 * A_ST;                      // [2][BN rows][8 chunks]
 
-  int g, m_tile, n_tile;
-  if (!find_tile(sc, GATED, BM, g, m_tile, n_tile)) return;
-  const FfnGroup fg = sc->g[g];
   const int rows = fg.rows, I = fg.inter;
   const bf16_t* A = static_cast<const bf16_t*>(GATED ? fg.A1 : fg.C1);
   const bf16_t* B = static_cast<const bf16_t*>(GATED ? fg.B1 : fg.B2);
   bf16_t* C = static_cast<bf16_t*>(GATED ? fg.C1 : fg.C2);
   const int Kd = GATED ? h : I;         // reduction length = lda = ldb
   const int Nout = GATED ? I : h;       // output columns = ldc
-  const int m0 = m_tile * BM, n0 = n_tile * BNO;
   const uint32_t b_rows = GATED ? 2 * I : h;
   const __amdgpu_buffer_rsrc_t ra_rs = make_rsrc(A, (uint32_t)rows * Kd * 2);
   const __amdgpu_buffer_rsrc_t rb_rs = make_rsrc(B, b_rows * (uint32_t)Kd * 2);
@@ -204,40 +336,36 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnSched* __restrict__ sc, 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
-  // DMA: instruction j of this wave fills tile rows 8*(4*j+wave) .. +8; lane L lands on
-  // row +L/8, slot L&7, so it fetches logical chunk (L&7) ^ row_swz(row).
+  // DMA: instruction j of this wave fills tile rows 8*(NW*j+wave) .. +8; lane L lands on
+  // row +L/8, slot L&7, so it fetches logical chunk (L&7) ^ row_swz(row) (NW is even, so
+  // bit 3 of the row is wave&1). The lane part of the source offset sits in one VGPR per
+  // operand (two for the gated B: gate rows and up rows); the rest is uniform (soffset).
+  // Rows past an operand's end read as zero; for the gated B, gate rows past I read up
+  // rows, which only feed output columns past I that are never stored.
   const int dr = lane >> 3;
   const int dc = (lane & 7) ^ dr ^ (wave & 1);
-  uint32_t a_off[AI], b_off[BI];
-#pragma unroll
-  for (int j = 0; j < AI; ++j) {
-    const int r = 8 * (4 * j + wave) + dr;
-    a_off[j] = ((uint32_t)(m0 + r) * Kd + dc * 8) * 2;
-  }
-#pragma unroll
-  for (int j = 0; j < BI; ++j) {
-    const int r = 8 * (4 * j + wave) + dr;
-    uint32_t wrow;
-    if (GATED) {
-      const bool up = r >= BN / 2;
-      int col = n0 + (up ? r - BN / 2 : r);
-      col = col < I ? col : I - 1;
-      wrow = col + (up ? I : 0);
-    } else {
-      wrow = n0 + r;
-    }
-    b_off[j] = (wrow * (uint32_t)Kd + dc * 8) * 2;
-  }
+  const uint32_t a_lane = ((uint32_t)(m0 + 8 * wave + dr) * Kd + dc * 8) * 2;
+  const uint32_t b_lane = ((uint32_t)(n0 + 8 * wave + dr) * Kd + dc * 8) * 2;
+  const uint32_t b_lane_up = GATED ? b_lane + (uint32_t)I * Kd * 2 : b_lane;
+  const uint32_t x_stride = (uint32_t)(8 * NW) * Kd * 2;   // bytes between instructions
+  constexpr int BH = GATED ? BI / 2 : BI;                   // instructions per B half
   // DMA instruction `x` (0 <= x < LPS) of k-step `step` into stage `stage`.
+  // k-steps [kb, kb + nk) of the Kd / 64: all of them, or this tile's k-slice (wave-
+  // uniform values, kept in SGPRs: the DMA takes the k offset as soffset)
+  const int kb = __builtin_amdgcn_readfirstlane(slice * (Kd / 64) / nslice);
+  const int nk = __builtin_amdgcn_readfirstlane((slice + 1) * (Kd / 64) / nslice) - kb;
   auto issue_one = [&](int step, int stage, int x) __attribute__((always_inline)) {
-    const uint32_t soff = (uint32_t)step * 128;
+    const uint32_t soff = (uint32_t)(kb + step) * 128;
     if (x < AI) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra_rs, LDS_PTR(As + stage * A_ST + 64 * (4 * x + wave)), 16, a_off[x], soff, 0, 0);
+          ra_rs, LDS_PTR(As + stage * A_ST + 64 * (NW * x + wave)), 16, a_lane,
+          soff + x * x_stride, 0, 0);
     } else {
       const int y = x - AI;
+      const int yh = y % BH;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb_rs, LDS_PTR(Bs + stage * B_ST + 64 * (4 * y + wave)), 16, b_off[y], soff, 0, 0);
+          rb_rs, LDS_PTR(Bs + stage * B_ST + 64 * (NW * y + wave)), 16,
+          y < BH ? b_lane : b_lane_up, soff + yh * x_stride, 0, 0);
     }
   };
 
@@ -304,7 +432,7 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnSched* __restrict__ sc, 
     }
   };
 
-  const int nk = Kd / 64;
+  if (nk > 0) {
 #pragma unroll
   for (int x = 0; x < LPS; ++x) issue_one(0, 0, x);
   wait_vmcnt<0>();
@@ -319,42 +447,24 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnSched* __restrict__ sc, 
     read_frags(0, (kt + 1) & 1, 0);
   }
   kstep((nk - 1) & 1, false, 0);
+  }
   __syncthreads();
 
-  // Epilogue. acc[i][j][q]: token row wm*WTM + i*32 + (lane&31); output column
-  // (col-tile base) + 8*(q>>2) + 4*(lane>>5) + (q&3). Stage bf16 in LDS, then 16-byte
-  // row-contiguous stores.
-  constexpr int PITCH = BNO * 2 + 16;                  // bytes per staged row
-  char* stage = reinterpret_cast<char*>(smem);
-  constexpr int TNO = GATED ? TN / 2 : TN;
+  if (part) {
+    // fp32 partial sums of a k-slice, in fragment order (each store is 1 KB contiguous)
+    float4* dst = reinterpret_cast<float4*>(part) + (size_t)wave * TM * TN * 4 * 64 + lane;
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int row = wm * WTM + i * 32 + (lane & 31);
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TNO; ++j) {
-      const int cbase = (GATED ? wn * (WTN / 2) : wn * WTN) + j * 32 + 4 * (lane >> 5);
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        float v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int q = q4 * 4 + u;
-          v[u] = GATED ? silu(acc[i][j][q]) * acc[i][j + TN / 2][q] : acc[i][j][q];
-        }
-        bf16x4_t pk = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-        *reinterpret_cast<bf16x4_t*>(stage + row * PITCH + (cbase + 8 * q4) * 2) = pk;
-      }
-    }
+        for (int q4 = 0; q4 < 4; ++q4)
+          dst[((i * TN + j) * 4 + q4) * 64] =
+              make_float4(acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2],
+                          acc[i][j][4 * q4 + 3]);
+    return;
   }
-  __syncthreads();
-  constexpr int RCH = BNO / 8;                         // 16-byte chunks per row
-  for (int id = tid; id < BM * RCH; id += 256) {
-    const int r = id / RCH, cc = id % RCH;
-    const int gr = m0 + r, gc = n0 + cc * 8;
-    if (gr < rows && gc < Nout)
-      *reinterpret_cast<uint4*>(C + (size_t)gr * Nout + gc) =
-          *reinterpret_cast<const uint4*>(stage + r * PITCH + cc * 16);
-  }
+  store_tile<BM, BN, WM, WN, GATED>(acc, fg, m0, n0, h, smem);
 }
 
 template <int BM, int BN, bool GATED>
@@ -364,16 +474,96 @@ constexpr size_t bf16_lds_bytes() {
   return ops > stg ? ops : stg;
 }
 
-// Two kernel names, so profiles tell the gate/up GEMM from the down projection.
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(256) void ffn_gate_up_bf16(const FfnSched* __restrict__ sc, int h) {
-  __shared__ uint4 smem[bf16_lds_bytes<BM, BN, true>() / 16];
-  gemm_bf16_body<BM, BN, WM, WN, true>(sc, h, smem);
+template <size_t A, size_t B>
+constexpr size_t cmax() { return A > B ? A : B; }
+
+// Two kernel names, so profiles tell the gate/up GEMM from the down projection. A block
+// takes a BM x BN tile, or one of the parts of an expert's tall last tile: (BM + 32*WM)
+// rows (one more MFMA row per wave) by BN / TSPLIT, which keeps the accumulators within
+// the register file.
+template <int WM, int WN>
+constexpr int tall_split() { return WM > 1 ? 2 : 1; }
+
+template <int BM, int BN, int WM, int WN, bool GATED, bool TALL>
+__device__ __forceinline__ void gemm_bf16_tile(const FfnSched* __restrict__ sc, int h,
+                                               float* __restrict__ part,
+                                               uint4* __restrict__ smem) {
+  constexpr int BMT = BM + 32 * WM, TS = tall_split<WM, WN>(), BNT = BN / TS;
+  constexpr int BNO = GATED ? BN / 2 : BN;
+  TileRef t;
+  if (!find_tile(sc, GATED, t)) return;
+  const FfnGroup& fg = sc->g[t.g];
+  const int m0 = t.m_tile * BM, n0 = t.n_tile * BNO;
+  if (TALL && t.tall)
+    gemm_bf16_body<TALL ? BMT : BM, TALL ? BNT : BN, WM, WN, GATED>(
+        fg, m0, n0 + (t.tall - 1) * (BNO / TS), h, smem, 0, 1, nullptr);
+  else
+    gemm_bf16_body<BM, BN, WM, WN, GATED>(fg, m0, n0, h, smem, t.slice, t.nslice,
+                                          t.piece >= 0 ? part + (size_t)t.piece * BM * BN
+                                                       : nullptr);
 }
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(256) void ffn_down_bf16(const FfnSched* __restrict__ sc, int h) {
-  __shared__ uint4 smem[bf16_lds_bytes<BM, BN, false>() / 16];
-  gemm_bf16_body<BM, BN, WM, WN, false>(sc, h, smem);
+
+template <int BM, int BN, int WM, int WN, bool GATED, bool TALL>
+constexpr size_t tile_lds_bytes() {
+  return TALL ? cmax<bf16_lds_bytes<BM, BN, GATED>(),
+                     bf16_lds_bytes<BM + 32 * WM, BN / tall_split<WM, WN>(), GATED>()>()
+              : bf16_lds_bytes<BM, BN, GATED>();
+}
+
+template <int BM, int BN, int WM, int WN, bool TALL>
+__global__ __launch_bounds__(64 * WM * WN) void ffn_gate_up_bf16(const FfnSched* __restrict__ sc,
+                                                                 int h, float* part) {
+  __shared__ uint4 smem[tile_lds_bytes<BM, BN, WM, WN, true, TALL>() / 16];
+  gemm_bf16_tile<BM, BN, WM, WN, true, TALL>(sc, h, part, smem);
+}
+template <int BM, int BN, int WM, int WN, bool TALL>
+__global__ __launch_bounds__(64 * WM * WN) void ffn_down_bf16(const FfnSched* __restrict__ sc,
+                                                              int h, float* part) {
+  __shared__ uint4 smem[tile_lds_bytes<BM, BN, WM, WN, false, TALL>() / 16];
+  gemm_bf16_tile<BM, BN, WM, WN, false, TALL>(sc, h, part, smem);
+}
+
+// Second half of split-K: block (xcd, r) adds the k-slice partial sums of the XCD's
+// r-th last-round tile in slice order and runs the tile epilogue.
+template <int BM, int BN, int WM, int WN, bool GATED>
+__global__ __launch_bounds__(64 * WM * WN) void ffn_splitk_reduce(
+    const FfnSched* __restrict__ sc, int h, const float* __restrict__ part) {
+  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+  constexpr int BNO = GATED ? BN / 2 : BN;
+  __shared__ uint4 smem[(size_t)BM * (BNO * 2 + 16) / 16];
+  const int xcd = blockIdx.x % kNumXcd, r = blockIdx.x / kNumXcd;
+  const XcdPlan q = xcd_plan(sc, GATED, xcd);
+  if (q.S == 1 || r >= q.rem) return;
+  TileRef t;
+  locate(sc, GATED, q.base + q.full + r, t);
+  if (t.tall) return;                     // stored by its own block
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  floatx16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  for (int sl = 0; sl < q.S; ++sl) {
+    const float4* src = reinterpret_cast<const float4*>(
+                            part + (size_t)(xcd * sc->cu_per_xcd + sl * q.rem + r) * BM * BN) +
+                        (size_t)wave * TM * TN * 4 * 64 + lane;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 v = src[((i * TN + j) * 4 + q4) * 64];
+          acc[i][j][4 * q4] += v.x;
+          acc[i][j][4 * q4 + 1] += v.y;
+          acc[i][j][4 * q4 + 2] += v.z;
+          acc[i][j][4 * q4 + 3] += v.w;
+        }
+  }
+  store_tile<BM, BN, WM, WN, GATED>(acc, sc->g[t.g], t.m_tile * BM, t.n_tile * BNO, h, smem);
 }
 
 // fp32 grouped GEMM: 64 x 64 tiles (gated: 32 gate + 32 up columns), 4x4 per thread.
@@ -382,9 +572,9 @@ template <bool GATED>
 __global__ __launch_bounds__(256) void ffn_gemm_f32(const FfnSched* __restrict__ sc, int h) {
   __shared__ float As[F_BK][F_BM + 4];
   __shared__ float Bs[F_BK][F_BN + 4];
-  int g, m_tile, n_tile;
-  if (!find_tile(sc, GATED, F_BM, g, m_tile, n_tile)) return;
-  const FfnGroup fg = sc->g[g];
+  TileRef t;
+  if (!find_tile(sc, GATED, t)) return;
+  const FfnGroup fg = sc->g[t.g];
   const int rows = fg.rows, I = fg.inter;
   const float* A = static_cast<const float*>(GATED ? fg.A1 : fg.C1);
   const float* B = static_cast<const float*>(GATED ? fg.B1 : fg.B2);
@@ -392,7 +582,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32(const FfnSched* __restrict__
   const int Kd = GATED ? h : I;
   const int Nout = GATED ? I : h;
   constexpr int BNO = GATED ? F_BN / 2 : F_BN;
-  const int m0 = m_tile * F_BM, n0 = n_tile * BNO;
+  const int m0 = t.m_tile * F_BM, n0 = t.n_tile * BNO;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   float acc[4][4] = {};
   for (int k0 = 0; k0 < Kd; k0 += F_BK) {
@@ -454,19 +644,33 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32(const FfnSched* __restrict__
 // Tile shapes chosen from the expected rows per local expert, T*K/E.
 enum class Tiles { Large, Medium, Small };
 
-template <int BM, int BN, int WM, int WN>
-bool launch_bf16_pair(const FfnSched* sc, int h, int64_t ub1, int64_t ub2, hipStream_t st,
-                      hipEvent_t const* ev) {
-  const int64_t g1 = (ub1 + kNumXcd - 1) / kNumXcd * kNumXcd;
-  const int64_t g2 = (ub2 + kNumXcd - 1) / kNumXcd * kNumXcd;
-  if (g1 > 0)
-    hipLaunchKernelGGL((ffn_gate_up_bf16<BM, BN, WM, WN>), dim3((unsigned)g1), dim3(256), 0,
-                       st, sc, h);
+Tiles tile_kind(const Dims& d) {
+  const double per_expert = d.E > 0 ? (double)d.T * d.K / d.E : 0.0;
+  return per_expert >= 384 ? Tiles::Large : (per_expert >= 48 ? Tiles::Medium : Tiles::Small);
+}
+
+template <int BM, int BN, int WM, int WN, bool TALL>
+bool launch_bf16_pair(const FfnSched* sc, int h, int64_t ub1, int64_t ub2, int cpx, float* part,
+                      hipStream_t st, hipEvent_t const* ev) {
+  constexpr int NT = 64 * WM * WN;
+  // per XCD: its share of the tiles plus room for one round of k-slices
+  const int64_t g1 = ((ub1 + kNumXcd - 1) / kNumXcd + cpx) * kNumXcd;
+  const int64_t g2 = ((ub2 + kNumXcd - 1) / kNumXcd + cpx) * kNumXcd;
+  const unsigned gr = (unsigned)(kNumXcd * (cpx / 2));   // tiles that can be split
+  if (ub1 > 0) {
+    hipLaunchKernelGGL((ffn_gate_up_bf16<BM, BN, WM, WN, TALL>), dim3((unsigned)g1), dim3(NT), 0, st,
+                       sc, h, part);
+    hipLaunchKernelGGL((ffn_splitk_reduce<BM, BN, WM, WN, true>), dim3(gr), dim3(NT), 0, st, sc,
+                       h, part);
+  }
   if (hipGetLastError() != hipSuccess) return false;
   if (ev && hipEventRecord(ev[1], st) != hipSuccess) return false;
-  if (g2 > 0)
-    hipLaunchKernelGGL((ffn_down_bf16<BM, BN, WM, WN>), dim3((unsigned)g2), dim3(256), 0, st,
-                       sc, h);
+  if (ub2 > 0) {
+    hipLaunchKernelGGL((ffn_down_bf16<BM, BN, WM, WN, TALL>), dim3((unsigned)g2), dim3(NT), 0, st, sc,
+                       h, part);
+    hipLaunchKernelGGL((ffn_splitk_reduce<BM, BN, WM, WN, false>), dim3(gr), dim3(NT), 0, st, sc,
+                       h, part);
+  }
   return hipGetLastError() == hipSuccess;
 }
 
@@ -474,19 +678,39 @@ bool launch_bf16_pair(const FfnSched* sc, int h, int64_t ub1, int64_t ub2, hipSt
 
 size_t ffn_sched_bytes(const Dims&) { return sizeof(FfnSched); }
 
+size_t ffn_splitk_bytes(const Dims& d) {
+  if (!d.bf16) return 0;
+  const Tiles k = tile_kind(d);
+  const size_t tile = k == Tiles::Large ? 256 * 256 : (k == Tiles::Medium ? 128 * 256 : 32 * 256);
+  return (size_t)kNumXcd * kCuPerXcdMax * tile * 4;
+}
+
 int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_t* offsets,
                const void* w13, const void* w2, const void* x, const void* w13_sh,
                const void* w2_sh, void* yp, void* y_sh, char* ws, const WsLayout& L,
                hipStream_t st, hipEvent_t const* ev) {
   FfnSched* sc = reinterpret_cast<FfnSched*>(ws + L.sched);
+  float* part = reinterpret_cast<float*>(ws + L.splitk);
   const int has_sh = (p->n_shared && d.sh_rows > 0) ? 1 : 0;
   const int64_t sh_t0 = (int64_t)d.rank * d.tpr;
   Tiles tiles = Tiles::Large;
-  int BM, BN1, BN2;
+  int BM, BN1, BN2, tall_extra = 0, tall_split = 1, split_max = 1;
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return MOE_ERR_LAUNCH;
+  const int cpx = n_cu / kNumXcd < 1 ? 1 : (n_cu / kNumXcd > kCuPerXcdMax ? kCuPerXcdMax
+                                                                         : n_cu / kNumXcd);
   if (d.bf16) {
-    const double per_expert = d.E > 0 ? (double)d.T * d.K / d.E : 0.0;
-    tiles = per_expert >= 384 ? Tiles::Large : (per_expert >= 48 ? Tiles::Medium : Tiles::Small);
+    tiles = tile_kind(d);
+    int min_k = d.h < p->inter ? d.h : p->inter;
+    if (has_sh && p->shared_inter < min_k) min_k = p->shared_inter;
+    split_max = min_k / 64 < kMaxSplit ? min_k / 64 : kMaxSplit;
     BM = tiles == Tiles::Large ? 256 : (tiles == Tiles::Medium ? 128 : 32);
+    // 32 rows per wave row of the tile; halves of the tall tile when WM = 2. The 256-row
+    // tile takes no tall tiles: its (320 x 128) halves cost about as much as full tiles.
+    tall_extra = tiles == Tiles::Small ? 32 : (tiles == Tiles::Medium ? 64 : 0);
+    tall_split = tiles == Tiles::Medium ? 2 : 1;
     BN1 = 128;   // output columns of the gated tile (256 B rows: 128 gate + 128 up)
     BN2 = 256;
   } else {
@@ -497,11 +721,12 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
                      static_cast<const char*>(w2), static_cast<const char*>(x),
                      static_cast<const char*>(w13_sh), static_cast<const char*>(w2_sh),
                      ws + L.hbuf, static_cast<char*>(yp), static_cast<char*>(y_sh), d.El, has_sh,
-                     d.sh_rows, sh_t0, d.h, p->inter, p->shared_inter, d.R_max, d.s, BM, BN1,
-                     BN2);
+                     d.sh_rows, sh_t0, d.h, p->inter, p->shared_inter, d.R_max, d.s, BM,
+                     tall_extra, tall_split, BN1, BN2, cpx, split_max);
   if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
   if (ev && hipEventRecord(ev[0], st) != hipSuccess) return MOE_ERR_LAUNCH;
-  // Upper bound on m-tiles: sum_e ceil(rows_e / BM) <= R_max / BM + E_l.
+  // Upper bound on m-tiles: sum_e ceil(rows_e / BM) <= R_max / BM + E_l (an expert with a
+  // tall last tile has mt - 1 + tall_split <= ceil(rows_e / BM) tiles per n-tile).
   const int64_t mt_ub = d.R_max / BM + d.El;
   const int64_t mt_sh = has_sh ? (d.sh_rows + BM - 1) / BM : 0;
   const int64_t nt1 = (p->inter + BN1 - 1) / BN1;
@@ -513,13 +738,13 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
   if (d.bf16) {
     switch (tiles) {
       case Tiles::Large:
-        ok = launch_bf16_pair<256, 256, 2, 2>(sc, d.h, ub1, ub2, st, ev);
+        ok = launch_bf16_pair<256, 256, 2, 2, false>(sc, d.h, ub1, ub2, cpx, part, st, ev);
         break;
       case Tiles::Medium:
-        ok = launch_bf16_pair<128, 256, 2, 2>(sc, d.h, ub1, ub2, st, ev);
+        ok = launch_bf16_pair<128, 256, 2, 2, true>(sc, d.h, ub1, ub2, cpx, part, st, ev);
         break;
       case Tiles::Small:
-        ok = launch_bf16_pair<32, 256, 1, 4>(sc, d.h, ub1, ub2, st, ev);
+        ok = launch_bf16_pair<32, 256, 1, 4, true>(sc, d.h, ub1, ub2, cpx, part, st, ev);
         break;
     }
   } else {
@@ -527,7 +752,7 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
     const int64_t g2 = (ub2 + kNumXcd - 1) / kNumXcd * kNumXcd;
     if (g1 > 0)
       hipLaunchKernelGGL(ffn_gemm_f32<true>, dim3((unsigned)g1), dim3(256), 0, st, sc, d.h);
-    if (ev) hipEventRecord(ev[1], st);
+    if (ev && hipEventRecord(ev[1], st) != hipSuccess) return MOE_ERR_LAUNCH;
     if (g2 > 0)
       hipLaunchKernelGGL(ffn_gemm_f32<false>, dim3((unsigned)g2), dim3(256), 0, st, sc, d.h);
     ok = hipGetLastError() == hipSuccess;

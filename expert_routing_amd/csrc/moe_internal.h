@@ -51,6 +51,7 @@ struct WsLayout {
   size_t kept;          // [E_l] i32
   size_t sched;         // ffn tile schedule
   size_t hbuf;          // [R_max + sh_rows][I_max] act
+  size_t splitk;        // split-K partial sums (fp32), bf16 problems only
   size_t total;
 };
 
@@ -75,5 +76,6 @@ int launch_combine(const moe_problem* p, const Dims& d, const void* yp, const in
                    const float* w, const void* y_sh, void* y, hipStream_t st);
 
 size_t ffn_sched_bytes(const Dims& d);
+size_t ffn_splitk_bytes(const Dims& d);
 
 }  // namespace moe
