@@ -94,6 +94,7 @@ WsLayout ws_layout(const moe_problem* p, const Dims& d) {
   const int imax = p->inter > p->shared_inter ? p->inter : p->shared_inter;
   L.hbuf = off;         off = align256(off + (size_t)(d.R_max + d.sh_rows) * imax * d.s);
   L.splitk = off;       off = align256(off + ffn_splitk_bytes(d));
+  L.arrive = off;       off = align256(off + ffn_arrive_bytes(d));
   L.total = off;
   return L;
 }

@@ -1,6 +1,7 @@
 // Combine: y[t] = sum_k w[t,k] * yp[dest_row[t,k]] (+ y_sh[t - t0]) with fp32
 // accumulation in k order, one rounding to the activation dtype at the end.
-// One wave per token; each lane owns 16-byte column chunks of the row.
+// One wave per (token, row segment of 64*CB_CH 16-byte chunks); each lane owns chunks
+// of the segment, so small batches still spread over the chip.
 #include "moe_internal.h"
 
 namespace moe {
@@ -41,7 +42,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
     if (d >= 0) { rows[nk] = d; wk[nk] = w[t * K + k]; ++nk; }
   }
   const bool has_sh = ysh && t >= t0 && t < t1;
-  for (int base = 0; base < row_chunks; base += 64 * CB_CH) {
+  {
+    const int base = blockIdx.y * 64 * CB_CH;
     float acc[CB_CH][EPC];
 #pragma unroll
     for (int u = 0; u < CB_CH; ++u)
@@ -104,7 +106,7 @@ int launch_combine(const moe_problem* p, const Dims& d, const void* yp, const in
   const int row_chunks = d.h * d.s / 16;
   const int64_t t0 = p->n_shared ? (int64_t)d.rank * d.tpr : 0;
   const int64_t t1 = p->n_shared ? t0 + d.tpr : 0;
-  const dim3 grid((unsigned)((d.T + 3) / 4));
+  const dim3 grid((unsigned)((d.T + 3) / 4), (unsigned)((row_chunks + 64 * CB_CH - 1) / (64 * CB_CH)));
   if (d.bf16)
     hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, st,
                        static_cast<const uint4*>(yp), dest_row, w,

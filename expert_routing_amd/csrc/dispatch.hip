@@ -178,7 +178,8 @@ __global__ __launch_bounds__(256) void disp_fill(const int32_t* __restrict__ off
   }
 }
 
-// One wave per token: x[t] is read once and stored to every row the token owns here.
+// One wave per (token, row segment of 64*CP_UNROLL 16-byte chunks): the segment of x[t]
+// is read once and stored to every row the token owns here.
 constexpr int CP_UNROLL = 8;
 __global__ __launch_bounds__(256) void disp_copy(const uint4* __restrict__ x,
                                                  const int32_t* __restrict__ dest_row,
@@ -195,7 +196,8 @@ __global__ __launch_bounds__(256) void disp_copy(const uint4* __restrict__ x,
   }
   if (nd == 0) return;
   const uint4* src = x + t * row_chunks;
-  for (int base = 0; base < row_chunks; base += 64 * CP_UNROLL) {
+  {
+    const int base = blockIdx.y * 64 * CP_UNROLL;   // this wave's row segment
     uint4 v[CP_UNROLL];
 #pragma unroll
     for (int u = 0; u < CP_UNROLL; ++u) {
@@ -249,7 +251,10 @@ int launch_dispatch(const moe_problem* p, const Dims& d, const void* x, const in
                        kept, row_src, static_cast<uint4*>(xp), d.R_max, d.El, d.e0, d.cap, pad,
                        row_chunks);
   if (x && d.T > 0)
-    hipLaunchKernelGGL(disp_copy, dim3((unsigned)((d.T + 3) / 4)), dim3(256), 0, st,
+    hipLaunchKernelGGL(disp_copy,
+                       dim3((unsigned)((d.T + 3) / 4),
+                            (unsigned)((row_chunks + 64 * CP_UNROLL - 1) / (64 * CP_UNROLL))),
+                       dim3(256), 0, st,
                        static_cast<const uint4*>(x), dest_row, static_cast<uint4*>(xp), (int)d.T,
                        d.K, row_chunks);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;

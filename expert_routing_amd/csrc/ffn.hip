@@ -19,6 +19,7 @@ constexpr int G_MAX = 513;       // local experts (<= 512) + shared expert
 constexpr int G_PAD = 520;
 constexpr int kMaxSplit = 4;     // k-slices of a tile in an XCD's last, partial round
 constexpr int kCuPerXcdMax = 32; // MI355X: 256 CUs in 8 XCDs
+constexpr int kArriveSlots = kNumXcd * kCuPerXcdMax;   // split tiles per GEMM
 
 struct FfnGroup {
   const void* A1;  // [rows][h]
@@ -56,7 +57,8 @@ __global__ __launch_bounds__(1024) void ffn_prep(FfnSched* __restrict__ sc,
                                                  int64_t sh_rows, int64_t sh_t0, int h, int inter,
                                                  int sh_inter, int64_t R_max, int s, int BM,
                                                  int tall_extra, int tall_split, int BN1,
-                                                 int BN2, int cu_per_xcd, int split_max) {
+                                                 int BN2, int cu_per_xcd, int split_max,
+                                                 int* __restrict__ arrive) {
   __shared__ int s1[1024], s2[1024];
   const int g = threadIdx.x;
   const int G = El + has_shared;
@@ -112,6 +114,7 @@ __global__ __launch_bounds__(1024) void ffn_prep(FfnSched* __restrict__ sc,
     sc->start1[g] = g == 0 ? 0 : s1[g - 1];
     sc->start2[g] = g == 0 ? 0 : s2[g - 1];
   }
+  for (int i = g; i < 2 * kArriveSlots; i += 1024) arrive[i] = 0;
   if (g == 0) {
     sc->n_groups = G;
     sc->tall_split = tall_split;
@@ -132,7 +135,9 @@ struct TileRef {
   int tall;     // 0: full tile; 1 + s: part s of the expert's tall last tile
   int slice;    // k-slice of a split tile, else 0
   int nslice;   // k-slices of the tile (1: not split)
-  int piece;    // partial-sum slot of a split tile, else -1
+  int piece;    // partial-sum slot of slice 0 of a split tile, else -1
+  int pstride;  // slots between consecutive slices of the tile
+  int tid_x;    // the tile's split index on its XCD (arrival counter)
 };
 
 struct XcdPlan {
@@ -185,6 +190,8 @@ __device__ __forceinline__ bool find_tile(const FfnSched* sc, bool first, TileRe
   t.slice = 0;
   t.nslice = 1;
   t.piece = -1;
+  t.pstride = 0;
+  t.tid_x = -1;
   if (slot < q.full || q.S == 1) {
     if (slot >= q.cnt) return false;
     L = q.base + slot;
@@ -194,7 +201,9 @@ __device__ __forceinline__ bool find_tile(const FfnSched* sc, bool first, TileRe
     L = q.base + q.full + p % q.rem;
     t.slice = p / q.rem;
     t.nslice = q.S;
-    t.piece = xcd * sc->cu_per_xcd + p;
+    t.piece = xcd * sc->cu_per_xcd + p % q.rem;
+    t.pstride = q.rem;
+    t.tid_x = xcd * sc->cu_per_xcd + p % q.rem;
   }
   locate(sc, first, L, t);
   if (t.tall && t.nslice > 1) {   // tall parts are not split: slice 0 takes all of K
@@ -295,6 +304,77 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[BM / WM / 32][B
   }
 }
 
+// Epilogue of a split tile, run by its last k-slice: element values are the fp32
+// partial sums of the slices (fragment order, one slot every pstride floats) added in
+// slice order, then staged and stored as in store_tile.
+template <int BM, int BN, int WM, int WN, bool GATED>
+__device__ __forceinline__ void store_tile_parts(const float* __restrict__ part, size_t pstride,
+                                                 int nslice, const FfnGroup& fg, int m0, int n0,
+                                                 int h, uint4* __restrict__ smem) {
+  constexpr int NT = 64 * WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int BNO = GATED ? BN / 2 : BN;
+  constexpr int PITCH = BNO * 2 + 16;
+  const int rows = fg.rows;
+  const int Nout = GATED ? fg.inter : h;
+  bf16_t* C = static_cast<bf16_t*>(GATED ? fg.C1 : fg.C2);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  char* stage = reinterpret_cast<char*>(smem);
+  constexpr int TNO = GATED ? TN / 2 : TN;
+  const float4* src = reinterpret_cast<const float4*>(part) + (size_t)wave * TM * TN * 4 * 64 + lane;
+  const size_t ss = pstride / 4;
+  auto sum = [&](int i, int j, int q4) __attribute__((always_inline)) {
+    const float4* p = src + ((i * TN + j) * 4 + q4) * 64;
+    float4 v[kMaxSplit];
+#pragma unroll
+    for (int sl = 0; sl < kMaxSplit; ++sl) v[sl] = p[(size_t)(sl < nslice ? sl : nslice - 1) * ss];
+    float4 a = v[0];
+#pragma unroll
+    for (int sl = 1; sl < kMaxSplit; ++sl) {
+      const bool on = sl < nslice;
+      a.x += on ? v[sl].x : 0.f;
+      a.y += on ? v[sl].y : 0.f;
+      a.z += on ? v[sl].z : 0.f;
+      a.w += on ? v[sl].w : 0.f;
+    }
+    return a;
+  };
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int row = wm * WTM + i * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < TNO; ++j) {
+      const int cbase = (GATED ? wn * (WTN / 2) : wn * WTN) + j * 32 + 4 * (lane >> 5);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 g = sum(i, j, q4);
+        float v[4] = {g.x, g.y, g.z, g.w};
+        if (GATED) {
+          const float4 u = sum(i, j + TN / 2, q4);
+          v[0] = silu(v[0]) * u.x;
+          v[1] = silu(v[1]) * u.y;
+          v[2] = silu(v[2]) * u.z;
+          v[3] = silu(v[3]) * u.w;
+        }
+        bf16x4_t pk = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        *reinterpret_cast<bf16x4_t*>(stage + row * PITCH + (cbase + 8 * q4) * 2) = pk;
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int RCH = BNO / 8;
+  for (int id = tid; id < BM * RCH; id += NT) {
+    const int r = id / RCH, cc = id % RCH;
+    const int gr = m0 + r, gc = n0 + cc * 8;
+    if (gr < rows && gc < Nout)
+      *reinterpret_cast<uint4*>(C + (size_t)gr * Nout + gc) =
+          *reinterpret_cast<const uint4*>(stage + r * PITCH + cc * 16);
+  }
+}
+
 // bf16 grouped GEMM. Block tile BM x BN (BN counts weight rows: for GATED half gate,
 // half up), k-step 64, WM x WN waves (4 or 8), each wave (BM/WM) x (BN/WN) as 32x32
 // MFMA tiles. With 8 waves two share each SIMD, so one wave's MFMAs keep the matrix
@@ -305,7 +385,8 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[BM / WM / 32][B
 template <int BM, int BN, int WM, int WN, bool GATED>
 __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n0, int h,
                                                uint4* __restrict__ smem, int slice,
-                                               int nslice, float* __restrict__ part) {
+                                               int nslice, float* __restrict__ part,
+                                               size_t pstride, int* __restrict__ arrive) {
   constexpr int NW = WM * WN, NT = 64 * NW;
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -451,8 +532,11 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
   __syncthreads();
 
   if (part) {
-    // fp32 partial sums of a k-slice, in fragment order (each store is 1 KB contiguous)
-    float4* dst = reinterpret_cast<float4*>(part) + (size_t)wave * TM * TN * 4 * 64 + lane;
+    // Split tile: store this slice's fp32 partial sums (fragment order, so each store is
+    // 1 KB contiguous), then count the slice in. The last slice to arrive adds all of
+    // them in slice order (the same order whichever arrives last) and stores the tile.
+    const size_t frag = (size_t)wave * TM * TN * 4 * 64 + lane;
+    float4* dst = reinterpret_cast<float4*>(part + (size_t)slice * pstride) + frag;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -462,6 +546,16 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
           dst[((i * TN + j) * 4 + q4) * 64] =
               make_float4(acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2],
                           acc[i][j][4 * q4 + 3]);
+    __threadfence();
+    __syncthreads();
+    // the flag lives in the (now idle) operand LDS: a second LDS object would make the
+    // compiler wait for all LDS DMA before every fragment read of the main loop
+    int* last = reinterpret_cast<int*>(smem);
+    if (tid == 0) *last = atomicAdd(arrive, 1) == nslice - 1;
+    __syncthreads();
+    if (!*last) return;
+    __threadfence();
+    store_tile_parts<BM, BN, WM, WN, GATED>(part, pstride, nslice, fg, m0, n0, h, smem);
     return;
   }
   store_tile<BM, BN, WM, WN, GATED>(acc, fg, m0, n0, h, smem);
@@ -487,20 +581,33 @@ constexpr int tall_split() { return WM > 1 ? 2 : 1; }
 template <int BM, int BN, int WM, int WN, bool GATED, bool TALL>
 __device__ __forceinline__ void gemm_bf16_tile(const FfnSched* __restrict__ sc, int h,
                                                float* __restrict__ part,
+                                               int* __restrict__ arrive,
                                                uint4* __restrict__ smem) {
   constexpr int BMT = BM + 32 * WM, TS = tall_split<WM, WN>(), BNT = BN / TS;
   constexpr int BNO = GATED ? BN / 2 : BN;
   TileRef t;
   if (!find_tile(sc, GATED, t)) return;
+  // the tile is the same for the whole block: keep it (and the operand pointers and
+  // buffer descriptors derived from it) in SGPRs
+  t.g = __builtin_amdgcn_readfirstlane(t.g);
+  t.m_tile = __builtin_amdgcn_readfirstlane(t.m_tile);
+  t.n_tile = __builtin_amdgcn_readfirstlane(t.n_tile);
+  t.tall = __builtin_amdgcn_readfirstlane(t.tall);
+  t.slice = __builtin_amdgcn_readfirstlane(t.slice);
+  t.nslice = __builtin_amdgcn_readfirstlane(t.nslice);
+  t.piece = __builtin_amdgcn_readfirstlane(t.piece);
+  t.pstride = __builtin_amdgcn_readfirstlane(t.pstride);
+  t.tid_x = __builtin_amdgcn_readfirstlane(t.tid_x);
   const FfnGroup& fg = sc->g[t.g];
   const int m0 = t.m_tile * BM, n0 = t.n_tile * BNO;
   if (TALL && t.tall)
     gemm_bf16_body<TALL ? BMT : BM, TALL ? BNT : BN, WM, WN, GATED>(
-        fg, m0, n0 + (t.tall - 1) * (BNO / TS), h, smem, 0, 1, nullptr);
+        fg, m0, n0 + (t.tall - 1) * (BNO / TS), h, smem, 0, 1, nullptr, 0, nullptr);
   else
-    gemm_bf16_body<BM, BN, WM, WN, GATED>(fg, m0, n0, h, smem, t.slice, t.nslice,
-                                          t.piece >= 0 ? part + (size_t)t.piece * BM * BN
-                                                       : nullptr);
+    gemm_bf16_body<BM, BN, WM, WN, GATED>(
+        fg, m0, n0, h, smem, t.slice, t.nslice,
+        t.piece >= 0 ? part + (size_t)t.piece * BM * BN : nullptr, (size_t)t.pstride * BM * BN,
+        arrive + (GATED ? 0 : kArriveSlots) + (t.tid_x >= 0 ? t.tid_x : 0));
 }
 
 template <int BM, int BN, int WM, int WN, bool GATED, bool TALL>
@@ -512,58 +619,17 @@ constexpr size_t tile_lds_bytes() {
 
 template <int BM, int BN, int WM, int WN, bool TALL>
 __global__ __launch_bounds__(64 * WM * WN) void ffn_gate_up_bf16(const FfnSched* __restrict__ sc,
-                                                                 int h, float* part) {
+                                                                 int h, float* part,
+                                                                 int* arrive) {
   __shared__ uint4 smem[tile_lds_bytes<BM, BN, WM, WN, true, TALL>() / 16];
-  gemm_bf16_tile<BM, BN, WM, WN, true, TALL>(sc, h, part, smem);
+  gemm_bf16_tile<BM, BN, WM, WN, true, TALL>(sc, h, part, arrive, smem);
 }
 template <int BM, int BN, int WM, int WN, bool TALL>
 __global__ __launch_bounds__(64 * WM * WN) void ffn_down_bf16(const FfnSched* __restrict__ sc,
-                                                              int h, float* part) {
+                                                              int h, float* part,
+                                                              int* arrive) {
   __shared__ uint4 smem[tile_lds_bytes<BM, BN, WM, WN, false, TALL>() / 16];
-  gemm_bf16_tile<BM, BN, WM, WN, false, TALL>(sc, h, part, smem);
-}
-
-// Second half of split-K: block (xcd, r) adds the k-slice partial sums of the XCD's
-// r-th last-round tile in slice order and runs the tile epilogue.
-template <int BM, int BN, int WM, int WN, bool GATED>
-__global__ __launch_bounds__(64 * WM * WN) void ffn_splitk_reduce(
-    const FfnSched* __restrict__ sc, int h, const float* __restrict__ part) {
-  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
-  constexpr int BNO = GATED ? BN / 2 : BN;
-  __shared__ uint4 smem[(size_t)BM * (BNO * 2 + 16) / 16];
-  const int xcd = blockIdx.x % kNumXcd, r = blockIdx.x / kNumXcd;
-  const XcdPlan q = xcd_plan(sc, GATED, xcd);
-  if (q.S == 1 || r >= q.rem) return;
-  TileRef t;
-  locate(sc, GATED, q.base + q.full + r, t);
-  if (t.tall) return;                     // stored by its own block
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  floatx16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  for (int sl = 0; sl < q.S; ++sl) {
-    const float4* src = reinterpret_cast<const float4*>(
-                            part + (size_t)(xcd * sc->cu_per_xcd + sl * q.rem + r) * BM * BN) +
-                        (size_t)wave * TM * TN * 4 * 64 + lane;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 v = src[((i * TN + j) * 4 + q4) * 64];
-          acc[i][j][4 * q4] += v.x;
-          acc[i][j][4 * q4 + 1] += v.y;
-          acc[i][j][4 * q4 + 2] += v.z;
-          acc[i][j][4 * q4 + 3] += v.w;
-        }
-  }
-  store_tile<BM, BN, WM, WN, GATED>(acc, sc->g[t.g], t.m_tile * BM, t.n_tile * BNO, h, smem);
+  gemm_bf16_tile<BM, BN, WM, WN, false, TALL>(sc, h, part, arrive, smem);
 }
 
 // fp32 grouped GEMM: 64 x 64 tiles (gated: 32 gate + 32 up columns), 4x4 per thread.
@@ -651,25 +717,20 @@ Tiles tile_kind(const Dims& d) {
 
 template <int BM, int BN, int WM, int WN, bool TALL>
 bool launch_bf16_pair(const FfnSched* sc, int h, int64_t ub1, int64_t ub2, int cpx, float* part,
-                      hipStream_t st, hipEvent_t const* ev) {
+                      int* arrive, hipStream_t st, hipEvent_t const* ev) {
   constexpr int NT = 64 * WM * WN;
   // per XCD: its share of the tiles plus room for one round of k-slices
   const int64_t g1 = ((ub1 + kNumXcd - 1) / kNumXcd + cpx) * kNumXcd;
   const int64_t g2 = ((ub2 + kNumXcd - 1) / kNumXcd + cpx) * kNumXcd;
-  const unsigned gr = (unsigned)(kNumXcd * (cpx / 2));   // tiles that can be split
   if (ub1 > 0) {
     hipLaunchKernelGGL((ffn_gate_up_bf16<BM, BN, WM, WN, TALL>), dim3((unsigned)g1), dim3(NT), 0, st,
-                       sc, h, part);
-    hipLaunchKernelGGL((ffn_splitk_reduce<BM, BN, WM, WN, true>), dim3(gr), dim3(NT), 0, st, sc,
-                       h, part);
+                       sc, h, part, arrive);
   }
   if (hipGetLastError() != hipSuccess) return false;
   if (ev && hipEventRecord(ev[1], st) != hipSuccess) return false;
   if (ub2 > 0) {
     hipLaunchKernelGGL((ffn_down_bf16<BM, BN, WM, WN, TALL>), dim3((unsigned)g2), dim3(NT), 0, st, sc,
-                       h, part);
-    hipLaunchKernelGGL((ffn_splitk_reduce<BM, BN, WM, WN, false>), dim3(gr), dim3(NT), 0, st, sc,
-                       h, part);
+                       h, part, arrive);
   }
   return hipGetLastError() == hipSuccess;
 }
@@ -677,6 +738,8 @@ bool launch_bf16_pair(const FfnSched* sc, int h, int64_t ub1, int64_t ub2, int c
 }  // namespace
 
 size_t ffn_sched_bytes(const Dims&) { return sizeof(FfnSched); }
+
+size_t ffn_arrive_bytes(const Dims&) { return 2 * kArriveSlots * sizeof(int); }
 
 size_t ffn_splitk_bytes(const Dims& d) {
   if (!d.bf16) return 0;
@@ -691,6 +754,7 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
                hipStream_t st, hipEvent_t const* ev) {
   FfnSched* sc = reinterpret_cast<FfnSched*>(ws + L.sched);
   float* part = reinterpret_cast<float*>(ws + L.splitk);
+  int* arrive = reinterpret_cast<int*>(ws + L.arrive);
   const int has_sh = (p->n_shared && d.sh_rows > 0) ? 1 : 0;
   const int64_t sh_t0 = (int64_t)d.rank * d.tpr;
   Tiles tiles = Tiles::Large;
@@ -722,7 +786,7 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
                      static_cast<const char*>(w13_sh), static_cast<const char*>(w2_sh),
                      ws + L.hbuf, static_cast<char*>(yp), static_cast<char*>(y_sh), d.El, has_sh,
                      d.sh_rows, sh_t0, d.h, p->inter, p->shared_inter, d.R_max, d.s, BM,
-                     tall_extra, tall_split, BN1, BN2, cpx, split_max);
+                     tall_extra, tall_split, BN1, BN2, cpx, split_max, arrive);
   if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
   if (ev && hipEventRecord(ev[0], st) != hipSuccess) return MOE_ERR_LAUNCH;
   // Upper bound on m-tiles: sum_e ceil(rows_e / BM) <= R_max / BM + E_l (an expert with a
@@ -738,13 +802,13 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
   if (d.bf16) {
     switch (tiles) {
       case Tiles::Large:
-        ok = launch_bf16_pair<256, 256, 2, 2, false>(sc, d.h, ub1, ub2, cpx, part, st, ev);
+        ok = launch_bf16_pair<256, 256, 2, 2, false>(sc, d.h, ub1, ub2, cpx, part, arrive, st, ev);
         break;
       case Tiles::Medium:
-        ok = launch_bf16_pair<128, 256, 2, 2, true>(sc, d.h, ub1, ub2, cpx, part, st, ev);
+        ok = launch_bf16_pair<128, 256, 2, 2, true>(sc, d.h, ub1, ub2, cpx, part, arrive, st, ev);
         break;
       case Tiles::Small:
-        ok = launch_bf16_pair<32, 256, 1, 4, true>(sc, d.h, ub1, ub2, cpx, part, st, ev);
+        ok = launch_bf16_pair<32, 256, 1, 4, true>(sc, d.h, ub1, ub2, cpx, part, arrive, st, ev);
         break;
     }
   } else {

@@ -52,6 +52,7 @@ struct WsLayout {
   size_t sched;         // ffn tile schedule
   size_t hbuf;          // [R_max + sh_rows][I_max] act
   size_t splitk;        // split-K partial sums (fp32), bf16 problems only
+  size_t arrive;        // split-K arrival counters
   size_t total;
 };
 
@@ -77,5 +78,6 @@ int launch_combine(const moe_problem* p, const Dims& d, const void* yp, const in
 
 size_t ffn_sched_bytes(const Dims& d);
 size_t ffn_splitk_bytes(const Dims& d);
+size_t ffn_arrive_bytes(const Dims& d);
 
 }  // namespace moe

@@ -51,25 +51,43 @@ __global__ __launch_bounds__(256) void router_gemm_bf16(const bf16_t* __restrict
   const int kb = blockIdx.z * kslice, ke = kb + kslice < h ? kb + kslice : h;
   logits += (size_t)blockIdx.z * T * E;
 
-  for (int k0 = kb; k0 < ke; k0 += RT_BK) {
+  // Global loads of the next k-step go to registers while the MFMAs run on the current
+  // one, so a block always has one stage in flight.
+  constexpr int WPT = BE * 16 / 256;         // float4 of W per thread per k-step
+  uint4 xr[2];
+  float4 wr[WPT];
+  auto load = [&](int k0) __attribute__((always_inline)) {
     // x tile: 64 rows x 8 chunks = 512 chunks, 2 per thread
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      int id = tid + i * 256, r = id >> 3, c = id & 7;
-      int t = t0 + r < T ? t0 + r : T - 1;
-      xs[swz(r, c)] = *reinterpret_cast<const uint4*>(x + (size_t)t * h + k0 + c * 8);
+      const int id = tid + i * 256, r = id >> 3, c = id & 7;
+      const int t = t0 + r < T ? t0 + r : T - 1;
+      xr[i] = *reinterpret_cast<const uint4*>(x + (size_t)t * h + k0 + c * 8);
     }
-    // w tile: BE rows x 64 fp32 = BE*16 float4; split into 3 bf16 planes
-    for (int id = tid; id < BE * 16; id += 256) {
-      int r = id >> 4, q = id & 15;          // q: float4 index within the row
-      int e = ebase + r;
-      float4 v = e < E ? *reinterpret_cast<const float4*>(w + (size_t)e * h + k0 + q * 4)
-                       : float4{0.f, 0.f, 0.f, 0.f};
+    // w tile: BE rows x 64 fp32 = BE*16 float4
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const int id = tid + i * 256, r = id >> 4, q = id & 15;
+      const int e = ebase + r;
+      wr[i] = e < E ? *reinterpret_cast<const float4*>(w + (size_t)e * h + k0 + q * 4)
+                    : float4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto store = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int id = tid + i * 256, r = id >> 3, c = id & 7;
+      xs[swz(r, c)] = xr[i];
+    }
+    // W split into 3 bf16 planes; 4 bf16 = half a 16-byte chunk
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const int id = tid + i * 256, r = id >> 4, q = id & 15;
+      const float4 v = wr[i];
       bf16_t h0, m0, l0, h1, m1, l1, h2, m2, l2, h3, m3, l3;
       split3(v.x, h0, m0, l0); split3(v.y, h1, m1, l1);
       split3(v.z, h2, m2, l2); split3(v.w, h3, m3, l3);
-      // 4 bf16 = half a 16-byte chunk
-      int chunk = swz(r, q >> 1), half = q & 1;
+      const int chunk = swz(r, q >> 1), half = q & 1;
       uint2* p0 = reinterpret_cast<uint2*>(&wsm[0][chunk]) + half;
       uint2* p1 = reinterpret_cast<uint2*>(&wsm[1][chunk]) + half;
       uint2* p2 = reinterpret_cast<uint2*>(&wsm[2][chunk]) + half;
@@ -77,7 +95,13 @@ __global__ __launch_bounds__(256) void router_gemm_bf16(const bf16_t* __restrict
       *p1 = uint2{(uint32_t)m0 | ((uint32_t)m1 << 16), (uint32_t)m2 | ((uint32_t)m3 << 16)};
       *p2 = uint2{(uint32_t)l0 | ((uint32_t)l1 << 16), (uint32_t)l2 | ((uint32_t)l3 << 16)};
     }
+  };
+
+  if (kb < ke) load(kb);
+  for (int k0 = kb; k0 < ke; k0 += RT_BK) {
+    store();
     __syncthreads();
+    if (k0 + RT_BK < ke) load(k0 + RT_BK);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {            // two k32 steps
       const int c = s * 4 + (lane >> 4);
@@ -179,7 +203,16 @@ __global__ __launch_bounds__(256) void select_topk(const float* __restrict__ log
     float l = -INFINITY, k = -INFINITY, r = 0.f;
     if (active && j < kpl && e < E) {
       l = logits[t * E + e];
-      for (int z = 1; z < nsplit; ++z) l += logits[(size_t)z * T * E + t * E + e];  // in order
+      // partial logits added in slice order; loads in groups of 8 so they overlap
+      for (int z0 = 1; z0 < nsplit; z0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          v[u] = z0 + u < nsplit ? logits[(size_t)(z0 + u) * T * E + t * E + e] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (z0 + u < nsplit) l += v[u];
+      }
       const float b = bias ? bias[e] : 0.f;
       if (score == MOE_SCORE_SOFTMAX) {
         l += b;
@@ -302,12 +335,13 @@ __global__ __launch_bounds__(256) void select_topk(const float* __restrict__ log
 
 }  // namespace
 
-// K-slices of the router GEMM: enough blocks to fill the chip (about 512), slices of at
+// K-slices of the router GEMM: enough blocks for about four per CU (each keeps one
+// k-step of loads in flight, so four hide most of the memory latency), slices of at
 // least 256 along h (a multiple of the 64-wide k-step).
 int route_split(const Dims& d) {
   const int64_t tiles = ((d.T + RT_BM - 1) / RT_BM) *
                         ((d.E + 63) / 64 > 0 ? (d.E + 63) / 64 : 1);
-  int s = tiles > 0 ? (int)((512 + tiles - 1) / tiles) : 1;
+  int s = tiles > 0 ? (int)((1024 + tiles - 1) / tiles) : 1;
   const int smax = d.h / 256 > 1 ? d.h / 256 : 1;
   s = s < 1 ? 1 : (s > smax ? smax : s);
   return s;

@@ -18,8 +18,9 @@ from gpu_cases import (TOL, W_RTOL, cpu_inputs, gpu_inputs, np_, rel_errors, rou
 pytestmark = pytest.mark.gpu
 
 # Small problems that span several tiles with ragged tails, compared in full. Between
-# them every GEMM tile shape meets experts whose last tile is a tall one (a remainder of
-# at most 32 rows per wave row riding on the last full tile) and experts whose is not.
+# them the 128- and 32-row tile shapes meet experts whose last tile is a tall one (a
+# remainder of at most 32 rows per wave row riding on the last full tile) and experts
+# whose is not, and most of them split the last round of tiles along K.
 BASE = CONFIGS["mixtral_prefill"]
 SMALL = {
     "tiny_f32": CONFIGS["tiny_f32"],
@@ -33,8 +34,10 @@ SMALL = {
                                                    shared_inter=192, n_ep=4, ep_rank=1),
     "bf16_medium": CONFIGS["skew_nodrop"].with_(T=1024, h=256, E=16, K=2, inter=256),
     "bf16_large_tiles": BASE.with_(T=1100, h=192, E=4, K=2, inter=384),
-    # 256-row tiles: two experts end in a short remainder (tall last tile), two do not
+    # 256-row tiles: two experts end in a short remainder, two do not
     "bf16_tall_large": BASE.with_(T=1080, h=128, E=4, K=2, inter=192),
+    # 256-row tiles under skewed routing: an expert of exactly 64 rows (short tile only)
+    "bf16_large_skew": CONFIGS["skew_nodrop"].with_(T=2048, h=128, E=8, K=2, inter=128),
     "bf16_decode": CONFIGS["dsv3_decode"].with_(T=8, h=256, E=64, inter=128),
     "bf16_k_eq_e": BASE.with_(T=70, h=128, E=4, K=4, inter=64),
     "bf16_one_token": BASE.with_(T=1, h=128, E=8, K=2, inter=64),
