@@ -218,6 +218,12 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ (r & 7));
 
 __device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
 
+// silu for the bf16 epilogues: the hardware reciprocal (about 1 ulp) instead of an IEEE
+// divide; the result is rounded to bf16 right after.
+__device__ __forceinline__ float silu_fast(float v) {
+  return v * __builtin_amdgcn_rcpf(1.f + __expf(-v));
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   // raw buffer: stride 0, num_records = bytes; reads past the end return zero
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -286,7 +292,7 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[BM / WM / 32][B
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int q = q4 * 4 + u;
-          v[u] = GATED ? silu(acc[i][j][q]) * acc[i][j + TN / 2][q] : acc[i][j][q];
+          v[u] = GATED ? silu_fast(acc[i][j][q]) * acc[i][j + TN / 2][q] : acc[i][j][q];
         }
         bf16x4_t pk = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
         *reinterpret_cast<bf16x4_t*>(stage + row * PITCH + (cbase + 8 * q4) * 2) = pk;
@@ -354,10 +360,10 @@ __device__ __forceinline__ void store_tile_parts(const float* __restrict__ part,
         float v[4] = {g.x, g.y, g.z, g.w};
         if (GATED) {
           const float4 u = sum(i, j + TN / 2, q4);
-          v[0] = silu(v[0]) * u.x;
-          v[1] = silu(v[1]) * u.y;
-          v[2] = silu(v[2]) * u.z;
-          v[3] = silu(v[3]) * u.w;
+          v[0] = silu_fast(v[0]) * u.x;
+          v[1] = silu_fast(v[1]) * u.y;
+          v[2] = silu_fast(v[2]) * u.z;
+          v[3] = silu_fast(v[3]) * u.w;
         }
         bf16x4_t pk = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
         *reinterpret_cast<bf16x4_t*>(stage + row * PITCH + (cbase + 8 * q4) * 2) = pk;
