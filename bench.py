@@ -142,6 +142,9 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one device copy of a known size (counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--materialize-xp", action="store_true",
+                    help="pass xp, so dispatch copies rows into it (default: no xp; the "
+                         "gate/up GEMM reads x through row_src)")
     args = ap.parse_args()
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, workload=args.workload)
@@ -167,6 +170,9 @@ def main():
     t = dict(b)
     t.update(x=inp["x"], w_router=inp["w_router"], bias=inp["bias"], w13=inp["w13"],
              w2=inp["w2"], w13_sh=inp["w13_sh"], w2_sh=inp["w2_sh"])
+    gather = not args.materialize_xp
+    if gather:
+        t["xp"] = None
     npts = len(moe.TRACE_POINTS)
     ev = moe.HipEvents(npts * args.steps)
 
@@ -209,7 +215,9 @@ def main():
     gate_up_flops = 4.0 * R * h * I + 4.0 * sh * h * cfg.shared_inter
     down_flops = 2.0 * R * I * h + 2.0 * sh * cfg.shared_inter * h
     route_bytes = T * h * s + E * h * 4 + T * K * 8
-    dispatch_bytes = T * h * s + R * h * s + 12 * T * K
+    # gathered: dispatch only builds the layout (ids in; dest_row, row_src, counts out) and
+    # the rows travel inside the gate/up GEMM's A loads
+    dispatch_bytes = (8 * T * K + 4 * R) if gather else (T * h * s + R * h * s + 12 * T * K)
     combine_bytes = R * h * s + T * h * s + 8 * T * K + sh * h * s
     gu = stage_ms["ffn_gate_up"] * 1e-3
     achieved = gate_up_flops / gu / 1e12
@@ -230,7 +238,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": T, "h": h, "E": E, "K": K, "inter": I,
                    "score": cfg.score, "capacity_factor": cfg.capacity_factor,
-                   "n_ep": cfg.n_ep, "n_shared": cfg.n_shared, "router": "fp32"},
+                   "n_ep": cfg.n_ep, "n_shared": cfg.n_shared, "router": "fp32",
+                   "xp": "gathered by the gate/up GEMM" if gather else "materialised"},
         "roofline": {"kernel": "ffn_gemm_bf16 gate/up (fused silu*mul)", "bound": "mfma",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,

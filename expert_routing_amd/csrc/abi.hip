@@ -177,10 +177,11 @@ static int v_dispatch(const moe_problem* p, const Dims& d, const void* x, const 
 }
 static int v_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_t* offsets,
                  const void* w13, const void* w2, const void* x, const void* w13_sh,
-                 const void* w2_sh, const void* yp, const void* y_sh, void* ws, size_t ws_bytes) {
+                 const void* w2_sh, const void* yp, const void* y_sh, void* ws, size_t ws_bytes,
+                 bool gather = false) {
   if (p->inter <= 0) return MOE_ERR_INVALID;
   if (!offsets || !w13 || !w2) return MOE_ERR_INVALID;
-  if (d.R_max > 0 && (!xp || !yp)) return MOE_ERR_INVALID;
+  if (d.R_max > 0 && ((!xp && !gather) || !yp)) return MOE_ERR_INVALID;
   if (p->n_shared) {
     if (d.sh_rows > 0 && (!x || !w13_sh || !w2_sh || !y_sh)) return MOE_ERR_INVALID;
   } else if (w13_sh || w2_sh || y_sh) {
@@ -269,16 +270,19 @@ static int forward_impl(const moe_problem* p, const moe_tensors* t, void* ws, si
   int st = make_dims(p, &d);
   if (st != MOE_OK) return st;
   if (p->inter <= 0 || (d.T > 0 && !t->x)) return MOE_ERR_INVALID;
+  // No xp: the row copy is skipped and the gate/up GEMM reads x through row_src.
+  const bool gather = t->xp == nullptr;
   if (events) {
     for (int i = 0; i < MOE_TRACE_POINTS; ++i)
       if (!events[i]) return MOE_ERR_INVALID;
   }
   // Check every stage before the first launch, so an error enqueues nothing.
   if ((st = v_route(p, d, t->x, t->w_router, t->topk_ids, t->topk_w, ws, ws_bytes)) != MOE_OK ||
-      (st = v_dispatch(p, d, t->x, t->topk_ids, t->counts, t->offsets, t->dest_row, t->row_src,
-                       t->send_bytes, t->n_dropped, t->xp, ws, ws_bytes)) != MOE_OK ||
+      (st = v_dispatch(p, d, gather ? nullptr : t->x, t->topk_ids, t->counts, t->offsets,
+                       t->dest_row, t->row_src, t->send_bytes, t->n_dropped, t->xp, ws,
+                       ws_bytes)) != MOE_OK ||
       (st = v_ffn(p, d, t->xp, t->offsets, t->w13, t->w2, t->x, t->w13_sh, t->w2_sh, t->yp,
-                  t->y_sh, ws, ws_bytes)) != MOE_OK ||
+                  t->y_sh, ws, ws_bytes, gather)) != MOE_OK ||
       (st = v_combine(p, d, t->yp, t->dest_row, t->topk_w, t->y_sh, t->y)) != MOE_OK)
     return st;
   const hipStream_t s = (hipStream_t)stream;
@@ -293,12 +297,14 @@ static int forward_impl(const moe_problem* p, const moe_tensors* t, void* ws, si
                                     (float*)(w + L.logits), s)) != MOE_OK)
     return st;
   if (!mark(MOE_TRACE_ROUTE)) return MOE_ERR_LAUNCH;
-  if ((st = launch_dispatch(p, d, t->x, t->topk_ids, t->counts, t->offsets, t->dest_row,
-                            t->row_src, t->send_bytes, t->n_dropped, t->xp, w, L, s)) != MOE_OK)
+  if ((st = launch_dispatch(p, d, gather ? nullptr : t->x, t->topk_ids, t->counts, t->offsets,
+                            t->dest_row, t->row_src, t->send_bytes, t->n_dropped, t->xp, w, L,
+                            s)) != MOE_OK)
     return st;
   if (!mark(MOE_TRACE_DISPATCH)) return MOE_ERR_LAUNCH;
   if ((st = launch_ffn(p, d, t->xp, t->offsets, t->w13, t->w2, t->x, t->w13_sh, t->w2_sh, t->yp,
-                       t->y_sh, w, L, s, ev ? ev + MOE_TRACE_FFN_PREP : nullptr)) != MOE_OK)
+                       t->y_sh, w, L, s, ev ? ev + MOE_TRACE_FFN_PREP : nullptr,
+                       gather ? t->row_src : nullptr)) != MOE_OK)
     return st;
   if (d.T > 0 && (st = launch_combine(p, d, t->yp, t->dest_row, t->topk_w, t->y_sh, t->y, s)) !=
                      MOE_OK)

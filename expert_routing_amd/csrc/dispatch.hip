@@ -250,7 +250,7 @@ int launch_dispatch(const moe_problem* p, const Dims& d, const void* x, const in
     hipLaunchKernelGGL(disp_fill, dim3((unsigned)((d.R_max + 3) / 4)), dim3(256), 0, st, offsets,
                        kept, row_src, static_cast<uint4*>(xp), d.R_max, d.El, d.e0, d.cap, pad,
                        row_chunks);
-  if (x && d.T > 0)
+  if (x && xp && d.T > 0)
     hipLaunchKernelGGL(disp_copy,
                        dim3((unsigned)((d.T + 3) / 4),
                             (unsigned)((row_chunks + 64 * CP_UNROLL - 1) / (64 * CP_UNROLL))),

@@ -22,7 +22,8 @@ constexpr int kCuPerXcdMax = 32; // MI355X: 256 CUs in 8 XCDs
 constexpr int kArriveSlots = kNumXcd * kCuPerXcdMax;   // split tiles per GEMM
 
 struct FfnGroup {
-  const void* A1;  // [rows][h]
+  const void* A1;  // [rows][h], or with gidx the token rows x [T][h]
+  const int32_t* gidx;  // gathered A rows: row r is token gidx[r] / gK (< 0: zero row)
   const void* B1;  // [2*inter][h]
   void* C1;        // [rows][inter]  (hbuf)
   const void* B2;  // [h][inter]
@@ -32,6 +33,8 @@ struct FfnGroup {
   int mt;     // m-tiles
   int tall;   // 1: the last m-tile also takes the (short) remainder: BM + tall_extra rows,
               // split into tall_split narrower tiles per n-tile
+  int arows;  // rows addressable through A1 (rows, or T when gathering)
+  int gK;     // pairs per token (row index -> token) when gathering
 };
 
 struct FfnSched {
@@ -58,7 +61,9 @@ __global__ __launch_bounds__(1024) void ffn_prep(FfnSched* __restrict__ sc,
                                                  int sh_inter, int64_t R_max, int s, int BM,
                                                  int tall_extra, int tall_split, int BN1,
                                                  int BN2, int cu_per_xcd, int split_max,
-                                                 int* __restrict__ arrive) {
+                                                 int* __restrict__ arrive,
+                                                 const int32_t* __restrict__ row_src, int K,
+                                                 int64_t T) {
   __shared__ int s1[1024], s2[1024];
   const int g = threadIdx.x;
   const int G = El + has_shared;
@@ -70,7 +75,8 @@ __global__ __launch_bounds__(1024) void ffn_prep(FfnSched* __restrict__ sc,
       const int r0 = offsets[g];
       rows = offsets[g + 1] - r0;
       I = inter;
-      fg.A1 = xp + (size_t)r0 * h * s;
+      fg.A1 = row_src ? x : xp + (size_t)r0 * h * s;
+      fg.gidx = row_src ? row_src + r0 : nullptr;
       fg.B1 = w13 + (size_t)g * 2 * inter * h * s;
       fg.C1 = hbuf + (size_t)r0 * inter * s;
       fg.B2 = w2 + (size_t)g * h * inter * s;
@@ -79,6 +85,7 @@ __global__ __launch_bounds__(1024) void ffn_prep(FfnSched* __restrict__ sc,
       rows = (int)sh_rows;
       I = sh_inter;
       fg.A1 = x + (size_t)sh_t0 * h * s;
+      fg.gidx = nullptr;
       fg.B1 = w13_sh;
       fg.C1 = hbuf + (size_t)R_max * inter * s;
       fg.B2 = w2_sh;
@@ -93,6 +100,8 @@ __global__ __launch_bounds__(1024) void ffn_prep(FfnSched* __restrict__ sc,
     fg.inter = I;
     fg.mt = mt;
     fg.tall = tall;
+    fg.arows = fg.gidx ? (int)T : rows;
+    fg.gK = K;
     sc->g[g] = fg;
     // per n-tile: mt tiles, or mt - 1 full ones and tall_split tall ones
     const int per_n = tall ? mt - 1 + tall_split : mt;
@@ -388,7 +397,7 @@ __device__ __forceinline__ void store_tile_parts(const float* __restrict__ part,
 // staging) one k-step ahead of the MFMAs. Every DMA request covers whole 128-byte row
 // segments (half-line requests roughly halve what L2 can deliver per CU). The MFMA takes
 // the weight fragment first, so a lane's accumulators hold 4 consecutive output columns.
-template <int BM, int BN, int WM, int WN, bool GATED>
+template <int BM, int BN, int WM, int WN, bool GATED, bool GATHER = false>
 __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n0, int h,
                                                uint4* __restrict__ smem, int slice,
                                                int nslice, float* __restrict__ part,
@@ -415,7 +424,8 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
   const int Kd = GATED ? h : I;         // reduction length = lda = ldb
   const int Nout = GATED ? I : h;       // output columns = ldc
   const uint32_t b_rows = GATED ? 2 * I : h;
-  const __amdgpu_buffer_rsrc_t ra_rs = make_rsrc(A, (uint32_t)rows * Kd * 2);
+  const uint32_t a_bytes = (uint32_t)(GATHER ? fg.arows : rows) * Kd * 2;
+  const __amdgpu_buffer_rsrc_t ra_rs = make_rsrc(A, a_bytes);
   const __amdgpu_buffer_rsrc_t rb_rs = make_rsrc(B, b_rows * (uint32_t)Kd * 2);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -436,6 +446,26 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
   const uint32_t b_lane_up = GATED ? b_lane + (uint32_t)I * Kd * 2 : b_lane;
   const uint32_t x_stride = (uint32_t)(8 * NW) * Kd * 2;   // bytes between instructions
   constexpr int BH = GATED ? BI / 2 : BI;                   // instructions per B half
+  // Gathered A (the gate/up GEMM reading x through the row -> token map): one offset per
+  // instruction and lane; rows past the group or unclaimed read zero (offset past the end).
+  uint32_t a_off[GATHER ? AI : 1];
+  if constexpr (GATHER) {
+    // all AI indices in flight at once (clamped, then masked), as global-memory loads
+    const __attribute__((address_space(1))) int32_t* gidx =
+        (const __attribute__((address_space(1))) int32_t*)fg.gidx;
+    int src[AI];
+#pragma unroll
+    for (int x = 0; x < AI; ++x) {
+      const int r = m0 + 8 * (NW * x + wave) + dr;
+      src[x] = gidx[r < rows ? r : rows - 1];
+    }
+#pragma unroll
+    for (int x = 0; x < AI; ++x) {
+      const int r = m0 + 8 * (NW * x + wave) + dr;
+      a_off[x] = (r < rows && src[x] >= 0) ? ((uint32_t)(src[x] / fg.gK) * Kd + dc * 8) * 2
+                                           : a_bytes;
+    }
+  }
   // DMA instruction `x` (0 <= x < LPS) of k-step `step` into stage `stage`.
   // k-steps [kb, kb + nk) of the Kd / 64: all of them, or this tile's k-slice (wave-
   // uniform values, kept in SGPRs: the DMA takes the k offset as soffset)
@@ -444,9 +474,13 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
   auto issue_one = [&](int step, int stage, int x) __attribute__((always_inline)) {
     const uint32_t soff = (uint32_t)(kb + step) * 128;
     if (x < AI) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra_rs, LDS_PTR(As + stage * A_ST + 64 * (NW * x + wave)), 16, a_lane,
-          soff + x * x_stride, 0, 0);
+      if constexpr (GATHER)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra_rs, LDS_PTR(As + stage * A_ST + 64 * (NW * x + wave)), 16, a_off[x], soff, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra_rs, LDS_PTR(As + stage * A_ST + 64 * (NW * x + wave)), 16, a_lane,
+            soff + x * x_stride, 0, 0);
     } else {
       const int y = x - AI;
       const int yh = y % BH;
@@ -606,14 +640,24 @@ __device__ __forceinline__ void gemm_bf16_tile(const FfnSched* __restrict__ sc, 
   t.tid_x = __builtin_amdgcn_readfirstlane(t.tid_x);
   const FfnGroup& fg = sc->g[t.g];
   const int m0 = t.m_tile * BM, n0 = t.n_tile * BNO;
-  if (TALL && t.tall)
-    gemm_bf16_body<TALL ? BMT : BM, TALL ? BNT : BN, WM, WN, GATED>(
-        fg, m0, n0 + (t.tall - 1) * (BNO / TS), h, smem, 0, 1, nullptr, 0, nullptr);
-  else
-    gemm_bf16_body<BM, BN, WM, WN, GATED>(
-        fg, m0, n0, h, smem, t.slice, t.nslice,
-        t.piece >= 0 ? part + (size_t)t.piece * BM * BN : nullptr, (size_t)t.pstride * BM * BN,
-        arrive + (GATED ? 0 : kArriveSlots) + (t.tid_x >= 0 ? t.tid_x : 0));
+  float* pt = t.piece >= 0 ? part + (size_t)t.piece * BM * BN : nullptr;
+  int* ar = arrive + (GATED ? 0 : kArriveSlots) + (t.tid_x >= 0 ? t.tid_x : 0);
+  const size_t ps = (size_t)t.pstride * BM * BN;
+  const int n0t = n0 + (t.tall - 1) * (BNO / TS);
+  if (GATED && fg.gidx) {   // gate/up reading x through the row -> token map
+    if (TALL && t.tall)
+      gemm_bf16_body<TALL ? BMT : BM, TALL ? BNT : BN, WM, WN, GATED, GATED>(
+          fg, m0, n0t, h, smem, 0, 1, nullptr, 0, nullptr);
+    else
+      gemm_bf16_body<BM, BN, WM, WN, GATED, GATED>(fg, m0, n0, h, smem, t.slice, t.nslice, pt,
+                                                   ps, ar);
+  } else {
+    if (TALL && t.tall)
+      gemm_bf16_body<TALL ? BMT : BM, TALL ? BNT : BN, WM, WN, GATED>(
+          fg, m0, n0t, h, smem, 0, 1, nullptr, 0, nullptr);
+    else
+      gemm_bf16_body<BM, BN, WM, WN, GATED>(fg, m0, n0, h, smem, t.slice, t.nslice, pt, ps, ar);
+  }
 }
 
 template <int BM, int BN, int WM, int WN, bool GATED, bool TALL>
@@ -653,6 +697,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32(const FfnSched* __restrict__
   float* C = static_cast<float*>(GATED ? fg.C1 : fg.C2);
   const int Kd = GATED ? h : I;
   const int Nout = GATED ? I : h;
+  const bool gather = GATED && fg.gidx;   // A rows are tokens of x
   constexpr int BNO = GATED ? F_BN / 2 : F_BN;
   const int m0 = t.m_tile * F_BM, n0 = t.n_tile * BNO;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
@@ -661,7 +706,9 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32(const FfnSched* __restrict__
     for (int id = tid; id < F_BM * F_BK; id += 256) {
       const int r = id / F_BK, k = id % F_BK, kk = k0 + k;
       const int gr = m0 + r;
-      As[k][r] = (gr < rows && kk < Kd) ? A[(size_t)gr * Kd + kk] : 0.f;
+      const int src = gr < rows ? (gather ? fg.gidx[gr] : gr) : -1;
+      const int64_t arow = gather ? (src >= 0 ? src / fg.gK : -1) : src;
+      As[k][r] = (arow >= 0 && kk < Kd) ? A[(size_t)arow * Kd + kk] : 0.f;
       int wrow = -1;
       if (GATED) {
         const int half = r >= F_BN / 2;
@@ -757,7 +804,7 @@ size_t ffn_splitk_bytes(const Dims& d) {
 int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_t* offsets,
                const void* w13, const void* w2, const void* x, const void* w13_sh,
                const void* w2_sh, void* yp, void* y_sh, char* ws, const WsLayout& L,
-               hipStream_t st, hipEvent_t const* ev) {
+               hipStream_t st, hipEvent_t const* ev, const int32_t* gather_rows) {
   FfnSched* sc = reinterpret_cast<FfnSched*>(ws + L.sched);
   float* part = reinterpret_cast<float*>(ws + L.splitk);
   int* arrive = reinterpret_cast<int*>(ws + L.arrive);
@@ -792,7 +839,8 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
                      static_cast<const char*>(w13_sh), static_cast<const char*>(w2_sh),
                      ws + L.hbuf, static_cast<char*>(yp), static_cast<char*>(y_sh), d.El, has_sh,
                      d.sh_rows, sh_t0, d.h, p->inter, p->shared_inter, d.R_max, d.s, BM,
-                     tall_extra, tall_split, BN1, BN2, cpx, split_max, arrive);
+                     tall_extra, tall_split, BN1, BN2, cpx, split_max, arrive, gather_rows, d.K,
+                     d.T);
   if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
   if (ev && hipEventRecord(ev[0], st) != hipSuccess) return MOE_ERR_LAUNCH;
   // Upper bound on m-tiles: sum_e ceil(rows_e / BM) <= R_max / BM + E_l (an expert with a

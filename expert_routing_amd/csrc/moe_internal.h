@@ -72,7 +72,8 @@ int launch_dispatch(const moe_problem* p, const Dims& d, const void* x, const in
 int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_t* offsets,
                const void* w13, const void* w2, const void* x, const void* w13_sh,
                const void* w2_sh, void* yp, void* y_sh, char* ws, const WsLayout& L,
-               hipStream_t st, hipEvent_t const* ev = nullptr);
+               hipStream_t st, hipEvent_t const* ev = nullptr,
+               const int32_t* gather_rows = nullptr);
 int launch_combine(const moe_problem* p, const Dims& d, const void* yp, const int32_t* dest_row,
                    const float* w, const void* y_sh, void* y, hipStream_t st);
 

@@ -194,7 +194,10 @@ int moe_combine(const moe_problem* p, const void* yp, const int32_t* dest_row,
 
 /* ---- the whole layer -------------------------------------------------------------
  * route -> dispatch -> expert FFN -> combine on one stream, with every intermediate
- * kept in caller memory (so each stage's output can be inspected).                   */
+ * kept in caller memory (so each stage's output can be inspected). xp may be NULL: the
+ * row copy is then skipped and the gate/up GEMM reads each row's token straight from x
+ * through row_src (the permutation folded into the GEMM's operand loads); every other
+ * output is bit-identical to a call with xp.                                          */
 typedef struct moe_tensors {
   const void* x;            /* [T][h] act                                  */
   const float* w_router;    /* [E][h] fp32                                 */
@@ -211,7 +214,7 @@ typedef struct moe_tensors {
   int32_t* row_src;         /* [R_max]                                     */
   int64_t* send_bytes;      /* [n_ep][n_ep] or NULL                        */
   int32_t* n_dropped;       /* [1]                                         */
-  void* xp;                 /* [R_max][h] act                              */
+  void* xp;                 /* [R_max][h] act, or NULL (see above)         */
   void* yp;                 /* [R_max][h] act                              */
   void* y_sh;               /* [T/n_ep][h] act or NULL                     */
   void* y;                  /* [T][h] act out                              */

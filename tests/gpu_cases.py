@@ -28,12 +28,16 @@ def run_stages(cfg, inp, p=None):
     return p, b
 
 
-def run_forward(cfg, inp, p=None):
+def run_forward(cfg, inp, p=None, gather=False):
+    """moe_forward; gather=True passes no xp, so the gate/up GEMM reads x through row_src."""
     p = p or moe.problem_from_config(cfg, T=inp["T"])
     b = moe.alloc_buffers(p, "cuda")
     t = dict(b)
     t.update(x=inp["x"], w_router=inp["w_router"], bias=inp["bias"], w13=inp["w13"],
              w2=inp["w2"], w13_sh=inp["w13_sh"], w2_sh=inp["w2_sh"])
+    if gather:
+        t["xp"] = None
+        b["xp"] = None
     moe.moe_forward(p, t, b["ws"])
     torch.cuda.synchronize()
     return p, b

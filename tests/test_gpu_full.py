@@ -1,6 +1,8 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the bench times
-(one moe_forward call). Routing and layout are compared in full; the FFN and the layer
-output on sampled rows / tokens that the fp64 oracle computes one by one."""
+(one moe_forward call, without xp). Routing and layout are compared in full; the FFN and
+the layer output on sampled rows / tokens that the fp64 oracle computes one by one (on a
+run that also materialises xp, so the row copy is checked too), and the bench's run
+without xp must give the identical y."""
 import numpy as np
 import pytest
 import torch
@@ -110,6 +112,13 @@ def test_full_config(name):
     mx, mean, zexact = rel_errors(_f64(b["y"][toks]), y_ref)
     print(f"[parity] {name}: sampled y max_rel {mx:.3e} mean_rel {mean:.3e}", flush=True)
     assert mx <= tmax and mean <= tmean and zexact
+    # --- the bench's configuration: no xp, the gate/up GEMM gathers x through row_src;
+    # bit-identical to the materialised run checked above
+    y_mat = b["y"].clone()
+    del b
+    _, g = run_forward(cfg, inp, gather=True)
+    assert torch.equal(g["y"], y_mat)
+    print(f"[gather] {name}: y identical without xp", flush=True)
 
 
 def test_layout_zero_pairs():

@@ -139,6 +139,23 @@ def test_forward_equals_stages_and_is_deterministic(name):
         assert torch.equal(a["y_sh"], f1["y_sh"])
 
 
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_gather_equals_materialised(name):
+    """Without xp the gate/up GEMM gathers its A rows from x through row_src: the same bf16
+    (or fp32) values in the same k order, so every output is bit-identical."""
+    cfg = SMALL[name]
+    inp = gpu_inputs(cfg)
+    _, f = run_forward(cfg, inp)
+    _, g = run_forward(cfg, inp, gather=True)
+    for k in ("topk_ids", "topk_w", "counts", "offsets", "dest_row", "row_src", "n_dropped",
+              "y"):
+        assert torch.equal(f[k], g[k]), k
+    R = int(f["offsets"][-1].item())    # rows past R are never written
+    assert torch.equal(f["yp"][:R], g["yp"][:R])
+    if f["y_sh"] is not None:
+        assert torch.equal(f["y_sh"], g["y_sh"])
+
+
 def test_all_pairs_dropped_or_remote_give_zero_rows():
     # capacity 1 per expert and 4 ranks: most tokens end with no local kept pair
     cfg = BASE.with_(T=64, h=128, E=8, K=2, inter=64, capacity_factor=0.0625, n_ep=4,
