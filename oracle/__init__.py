@@ -22,3 +22,4 @@ from .ffn import swiglu_ffn, expert_ffn, shared_ffn  # noqa: F401
 from .combine import combine  # noqa: F401
 from .forward import forward  # noqa: F401
 from . import volumes  # noqa: F401
+from . import layout  # noqa: F401
