@@ -4,11 +4,13 @@ Ground truth used here is independent of the oracle's own code path:
   * brute force: the selected set is the K-subset of allowed experts with the largest
     key sum, the lexicographically smallest one among equal sums (lower index wins a
     tie); group limit likewise over M-subsets of groups, with each group's score taken
-    as the best pair sum inside the group;
+    as the best pair sum inside the group. Subset sums are correctly rounded (fsum), so
+    subsets holding the same key values compare equal whatever the summation order;
   * scipy.special.softmax / expit as library routines for the weights;
   * a pure-Python triple loop for the router product on tiny shapes.
 """
 import itertools
+import math
 
 import numpy as np
 import pytest
@@ -32,13 +34,13 @@ def brute_select(key, K, n_groups=1, topk_groups=1):
         scores = [gscore(g) for g in range(n_groups)]
         best = None
         for gs in itertools.combinations(range(n_groups), topk_groups):
-            s = sum(scores[g] for g in gs)
+            s = math.fsum(scores[g] for g in gs)
             if best is None or s > best[0]:
                 best = (s, gs)
         allowed = [e for g in best[1] for e in range(g * gsz, (g + 1) * gsz)]
     best = None
     for S in itertools.combinations(sorted(allowed), K):
-        s = sum(key[e] for e in S)
+        s = math.fsum(key[e] for e in S)
         if best is None or s > best[0]:
             best = (s, S)
     return np.array(best[1])
