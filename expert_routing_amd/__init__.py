@@ -88,6 +88,7 @@ _select = _sig("moe_select", [_P, _V, _V, _V, _V, _V])
 _dispatch = _sig("moe_dispatch", [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _SZ, _V])
 _expert_ffn = _sig("moe_expert_ffn", [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _SZ, _V])
 _combine = _sig("moe_combine", [_P, _V, _V, _V, _V, _V, _V])
+_layout_stats = _sig("moe_layout_stats", [_P, _V, _V, _V, _V, _V, _V, _SZ, _V])
 _forward = _sig("moe_forward", [_P, ctypes.POINTER(Tensors), _V, _SZ, _V])
 _forward_traced = _sig("moe_forward_traced",
                        [_P, ctypes.POINTER(Tensors), _V, _SZ, _V, ctypes.POINTER(_V)])
@@ -95,7 +96,7 @@ TRACE_POINTS = ["begin", "route", "dispatch", "ffn_prep", "ffn_gate_up", "ffn_do
 
 EXPORTED = ["moe_check_problem", "moe_capacity", "moe_max_rows", "moe_workspace_bytes",
             "moe_status_string", "moe_route", "moe_select", "moe_dispatch", "moe_expert_ffn",
-            "moe_combine", "moe_forward", "moe_forward_traced"]
+            "moe_combine", "moe_layout_stats", "moe_forward", "moe_forward_traced"]
 
 
 class MoeError(RuntimeError):
@@ -180,6 +181,14 @@ def moe_expert_ffn(p, xp, offsets, w13, w2, x, w13_sh, w2_sh, yp, y_sh, ws, stre
 def moe_combine(p, yp, dest_row, topk_w, y_sh, y, stream=None):
     _ok(_combine(ctypes.byref(p), _ptr(yp), _ptr(dest_row), _ptr(topk_w), _ptr(y_sh), _ptr(y),
                  _stream(stream)), "moe_combine")
+
+
+def moe_layout_stats(p, topk_ids, tokens_to, recv_pairs, fanout_hist, busiest, ws,
+                     stream=None):
+    wp, wn = _ws(ws)
+    _ok(_layout_stats(ctypes.byref(p), _ptr(topk_ids), _ptr(tokens_to), _ptr(recv_pairs),
+                      _ptr(fanout_hist), _ptr(busiest), wp, wn, _stream(stream)),
+        "moe_layout_stats")
 
 
 def moe_forward(p, t: dict, ws, stream=None):

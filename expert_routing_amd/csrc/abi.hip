@@ -95,6 +95,8 @@ WsLayout ws_layout(const moe_problem* p, const Dims& d) {
   L.hbuf = off;         off = align256(off + (size_t)(d.R_max + d.sh_rows) * imax * d.s);
   L.splitk = off;       off = align256(off + ffn_splitk_bytes(d));
   L.arrive = off;       off = align256(off + ffn_arrive_bytes(d));
+  L.stats_recv = align256((size_t)(d.E + d.El + 2) * 4);
+  L.stats = off;        off = align256(off + L.stats_recv + (size_t)d.N * 8);
   L.total = off;
   return L;
 }
@@ -261,6 +263,20 @@ int moe_combine(const moe_problem* p, const void* yp, const int32_t* dest_row,
   if ((st = v_combine(p, d, yp, dest_row, topk_w, y_sh, y)) != MOE_OK) return st;
   if (d.T == 0) return MOE_OK;
   return launch_combine(p, d, yp, dest_row, topk_w, y_sh, y, (hipStream_t)stream);
+}
+
+int moe_layout_stats(const moe_problem* p, const int32_t* topk_ids, int64_t* tokens_to,
+                     int64_t* recv_pairs, int64_t* fanout_hist, int64_t* busiest, void* ws,
+                     size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = make_dims(p, &d);
+  if (st != MOE_OK) return st;
+  if (d.T > 0 && !topk_ids) return MOE_ERR_INVALID;
+  if (tokens_to && d.T > 0 && d.tpr == 0) return MOE_ERR_INVALID;   // T % n_ep != 0
+  if ((st = check_ws(p, d, ws, ws_bytes)) != MOE_OK) return st;
+  const WsLayout L = ws_layout(p, d);
+  return launch_layout_stats(p, d, topk_ids, tokens_to, recv_pairs, fanout_hist, busiest,
+                             (char*)ws, L, (hipStream_t)stream);
 }
 
 static int forward_impl(const moe_problem* p, const moe_tensors* t, void* ws, size_t ws_bytes,

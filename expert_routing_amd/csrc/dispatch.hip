@@ -215,6 +215,75 @@ __global__ __launch_bounds__(256) void disp_copy(const uint4* __restrict__ x,
   }
 }
 
+// Layout statistics (no rows written): per chunk the same ranks and kept flags as
+// disp_layout, then per token its distinct target chips among kept pairs.
+//   tokens_to[i][j] += 1 per distinct target chip j of a token of chip i,
+//   recv[j] += 1 per kept pair on chip j, hist[f] += 1 for a token reaching f chips.
+__global__ __launch_bounds__(CH) void disp_stats(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ chunk_base, int T, int K,
+    int E, int El, int64_t cap, int64_t tpr, int N, unsigned long long* __restrict__ tokens_to,
+    unsigned long long* __restrict__ recv, unsigned long long* __restrict__ hist) {
+  __shared__ unsigned long long masks[CH / 64][512];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x;
+  const int64_t t = (int64_t)c * CH + tid;
+  for (int i = tid; i < (CH / 64) * E; i += CH) masks[i / E][i % E] = 0ull;
+  __syncthreads();
+  int ev[16];
+  for (int k = 0; k < K; ++k) {
+    int e = t < T ? ids[t * K + k] : -1;
+    if (e < 0 || e >= E) e = -1;
+    ev[k] = e;
+    if (e >= 0) atomicOr(&masks[wave][e], 1ull << lane);
+  }
+  __syncthreads();
+  if (t >= T) return;
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int dst[16];
+  for (int k = 0; k < K; ++k) {
+    const int e = ev[k];
+    dst[k] = -1;
+    if (e < 0) continue;
+    int rank = chunk_base[(size_t)c * E + e] + __popcll(masks[wave][e] & below);
+    for (int w = 0; w < wave; ++w) rank += __popcll(masks[w][e]);
+    if (cap < 0 || rank < cap) {
+      dst[k] = e / El;
+      if (recv) atomicAdd(&recv[dst[k]], 1ull);
+    }
+  }
+  int fan = 0;
+  for (int k = 0; k < K; ++k) {
+    if (dst[k] < 0) continue;
+    bool seen = false;
+    for (int q = 0; q < k; ++q) seen = seen || dst[q] == dst[k];
+    if (seen) continue;
+    ++fan;
+    if (tokens_to) atomicAdd(&tokens_to[(t / tpr) * N + dst[k]], 1ull);
+  }
+  if (hist) atomicAdd(&hist[fan], 1ull);
+}
+
+__global__ __launch_bounds__(256) void fill_zero_u64(unsigned long long* __restrict__ p,
+                                                     int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0ull;
+}
+
+// One block: the largest of n values.
+__global__ __launch_bounds__(256) void max_u64(const unsigned long long* __restrict__ v, int n,
+                                               unsigned long long* __restrict__ out) {
+  __shared__ unsigned long long m[256];
+  unsigned long long x = 0ull;
+  for (int i = threadIdx.x; i < n; i += 256) x = v[i] > x ? v[i] : x;
+  m[threadIdx.x] = x;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s && m[threadIdx.x + s] > m[threadIdx.x]) m[threadIdx.x] = m[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = m[0];
+}
+
 }  // namespace
 
 int launch_dispatch(const moe_problem* p, const Dims& d, const void* x, const int32_t* ids,
@@ -257,6 +326,45 @@ int launch_dispatch(const moe_problem* p, const Dims& d, const void* x, const in
                        dim3(256), 0, st,
                        static_cast<const uint4*>(x), dest_row, static_cast<uint4*>(xp), (int)d.T,
                        d.K, row_chunks);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+int launch_layout_stats(const moe_problem* p, const Dims& d, const int32_t* ids,
+                        int64_t* tokens_to, int64_t* recv_pairs, int64_t* fanout_hist,
+                        int64_t* busiest, char* ws, const WsLayout& L, hipStream_t st) {
+  const int n_chunks = (int)((d.T + CH - 1) / CH);
+  int32_t* chunk_counts = reinterpret_cast<int32_t*>(ws + L.chunk_counts);
+  int32_t* chunk_base = reinterpret_cast<int32_t*>(ws + L.chunk_base);
+  int32_t* kept = reinterpret_cast<int32_t*>(ws + L.kept);
+  // counts, offsets and dropped of the scan go to scratch: only the ranks are needed
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.stats);
+  int32_t* offsets = counts + d.E;
+  int32_t* dropped = offsets + d.El + 1;
+  unsigned long long* recv = reinterpret_cast<unsigned long long*>(recv_pairs);
+  if (busiest && !recv)   // the maximum needs the per-chip loads: keep them in scratch
+    recv = reinterpret_cast<unsigned long long*>(ws + L.stats + L.stats_recv);
+  auto zero = [&](void* q, int64_t n) {
+    if (q && n > 0)
+      hipLaunchKernelGGL(fill_zero_u64, dim3((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024)),
+                         dim3(256), 0, st, static_cast<unsigned long long*>(q), n);
+  };
+  zero(tokens_to, (int64_t)d.N * d.N);
+  zero(recv, d.N);
+  zero(fanout_hist, d.K + 1);
+  if (n_chunks > 0) {
+    hipLaunchKernelGGL(disp_hist, dim3(n_chunks), dim3(CH), 0, st, ids, chunk_counts, (int)d.T,
+                       d.K, d.E);
+    hipLaunchKernelGGL(disp_scan, dim3(1), dim3(1024), 0, st, chunk_counts, chunk_base, counts,
+                       kept, offsets, dropped, static_cast<int64_t*>(nullptr), n_chunks, d.E,
+                       d.El, d.e0, d.cap, 0, d.N);
+    hipLaunchKernelGGL(disp_stats, dim3(n_chunks), dim3(CH), 0, st, ids, chunk_base, (int)d.T,
+                       d.K, d.E, d.El, d.cap, d.tpr, d.N,
+                       reinterpret_cast<unsigned long long*>(tokens_to), recv,
+                       reinterpret_cast<unsigned long long*>(fanout_hist));
+  }
+  if (busiest)
+    hipLaunchKernelGGL(max_u64, dim3(1), dim3(256), 0, st, recv, d.N,
+                       reinterpret_cast<unsigned long long*>(busiest));
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 

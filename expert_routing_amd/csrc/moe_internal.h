@@ -53,6 +53,8 @@ struct WsLayout {
   size_t hbuf;          // [R_max + sh_rows][I_max] act
   size_t splitk;        // split-K partial sums (fp32), bf16 problems only
   size_t arrive;        // split-K arrival counters
+  size_t stats;         // layout statistics scratch: scan outputs [E + E_l + 2] i32, then
+  size_t stats_recv;    //   (at this offset from stats) per-chip loads [N] u64
   size_t total;
 };
 
@@ -74,6 +76,9 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
                const void* w2_sh, void* yp, void* y_sh, char* ws, const WsLayout& L,
                hipStream_t st, hipEvent_t const* ev = nullptr,
                const int32_t* gather_rows = nullptr);
+int launch_layout_stats(const moe_problem* p, const Dims& d, const int32_t* ids,
+                        int64_t* tokens_to, int64_t* recv_pairs, int64_t* fanout_hist,
+                        int64_t* busiest, char* ws, const WsLayout& L, hipStream_t st);
 int launch_combine(const moe_problem* p, const Dims& d, const void* yp, const int32_t* dest_row,
                    const float* w, const void* y_sh, void* y, hipStream_t st);
 

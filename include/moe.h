@@ -192,6 +192,24 @@ int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* offsets,
 int moe_combine(const moe_problem* p, const void* yp, const int32_t* dest_row,
                 const float* topk_w, const void* y_sh, void* y, void* stream);
 
+/* ---- layout statistics -----------------------------------------------------------
+ * What the routing in topk_ids sends where, after capacity exactly as moe_dispatch
+ * keeps pairs, over n_ep virtual ranks (experts in contiguous blocks of E/n_ep, tokens
+ * in contiguous blocks of T/n_ep). A token reaches at most K ranks while one rank's
+ * tokens together reach many ("总览" section "Dispatch 通信矩阵": per-token versus
+ * per-chip fan-out; node-limited routing is the group limit with one group per node);
+ * the busiest rank's load over random top-K selections is the Monte Carlo estimate of
+ * "如何在不跑模型时估算 EP 负载？". Every output may be NULL; all are int64, overwritten.
+ *   tokens_to   [n_ep][n_ep]: distinct tokens of rank i with at least one kept pair on
+ *               rank j (one row copy per target rank; send_bytes counts every pair).
+ *               Needs T % n_ep == 0, else MOE_ERR_INVALID
+ *   recv_pairs  [n_ep]: kept pairs whose expert lives on rank j
+ *   fanout_hist [K+1]: tokens by their number of distinct target ranks
+ *   busiest     [1]: the largest recv_pairs entry                                     */
+int moe_layout_stats(const moe_problem* p, const int32_t* topk_ids, int64_t* tokens_to,
+                     int64_t* recv_pairs, int64_t* fanout_hist, int64_t* busiest, void* ws,
+                     size_t ws_bytes, void* stream);
+
 /* ---- the whole layer -------------------------------------------------------------
  * route -> dispatch -> expert FFN -> combine on one stream, with every intermediate
  * kept in caller memory (so each stage's output can be inspected). xp may be NULL: the

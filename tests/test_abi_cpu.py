@@ -114,6 +114,11 @@ def test_null_and_workspace_errors_before_launch():
                            1 << 30, None) == -1
     assert moe._combine(b, fake, None, fake, None, fake, None) == -1
     assert moe._forward(b, None, fake, 1 << 30, None) == -1
+    # layout statistics: ids required; tokens_to needs T % n_ep == 0; workspace checked
+    assert moe._layout_stats(b, None, fake, fake, fake, fake, fake, 1 << 30, None) == -1
+    assert moe._layout_stats(moe.ctypes.byref(p2), fake, fake, None, None, None, fake, 1 << 30,
+                             None) == -1
+    assert moe._layout_stats(b, fake, fake, fake, fake, fake, fake, 16, None) == -3
 
 
 def test_empty_batch_is_a_no_op():
