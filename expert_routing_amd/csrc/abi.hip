@@ -71,6 +71,17 @@ int make_dims(const moe_problem* p, Dims* d) {
     rmax = p->pad_to_capacity ? capped : (capped < rmax ? capped : rmax);
   }
   if (rmax >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  if (bf16) {
+    // the bf16 GEMMs address each operand with 32-bit byte offsets (buffer descriptors):
+    // x and one expert's row block (at most T rows, a token names an expert once; cap
+    // rows when padding), weight blocks of 2*inter rows
+    int64_t lead = p->h > p->inter ? p->h : p->inter;
+    lead = lead > p->shared_inter ? lead : p->shared_inter;
+    const int64_t rows = (p->pad_to_capacity && cap > p->T) ? cap : p->T;
+    const int64_t wrows = 2 * (int64_t)(p->inter > p->shared_inter ? p->inter : p->shared_inter);
+    if ((rows + 1) * lead * 2 >= (int64_t)1 << 32 || wrows * p->h * 2 >= (int64_t)1 << 32)
+      return MOE_ERR_UNSUPPORTED;
+  }
   d->R_max = rmax;
   d->tpr = (p->T % p->n_ep == 0) ? p->T / p->n_ep : 0;
   d->sh_rows = p->n_shared ? d->tpr : 0;

@@ -107,7 +107,10 @@ typedef struct moe_problem {
  * ep_rank outside [0, n_ep), E % n_groups != 0, topk_groups outside 1..n_groups,
  * topk_groups*E/n_groups < K, padding without a capacity, n_shared not 0/1,
  * n_shared = 1 with T % n_ep != 0. Unsupported (bf16): h % 64 != 0, inter % 64 != 0,
- * shared_inter % 64 != 0; (fp32): h % 4 != 0. */
+ * shared_inter % 64 != 0, or operands beyond the GEMMs' 32-bit byte offsets:
+ * (rows + 1) * max(h, inter, shared_inter) * 2 >= 2^32 with rows = T (the capacity when
+ * padding to a larger one), or 2 * max(inter, shared_inter) * h * 2 >= 2^32;
+ * (fp32): h % 4 != 0; both: T*K >= 2^31. */
 int moe_check_problem(const moe_problem* p);
 
 /* Capacity per expert in *cap (-1 when there is no limit). */

@@ -94,6 +94,16 @@ def test_unsupported_bf16_shapes(kw):
     assert moe.check_problem(moe.Problem(**base)) == 0
 
 
+def test_bf16_operand_offset_limits():
+    # the GEMMs' 32-bit byte offsets: tokens x hidden and 2*inter x hidden must fit
+    ok = dict(T=262144, h=7168, E=8, K=2, inter=2048)          # x = 3.5 GiB
+    assert moe.check_problem(moe.Problem(**ok)) == 0
+    assert moe.check_problem(moe.Problem(**dict(ok, T=300000))) == -2
+    assert moe.check_problem(moe.Problem(**dict(ok, T=64, inter=1 << 17))) == 0   # 3.8 GB
+    assert moe.check_problem(moe.Problem(**dict(ok, T=64, inter=3 << 16))) == -2  # 5.6 GB
+    assert moe.check_problem(moe.Problem(**dict(ok, T=300000, dtype="f32"))) == 0
+
+
 def test_null_and_workspace_errors_before_launch():
     p = moe.Problem(T=32, h=64, E=8, K=2, inter=64)
     b = moe.ctypes.byref(p)
