@@ -30,9 +30,9 @@ struct FfnGroup {
   void* C2;        // [rows][h]
   int rows;
   int inter;
-  int mt;     // m-tiles
-  int tall;   // 1: the last m-tile also takes the (short) remainder: BM + tall_extra rows,
-              // split into tall_split narrower tiles per n-tile
+  int mt[2];    // m-tiles of the gate/up [0] and down [1] GEMMs (their tile heights differ)
+  int tall[2];  // 1: the last m-tile also takes the (short) remainder: BM + tall_extra rows,
+                // split into tall_split narrower tiles per n-tile
   int arows;  // rows addressable through A1 (rows, or T when gathering)
   int gK;     // pairs per token (row index -> token) when gathering
 };
@@ -41,10 +41,10 @@ struct FfnSched {
   int n_groups;
   int total1;
   int total2;
-  int tall_split;
+  int tall_split[2];
   int cu_per_xcd;   // CUs of one XCD (one round of blocks there)
   int split_max;    // 1: no split-K; else the most k-slices a tile may take
-  int pad2_[2];
+  int pad2_;
   int start1[G_PAD];
   int start2[G_PAD];
   FfnGroup g[G_MAX];
@@ -58,8 +58,9 @@ __global__ __launch_bounds__(1024) void ffn_prep(FfnSched* __restrict__ sc,
                                                  const char* w2_sh, char* hbuf, char* yp,
                                                  char* y_sh, int El, int has_shared,
                                                  int64_t sh_rows, int64_t sh_t0, int h, int inter,
-                                                 int sh_inter, int64_t R_max, int s, int BM,
-                                                 int tall_extra, int tall_split, int BN1,
+                                                 int sh_inter, int64_t R_max, int s, int BM1,
+                                                 int BM2, int tall_extra1, int tall_extra2,
+                                                 int tall_split1, int tall_split2, int BN1,
                                                  int BN2, int cu_per_xcd, int split_max,
                                                  int* __restrict__ arrive,
                                                  const int32_t* __restrict__ row_src, int K,
@@ -92,21 +93,26 @@ __global__ __launch_bounds__(1024) void ffn_prep(FfnSched* __restrict__ sc,
       fg.C2 = y_sh;
     }
     // A remainder of at most tall_extra rows rides on the expert's last full tile (it
-    // reads the same weights) instead of costing a tile of its own.
-    const int q = rows / BM, r = rows % BM;
-    const int tall = q >= 1 && r > 0 && r <= tall_extra;
-    const int mt = tall ? q : (rows + BM - 1) / BM;
+    // reads the same weights) instead of costing a tile of its own. Per n-tile: mt tiles,
+    // or mt - 1 full ones and tall_split tall ones.
+    int per_n[2];
+    const int BMg[2] = {BM1, BM2}, TEg[2] = {tall_extra1, tall_extra2};
+    const int TSg[2] = {tall_split1, tall_split2};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int q = rows / BMg[k], r = rows % BMg[k];
+      const int tall = q >= 1 && r > 0 && r <= TEg[k];
+      fg.mt[k] = tall ? q : (rows + BMg[k] - 1) / BMg[k];
+      fg.tall[k] = tall;
+      per_n[k] = tall ? fg.mt[k] - 1 + TSg[k] : fg.mt[k];
+    }
     fg.rows = rows;
     fg.inter = I;
-    fg.mt = mt;
-    fg.tall = tall;
     fg.arows = fg.gidx ? (int)T : rows;
     fg.gK = K;
     sc->g[g] = fg;
-    // per n-tile: mt tiles, or mt - 1 full ones and tall_split tall ones
-    const int per_n = tall ? mt - 1 + tall_split : mt;
-    t1 = per_n * ((I + BN1 - 1) / BN1);
-    t2 = per_n * ((h + BN2 - 1) / BN2);
+    t1 = per_n[0] * ((I + BN1 - 1) / BN1);
+    t2 = per_n[1] * ((h + BN2 - 1) / BN2);
   }
   s1[g] = t1;
   s2[g] = t2;
@@ -126,7 +132,8 @@ __global__ __launch_bounds__(1024) void ffn_prep(FfnSched* __restrict__ sc,
   for (int i = g; i < 2 * kArriveSlots; i += 1024) arrive[i] = 0;
   if (g == 0) {
     sc->n_groups = G;
-    sc->tall_split = tall_split;
+    sc->tall_split[0] = tall_split1;
+    sc->tall_split[1] = tall_split2;
     sc->cu_per_xcd = cu_per_xcd;
     sc->split_max = split_max;
     sc->total1 = s1[G - 1];
@@ -177,10 +184,11 @@ __device__ __forceinline__ void locate(const FfnSched* sc, bool first, int L, Ti
     if (start[mid] <= L) lo = mid; else hi = mid;
   }
   t.g = lo;
-  const int mt = sc->g[lo].mt;
+  const int gi = first ? 0 : 1;
+  const int mt = sc->g[lo].mt[gi];
   const int local = L - start[lo];
-  if (sc->g[lo].tall) {
-    const int per_n = mt - 1 + sc->tall_split;
+  if (sc->g[lo].tall[gi]) {
+    const int per_n = mt - 1 + sc->tall_split[gi];
     const int w = local % per_n;
     t.n_tile = local / per_n;
     t.m_tile = w < mt - 1 ? w : mt - 1;
@@ -760,32 +768,56 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32(const FfnSched* __restrict__
   }
 }
 
-// Tile shapes chosen from the expected rows per local expert, T*K/E.
+// Tile shapes chosen from the expected rows per local expert, T*K/E, for each GEMM. The
+// gate/up GEMM reduces over h (long) and takes 256-row tiles from ~100 rows per expert on;
+// the down GEMM reduces over I (often short), where per-tile overhead and the rows a
+// 256-row tile wastes on small experts weigh more, so it switches later (measured on the
+// DeepSeek-V3 share: gate/up 519 -> 424 us with 256-row tiles, down 249 -> 315 us).
 enum class Tiles { Large, Medium, Small };
 
-Tiles tile_kind(const Dims& d) {
+Tiles tile_kind(const Dims& d, bool gate_up) {
   const double per_expert = d.E > 0 ? (double)d.T * d.K / d.E : 0.0;
-  return per_expert >= 384 ? Tiles::Large : (per_expert >= 48 ? Tiles::Medium : Tiles::Small);
+  const double large = gate_up ? 96 : 384;
+  return per_expert >= large ? Tiles::Large : (per_expert >= 48 ? Tiles::Medium : Tiles::Small);
+}
+
+struct Tiling {
+  int BM, tall_extra, tall_split;   // tall: 32 rows per wave row; halves when WM = 2
+};
+Tiling tiling(Tiles k) {
+  switch (k) {
+    case Tiles::Large: return {256, 0, 1};   // its tall parts would cost as much as tiles
+    case Tiles::Medium: return {128, 64, 2};
+    default: return {32, 32, 1};
+  }
 }
 
 template <int BM, int BN, int WM, int WN, bool TALL>
-bool launch_bf16_pair(const FfnSched* sc, int h, int64_t ub1, int64_t ub2, int cpx, float* part,
-                      int* arrive, hipStream_t st, hipEvent_t const* ev) {
+bool launch_bf16_gemm(bool gated, const FfnSched* sc, int h, int64_t ub, int cpx, float* part,
+                      int* arrive, hipStream_t st) {
   constexpr int NT = 64 * WM * WN;
+  if (ub <= 0) return true;
   // per XCD: its share of the tiles plus room for one round of k-slices
-  const int64_t g1 = ((ub1 + kNumXcd - 1) / kNumXcd + cpx) * kNumXcd;
-  const int64_t g2 = ((ub2 + kNumXcd - 1) / kNumXcd + cpx) * kNumXcd;
-  if (ub1 > 0) {
-    hipLaunchKernelGGL((ffn_gate_up_bf16<BM, BN, WM, WN, TALL>), dim3((unsigned)g1), dim3(NT), 0, st,
-                       sc, h, part, arrive);
-  }
-  if (hipGetLastError() != hipSuccess) return false;
-  if (ev && hipEventRecord(ev[1], st) != hipSuccess) return false;
-  if (ub2 > 0) {
-    hipLaunchKernelGGL((ffn_down_bf16<BM, BN, WM, WN, TALL>), dim3((unsigned)g2), dim3(NT), 0, st, sc,
-                       h, part, arrive);
-  }
+  const int64_t g = ((ub + kNumXcd - 1) / kNumXcd + cpx) * kNumXcd;
+  if (gated)
+    hipLaunchKernelGGL((ffn_gate_up_bf16<BM, BN, WM, WN, TALL>), dim3((unsigned)g), dim3(NT), 0,
+                       st, sc, h, part, arrive);
+  else
+    hipLaunchKernelGGL((ffn_down_bf16<BM, BN, WM, WN, TALL>), dim3((unsigned)g), dim3(NT), 0,
+                       st, sc, h, part, arrive);
   return hipGetLastError() == hipSuccess;
+}
+
+bool launch_bf16(Tiles k, bool gated, const FfnSched* sc, int h, int64_t ub, int cpx,
+                 float* part, int* arrive, hipStream_t st) {
+  switch (k) {
+    case Tiles::Large:
+      return launch_bf16_gemm<256, 256, 2, 2, false>(gated, sc, h, ub, cpx, part, arrive, st);
+    case Tiles::Medium:
+      return launch_bf16_gemm<128, 256, 2, 2, true>(gated, sc, h, ub, cpx, part, arrive, st);
+    default:
+      return launch_bf16_gemm<32, 256, 1, 4, true>(gated, sc, h, ub, cpx, part, arrive, st);
+  }
 }
 
 }  // namespace
@@ -796,8 +828,12 @@ size_t ffn_arrive_bytes(const Dims&) { return 2 * kArriveSlots * sizeof(int); }
 
 size_t ffn_splitk_bytes(const Dims& d) {
   if (!d.bf16) return 0;
-  const Tiles k = tile_kind(d);
-  const size_t tile = k == Tiles::Large ? 256 * 256 : (k == Tiles::Medium ? 128 * 256 : 32 * 256);
+  size_t tile = 0;
+  for (int gu = 0; gu < 2; ++gu) {
+    const Tiles k = tile_kind(d, gu == 1);
+    const size_t t = k == Tiles::Large ? 256 * 256 : (k == Tiles::Medium ? 128 * 256 : 32 * 256);
+    tile = t > tile ? t : tile;
+  }
   return (size_t)kNumXcd * kCuPerXcdMax * tile * 4;
 }
 
@@ -810,8 +846,9 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
   int* arrive = reinterpret_cast<int*>(ws + L.arrive);
   const int has_sh = (p->n_shared && d.sh_rows > 0) ? 1 : 0;
   const int64_t sh_t0 = (int64_t)d.rank * d.tpr;
-  Tiles tiles = Tiles::Large;
-  int BM, BN1, BN2, tall_extra = 0, tall_split = 1, split_max = 1;
+  Tiles k1 = Tiles::Large, k2 = Tiles::Large;
+  Tiling t1{F_BM, 0, 1}, t2{F_BM, 0, 1};
+  int BN1 = F_BN / 2, BN2 = F_BN, split_max = 1;
   int dev = 0, n_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -819,52 +856,40 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
   const int cpx = n_cu / kNumXcd < 1 ? 1 : (n_cu / kNumXcd > kCuPerXcdMax ? kCuPerXcdMax
                                                                          : n_cu / kNumXcd);
   if (d.bf16) {
-    tiles = tile_kind(d);
+    k1 = tile_kind(d, true);
+    k2 = tile_kind(d, false);
+    t1 = tiling(k1);
+    t2 = tiling(k2);
     int min_k = d.h < p->inter ? d.h : p->inter;
     if (has_sh && p->shared_inter < min_k) min_k = p->shared_inter;
     split_max = min_k / 64 < kMaxSplit ? min_k / 64 : kMaxSplit;
-    BM = tiles == Tiles::Large ? 256 : (tiles == Tiles::Medium ? 128 : 32);
-    // 32 rows per wave row of the tile; halves of the tall tile when WM = 2. The 256-row
-    // tile takes no tall tiles: its (320 x 128) halves cost about as much as full tiles.
-    tall_extra = tiles == Tiles::Small ? 32 : (tiles == Tiles::Medium ? 64 : 0);
-    tall_split = tiles == Tiles::Medium ? 2 : 1;
     BN1 = 128;   // output columns of the gated tile (256 B rows: 128 gate + 128 up)
     BN2 = 256;
-  } else {
-    BM = F_BM; BN1 = F_BN / 2; BN2 = F_BN;
   }
   hipLaunchKernelGGL(ffn_prep, dim3(1), dim3(1024), 0, st, sc, offsets,
                      static_cast<const char*>(xp), static_cast<const char*>(w13),
                      static_cast<const char*>(w2), static_cast<const char*>(x),
                      static_cast<const char*>(w13_sh), static_cast<const char*>(w2_sh),
                      ws + L.hbuf, static_cast<char*>(yp), static_cast<char*>(y_sh), d.El, has_sh,
-                     d.sh_rows, sh_t0, d.h, p->inter, p->shared_inter, d.R_max, d.s, BM,
-                     tall_extra, tall_split, BN1, BN2, cpx, split_max, arrive, gather_rows, d.K,
-                     d.T);
+                     d.sh_rows, sh_t0, d.h, p->inter, p->shared_inter, d.R_max, d.s, t1.BM,
+                     t2.BM, t1.tall_extra, t2.tall_extra, t1.tall_split, t2.tall_split, BN1, BN2,
+                     cpx, split_max, arrive, gather_rows, d.K, d.T);
   if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
   if (ev && hipEventRecord(ev[0], st) != hipSuccess) return MOE_ERR_LAUNCH;
   // Upper bound on m-tiles: sum_e ceil(rows_e / BM) <= R_max / BM + E_l (an expert with a
   // tall last tile has mt - 1 + tall_split <= ceil(rows_e / BM) tiles per n-tile).
-  const int64_t mt_ub = d.R_max / BM + d.El;
-  const int64_t mt_sh = has_sh ? (d.sh_rows + BM - 1) / BM : 0;
+  auto m_ub = [&](int BM) { return d.R_max / BM + d.El; };
+  auto m_sh = [&](int BM) { return has_sh ? (d.sh_rows + BM - 1) / BM : (int64_t)0; };
   const int64_t nt1 = (p->inter + BN1 - 1) / BN1;
   const int64_t nt1s = has_sh ? (p->shared_inter + BN1 - 1) / BN1 : 0;
   const int64_t nt2 = (d.h + BN2 - 1) / BN2;
-  const int64_t ub1 = mt_ub * nt1 + mt_sh * nt1s;
-  const int64_t ub2 = (mt_ub + mt_sh) * nt2;
+  const int64_t ub1 = m_ub(t1.BM) * nt1 + m_sh(t1.BM) * nt1s;
+  const int64_t ub2 = (m_ub(t2.BM) + m_sh(t2.BM)) * nt2;
   bool ok = true;
   if (d.bf16) {
-    switch (tiles) {
-      case Tiles::Large:
-        ok = launch_bf16_pair<256, 256, 2, 2, false>(sc, d.h, ub1, ub2, cpx, part, arrive, st, ev);
-        break;
-      case Tiles::Medium:
-        ok = launch_bf16_pair<128, 256, 2, 2, true>(sc, d.h, ub1, ub2, cpx, part, arrive, st, ev);
-        break;
-      case Tiles::Small:
-        ok = launch_bf16_pair<32, 256, 1, 4, true>(sc, d.h, ub1, ub2, cpx, part, arrive, st, ev);
-        break;
-    }
+    ok = launch_bf16(k1, true, sc, d.h, ub1, cpx, part, arrive, st);
+    if (ok && ev) ok = hipEventRecord(ev[1], st) == hipSuccess;
+    if (ok) ok = launch_bf16(k2, false, sc, d.h, ub2, cpx, part, arrive, st);
   } else {
     const int64_t g1 = (ub1 + kNumXcd - 1) / kNumXcd * kNumXcd;
     const int64_t g2 = (ub2 + kNumXcd - 1) / kNumXcd * kNumXcd;
