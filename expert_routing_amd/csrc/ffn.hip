@@ -347,21 +347,25 @@ __device__ __forceinline__ void store_tile_parts(const float* __restrict__ part,
   const int wm = wave / WN, wn = wave % WN;
   char* stage = reinterpret_cast<char*>(smem);
   constexpr int TNO = GATED ? TN / 2 : TN;
-  const float4* src = reinterpret_cast<const float4*>(part) + (size_t)wave * TM * TN * 4 * 64 + lane;
-  const size_t ss = pstride / 4;
-  auto sum = [&](int i, int j, int q4) __attribute__((always_inline)) {
-    const float4* p = src + ((i * TN + j) * 4 + q4) * 64;
-    float4 v[kMaxSplit];
-#pragma unroll
-    for (int sl = 0; sl < kMaxSplit; ++sl) v[sl] = p[(size_t)(sl < nslice ? sl : nslice - 1) * ss];
+  // Buffer loads: a slot past the last slice lies past the descriptor's end and reads
+  // zero without touching memory, so every 32x32 block issues all its loads at once
+  // (slices x 4 float4, twice when gated) before adding them in slice order.
+  const __amdgpu_buffer_rsrc_t prs =
+      make_rsrc(part, (uint32_t)((size_t)nslice * pstride * sizeof(float)));
+  const uint32_t lane_off =
+      (uint32_t)(((size_t)wave * TM * TN * 4 * 64 + lane) * sizeof(float4));
+  const uint32_t slice_bytes = (uint32_t)(pstride * sizeof(float));
+  auto ld = [&](int i, int j, int q4, int sl) __attribute__((always_inline)) {
+    return __builtin_bit_cast(
+        float4, __builtin_amdgcn_raw_buffer_load_b128(
+                    prs, lane_off + (uint32_t)(((i * TN + j) * 4 + q4) * 64 * sizeof(float4)),
+                    (uint32_t)sl * slice_bytes, 0));
+  };
+  auto add_slices = [&](const float4 (&v)[kMaxSplit]) __attribute__((always_inline)) {
     float4 a = v[0];
 #pragma unroll
     for (int sl = 1; sl < kMaxSplit; ++sl) {
-      const bool on = sl < nslice;
-      a.x += on ? v[sl].x : 0.f;
-      a.y += on ? v[sl].y : 0.f;
-      a.z += on ? v[sl].z : 0.f;
-      a.w += on ? v[sl].w : 0.f;
+      a.x += v[sl].x; a.y += v[sl].y; a.z += v[sl].z; a.w += v[sl].w;
     }
     return a;
   };
@@ -371,20 +375,29 @@ __device__ __forceinline__ void store_tile_parts(const float* __restrict__ part,
 #pragma unroll
     for (int j = 0; j < TNO; ++j) {
       const int cbase = (GATED ? wn * (WTN / 2) : wn * WTN) + j * 32 + 4 * (lane >> 5);
+      float4 g[4][kMaxSplit], u[GATED ? 4 : 1][kMaxSplit];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+        for (int sl = 0; sl < kMaxSplit; ++sl) {
+          g[q4][sl] = ld(i, j, q4, sl);
+          if (GATED) u[q4][sl] = ld(i, j + TN / 2, q4, sl);
+        }
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 g = sum(i, j, q4);
-        float v[4] = {g.x, g.y, g.z, g.w};
+        const float4 gs = add_slices(g[q4]);
+        float v[4] = {gs.x, gs.y, gs.z, gs.w};
         if (GATED) {
-          const float4 u = sum(i, j + TN / 2, q4);
-          v[0] = silu_fast(v[0]) * u.x;
-          v[1] = silu_fast(v[1]) * u.y;
-          v[2] = silu_fast(v[2]) * u.z;
-          v[3] = silu_fast(v[3]) * u.w;
+          const float4 us = add_slices(u[q4]);
+          v[0] = silu_fast(v[0]) * us.x;
+          v[1] = silu_fast(v[1]) * us.y;
+          v[2] = silu_fast(v[2]) * us.z;
+          v[3] = silu_fast(v[3]) * us.w;
         }
         bf16x4_t pk = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
         *reinterpret_cast<bf16x4_t*>(stage + row * PITCH + (cbase + 8 * q4) * 2) = pk;
       }
+      __builtin_amdgcn_sched_barrier(0);   // one block's loads in flight at a time
     }
   }
   __syncthreads();
