@@ -6,10 +6,15 @@
 // the offsets into a tile table; every GEMM block finds its (group, n-tile, m-tile) by
 // binary search, so the host never waits for the routing result.
 //
-// bf16 path: 256 threads (4 waves), MFMA 32x32x16 bf16 with fp32 accumulators, LDS
-// double buffering with register prefetch of the next K slice, XOR-swizzled LDS rows,
-// an LDS-staged epilogue for 16-byte coalesced stores, and an XCD-aware block order
-// (consecutive tiles of one expert land on one XCD's L2).
+// bf16 path: 256 threads (4 waves), MFMA 32x32x16 bf16 with fp32 accumulators; operand
+// tiles stream by buffer->LDS DMA into two 64-deep stages of XOR-swizzled 128-byte rows,
+// one k-step ahead of the MFMAs; an LDS-staged epilogue writes 16-byte coalesced rows;
+// an XCD-aware block order keeps consecutive tiles of one expert on one XCD's L2. Tile
+// shapes (256, 128 or 32 rows by 256 weight rows) are chosen per GEMM from the rows per
+// expert; with 128- and 32-row tiles a short remainder rides on an expert's last tile
+// (tall tiles); an XCD's last, partial round of tiles is split along K (fp32 partials,
+// summed in slice order by the last slice to arrive). Without xp the gate/up GEMM reads
+// its A rows straight from x through the row -> token map.
 #include "moe_internal.h"
 
 namespace moe {
@@ -231,8 +236,6 @@ __device__ __forceinline__ bool find_tile(const FfnSched* sc, bool first, TileRe
   return true;
 }
 
-__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ (r & 7)); }
-
 __device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
 
 // silu for the bf16 epilogues: the hardware reciprocal (about 1 ulp) instead of an IEEE
@@ -247,9 +250,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 
-__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
