@@ -333,6 +333,26 @@ __global__ __launch_bounds__(256) void select_topk(const float* __restrict__ log
   }
 }
 
+// Partial logits of the k-slices added in slice order into slab 0, one thread per
+// logit (the same additions, in the same order, as select_topk's own summation).
+__global__ __launch_bounds__(256) void logits_reduce(float* __restrict__ logits, int64_t n,
+                                                     int nsplit) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * 256) {
+    float v[32];
+    const int m = nsplit < 32 ? nsplit : 32;
+#pragma unroll
+    for (int z = 0; z < 32; ++z)
+      if (z < m) v[z] = logits[(size_t)z * n + i];
+    float l = v[0];
+#pragma unroll
+    for (int z = 1; z < 32; ++z)
+      if (z < m) l += v[z];
+    for (int z = 32; z < nsplit; ++z) l += logits[(size_t)z * n + i];
+    logits[i] = l;
+  }
+}
+
 }  // namespace
 
 // K-slices of the router GEMM: enough blocks for about four per CU (each keeps one
@@ -387,6 +407,15 @@ int launch_route(const moe_problem* p, const Dims& d, const void* x, const float
                        w_router, logits, (int)d.T, d.h, d.E, kslice);
   }
   if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
+  if (gz >= 8 && d.T <= 1024) {
+    // small batch, many slabs: select would run too few waves to add them quickly; add
+    // them with one thread per logit, then select reads one
+    const int64_t n = d.T * d.E;
+    const unsigned blocks = (unsigned)((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048);
+    hipLaunchKernelGGL(logits_reduce, dim3(blocks), dim3(256), 0, st, logits, n, (int)gz);
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
+    return select_with(p, d, logits, 1, bias, ids, w, st);
+  }
   return select_with(p, d, logits, (int)gz, bias, ids, w, st);
 }
 
