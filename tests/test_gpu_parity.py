@@ -41,6 +41,13 @@ SMALL = {
     "bf16_decode": CONFIGS["dsv3_decode"].with_(T=8, h=256, E=64, inter=128),
     "bf16_k_eq_e": BASE.with_(T=70, h=128, E=4, K=4, inter=64),
     "bf16_one_token": BASE.with_(T=1, h=128, E=8, K=2, inter=64),
+    # the limits: 512 experts, top-16 under group-limited sigmoid routing over 4 ranks;
+    # one expert (the layer reduces to a dense SwiGLU FFN); the smallest bf16 hidden size
+    "bf16_e512_k16": CONFIGS["dsv3_ep8"].with_(T=96, h=128, E=512, K=16, n_groups=16,
+                                              topk_groups=8, inter=64, n_ep=4, ep_rank=3,
+                                              shared_inter=64),
+    "bf16_dense_e1": BASE.with_(T=100, h=192, E=1, K=1, inter=128),
+    "bf16_h64": BASE.with_(T=130, h=64, E=4, K=2, inter=64),
 }
 
 
