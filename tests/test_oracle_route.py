@@ -76,8 +76,12 @@ def test_topk_matches_brute_force_sigmoid_bias(case, braw):
     bias = np.array(braw[:E], float) * 0.25
     rr = route(K=K, score="sigmoid", n_groups=G, topk_groups=M, logits=L, bias=bias)
     key = sps.expit(L) + bias[None, :]
+    # the oracle's keys are the library sigmoid plus bias (to rounding) ...
+    np.testing.assert_allclose(rr.keys, key, rtol=0, atol=1e-15)
+    # ... and its selection is the brute-force one on those same keys (exact ties, such
+    # as sigmoid(2) + sigmoid(-2) against 1/2 + 1/2, hinge on the last bit of each key)
     for t in range(L.shape[0]):
-        np.testing.assert_array_equal(rr.ids[t], brute_select(key[t], K, G, M))
+        np.testing.assert_array_equal(rr.ids[t], brute_select(rr.keys[t], K, G, M))
 
 
 def test_tie_goes_to_lower_index():
