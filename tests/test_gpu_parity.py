@@ -47,6 +47,8 @@ SMALL = {
                                               topk_groups=8, inter=64, n_ep=4, ep_rank=3,
                                               shared_inter=64),
     "bf16_dense_e1": BASE.with_(T=100, h=192, E=1, K=1, inter=128),
+    # 128-token router blocks (many experts, large batch) with a ragged last block
+    "bf16_router_bm128": CONFIGS["skew_nodrop"].with_(T=1100, h=192, E=64, K=6, inter=64),
     "bf16_h64": BASE.with_(T=130, h=64, E=4, K=2, inter=64),
 }
 
