@@ -36,7 +36,7 @@ SMALL = {
     "bf16_large_tiles": BASE.with_(T=1100, h=192, E=4, K=2, inter=384),
     # 256-row tiles: two experts end in a short remainder, two do not
     "bf16_tall_large": BASE.with_(T=1080, h=128, E=4, K=2, inter=192),
-    # 256-row tiles under skewed routing: an expert of exactly 64 rows (short tile only)
+    # 256-row tiles under skewed routing, including an expert of exactly 64 rows
     "bf16_large_skew": CONFIGS["skew_nodrop"].with_(T=2048, h=128, E=8, K=2, inter=128),
     "bf16_decode": CONFIGS["dsv3_decode"].with_(T=8, h=256, E=64, inter=128),
     "bf16_k_eq_e": BASE.with_(T=70, h=128, E=4, K=4, inter=64),
@@ -47,7 +47,7 @@ SMALL = {
                                               topk_groups=8, inter=64, n_ep=4, ep_rank=3,
                                               shared_inter=64),
     "bf16_dense_e1": BASE.with_(T=100, h=192, E=1, K=1, inter=128),
-    # 128-token router blocks (many experts, large batch) with a ragged last block
+    # a large batch over 64 experts, with a ragged last router block
     "bf16_router_bm128": CONFIGS["skew_nodrop"].with_(T=1100, h=192, E=64, K=6, inter=64),
     "bf16_h64": BASE.with_(T=130, h=64, E=4, K=2, inter=64),
 }
@@ -223,7 +223,9 @@ def test_renorm_off():
         np.testing.assert_allclose(w.cpu().numpy(), rr.weights, rtol=W_RTOL, atol=1e-7)
 
 
-def test_forward_traced_matches_forward():
+@pytest.mark.parametrize("gather", [False, True])
+def test_forward_traced_matches_forward(gather):
+    """The traced forward (what bench.py times, without xp) enqueues the same work."""
     import expert_routing_amd as moe
     cfg = SMALL["bf16_groups_shared"]
     inp = gpu_inputs(cfg)
@@ -232,6 +234,8 @@ def test_forward_traced_matches_forward():
     t = dict(b)
     t.update(x=inp["x"], w_router=inp["w_router"], bias=inp["bias"], w13=inp["w13"],
              w2=inp["w2"], w13_sh=inp["w13_sh"], w2_sh=inp["w2_sh"])
+    if gather:
+        t["xp"] = None
     ev = moe.HipEvents(len(moe.TRACE_POINTS))
     moe.moe_forward_traced(p, t, b["ws"], ev.handles)
     torch.cuda.synchronize()
