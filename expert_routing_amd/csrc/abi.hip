@@ -1,5 +1,6 @@
-// C ABI: validation, sizing and the five stage entry points. Host code only; the
-// kernels live in route.hip, dispatch.hip, ffn.hip and combine.hip.
+// C ABI: validation, sizing, the stage entry points, the whole-layer forward (optionally
+// traced) and the layout statistics. Host code only; the kernels live in route.hip,
+// dispatch.hip, ffn.hip and combine.hip.
 #include <math.h>
 #include <string.h>
 

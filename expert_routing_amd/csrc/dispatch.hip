@@ -11,7 +11,10 @@
 //   layout  per chunk: each wave ORs 64-bit lane masks per expert in LDS, so a pair's
 //           rank inside the chunk is a popcount of earlier lanes and earlier waves;
 //   fill    rows nobody claims get row_src = -1 (pad rows also zero xp);
-//   copy    one wave per token reads x[t] once and writes it to each of its rows.
+//   copy    one wave per (token, row segment) reads the segment of x[t] once and writes
+//           it to each of the token's rows (skipped when the caller passes no xp);
+//   stats   (moe_layout_stats) the same ranks and kept flags, reduced to per-token
+//           target ranks instead of rows.
 #include "moe_internal.h"
 
 namespace moe {

@@ -6,7 +6,9 @@
 // significant bits, so every remainder is representable), and x*hi + x*mid + x*lo are
 // summed into fp32 accumulators. Every product of bf16 operands is exact in fp32, so
 // this is an fp32 GEMM with exact operands and fp32 accumulation, at bf16 MFMA rate.
-// fp32 activations take a plain VALU GEMM.
+// fp32 activations take a plain VALU GEMM. The reduction is split along h into k-slices
+// (enough blocks for the chip) whose partial logits are added in slice order before, or
+// while, selecting.
 #include "moe_internal.h"
 
 namespace moe {
