@@ -418,7 +418,7 @@ __device__ __forceinline__ void store_tile_parts(const float* __restrict__ part,
 // staging) one k-step ahead of the MFMAs. Every DMA request covers whole 128-byte row
 // segments (half-line requests roughly halve what L2 can deliver per CU). The MFMA takes
 // the weight fragment first, so a lane's accumulators hold 4 consecutive output columns.
-template <int BM, int BN, int WM, int WN, bool GATED, bool GATHER = false>
+template <int BM, int BN, int WM, int WN, bool GATED, bool GATHER = false, int NS = 2>
 __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n0, int h,
                                                uint4* __restrict__ smem, int slice,
                                                int nslice, float* __restrict__ part,
@@ -435,8 +435,9 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
   constexpr int LPS = AI + BI;
   constexpr int A_ST = BM * 8, B_ST = BN * 8;       // uint4 per stage
   constexpr int NMF = TM * TN;                      // MFMAs per k16 phase
-  uint4* As = smem;                                 // [2][BM rows][8 chunks]
-  uint4* Bs = smem + 2 * A_ST;                      // [2][BN rows][8 chunks]
+  static_assert(NS >= 2 && NS <= 4 && LPS * (NS - 2) < 64, "LDS stages");
+  uint4* As = smem;                                 // [NS][BM rows][8 chunks]
+  uint4* Bs = smem + NS * A_ST;                     // [NS][BN rows][8 chunks]
 
   const int rows = fg.rows, I = fg.inter;
   const bf16_t* A = static_cast<const bf16_t*>(GATED ? fg.A1 : fg.C1);
@@ -550,7 +551,8 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
   // fragments, then its other MFMAs. With `dma`, the next k-step's DMA rides along one
   // instruction every kDmaStride MFMAs: a burst of VMEM issues would block the wave, and
   // one per MFMA (measured) outruns what the address units accept from four waves.
-  auto kstep = [&](int stage, bool dma, int next_step) __attribute__((always_inline)) {
+  auto kstep = [&](int stage, bool dma, int next_step, int dma_stage)
+                   __attribute__((always_inline)) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int cur = kk & 1;
@@ -560,7 +562,7 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
             fb[cur][t % TN], fa[cur][t / TN], acc[t / TN][t % TN], 0, 0, 0);
         const int slot = kk * NMF + t;            // MFMA index within the k-step
         if (dma && slot >= 1 && (slot - 1) % kDmaStride == 0 && (slot - 1) / kDmaStride < LPS)
-          issue_one(next_step, stage ^ 1, (slot - 1) / kDmaStride);
+          issue_one(next_step, dma_stage, (slot - 1) / kDmaStride);
         if (t == 0 && kk < 3) {
           __builtin_amdgcn_sched_barrier(0);
           read_frags(cur ^ 1, stage, kk + 1);
@@ -570,25 +572,44 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
     }
     if (dma) {   // instructions left over when the k-step has too few MFMAs
 #pragma unroll
-      for (int x = (4 * NMF - 2) / kDmaStride + 1; x < LPS; ++x) issue_one(next_step, stage ^ 1, x);
+      for (int x = (4 * NMF - 2) / kDmaStride + 1; x < LPS; ++x)
+        issue_one(next_step, dma_stage, x);
     }
   };
 
+  // NS stages: k-step kt lives in stage kt % NS; up to NS - 1 k-steps are in flight.
   if (nk > 0) {
 #pragma unroll
-  for (int x = 0; x < LPS; ++x) issue_one(0, 0, x);
-  wait_vmcnt<0>();
+  for (int s0 = 0; s0 < NS - 1; ++s0)
+    if (s0 < nk)
+#pragma unroll
+      for (int x = 0; x < LPS; ++x) issue_one(s0, s0, x);
+  if (nk >= NS - 1) wait_vmcnt<LPS * (NS - 2)>();   // k-step 0 has landed
+  else wait_vmcnt<0>();
   lds_barrier();
   read_frags(0, 0, 0);
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    kstep(kt & 1, true, kt + 1);
-    // k-step kt+1 has landed (this wave's DMA) and every wave is past its reads of
-    // stage kt&1; the barrier publishes the DMA of all waves
-    wait_vmcnt<0>();
+  int kt = 0;
+  for (; kt + NS - 1 < nk; ++kt) {
+    // the DMA of k-step kt + NS - 1 refills the stage k-step kt - 1 used: every wave
+    // passed the barrier after its last reads there
+    kstep(kt % NS, true, kt + NS - 1, (kt + NS - 1) % NS);
+    // k-step kt+1 has landed (this wave's DMA; the NS - 2 after it may still be in
+    // flight) and every wave is past its reads of stage kt % NS; the barrier publishes
+    // the DMA of all waves
+    wait_vmcnt<LPS * (NS - 2)>();
     lds_barrier();
-    read_frags(0, (kt + 1) & 1, 0);
+    read_frags(0, (kt + 1) % NS, 0);
   }
-  kstep((nk - 1) & 1, false, 0);
+  for (; kt + 1 < nk; ++kt) {   // the last NS - 2 k-steps: nothing left to fetch
+    kstep(kt % NS, false, 0, 0);
+    const int after = nk - kt - 2;   // k-steps still in flight behind k-step kt+1
+    if (NS > 3 && after >= 2) wait_vmcnt<LPS * (NS > 3 ? 2 : 0)>();
+    else if (NS > 2 && after >= 1) wait_vmcnt<LPS * (NS > 2 ? 1 : 0)>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    read_frags(0, (kt + 1) % NS, 0);
+  }
+  kstep((nk - 1) % NS, false, 0, 0);
   }
   __syncthreads();
 
@@ -622,9 +643,9 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
   store_tile<BM, BN, WM, WN, GATED>(acc, fg, m0, n0, h, smem);
 }
 
-template <int BM, int BN, bool GATED>
+template <int BM, int BN, bool GATED, int NS = 2>
 constexpr size_t bf16_lds_bytes() {
-  constexpr size_t ops = 2 * (size_t)(BM + BN) * 8 * 16;
+  constexpr size_t ops = NS * (size_t)(BM + BN) * 8 * 16;
   constexpr size_t stg = (size_t)BM * ((GATED ? BN / 2 : BN) * 2 + 16);
   return ops > stg ? ops : stg;
 }
@@ -639,6 +660,11 @@ constexpr size_t cmax() { return A > B ? A : B; }
 template <int WM, int WN>
 constexpr int tall_split() { return WM > 1 ? 2 : 1; }
 
+// LDS stages per tile shape: the 256-row tile fits two; the smaller ones take more, so
+// more k-steps of operands are in flight (they stream more bytes per MFMA).
+template <int BM>
+constexpr int kernel_stages() { return BM >= 256 ? 2 : (BM >= 128 ? 3 : 4); }
+
 template <int BM, int BN, int WM, int WN, bool GATED, bool TALL>
 __device__ __forceinline__ void gemm_bf16_tile(const FfnSched* __restrict__ sc, int h,
                                                float* __restrict__ part,
@@ -646,6 +672,7 @@ __device__ __forceinline__ void gemm_bf16_tile(const FfnSched* __restrict__ sc, 
                                                uint4* __restrict__ smem) {
   constexpr int BMT = BM + 32 * WM, TS = tall_split<WM, WN>(), BNT = BN / TS;
   constexpr int BNO = GATED ? BN / 2 : BN;
+  constexpr int NS = kernel_stages<BM>();
   TileRef t;
   if (!find_tile(sc, GATED, t)) return;
   // the tile is the same for the whole block: keep it (and the operand pointers and
@@ -667,25 +694,27 @@ __device__ __forceinline__ void gemm_bf16_tile(const FfnSched* __restrict__ sc, 
   const int n0t = n0 + (t.tall - 1) * (BNO / TS);
   if (GATED && fg.gidx) {   // gate/up reading x through the row -> token map
     if (TALL && t.tall)
-      gemm_bf16_body<TALL ? BMT : BM, TALL ? BNT : BN, WM, WN, GATED, GATED>(
+      gemm_bf16_body<TALL ? BMT : BM, TALL ? BNT : BN, WM, WN, GATED, GATED, NS>(
           fg, m0, n0t, h, smem, 0, 1, nullptr, 0, nullptr);
     else
-      gemm_bf16_body<BM, BN, WM, WN, GATED, GATED>(fg, m0, n0, h, smem, t.slice, t.nslice, pt,
+      gemm_bf16_body<BM, BN, WM, WN, GATED, GATED, NS>(fg, m0, n0, h, smem, t.slice, t.nslice, pt,
                                                    ps, ar);
   } else {
     if (TALL && t.tall)
-      gemm_bf16_body<TALL ? BMT : BM, TALL ? BNT : BN, WM, WN, GATED>(
+      gemm_bf16_body<TALL ? BMT : BM, TALL ? BNT : BN, WM, WN, GATED, false, NS>(
           fg, m0, n0t, h, smem, 0, 1, nullptr, 0, nullptr);
     else
-      gemm_bf16_body<BM, BN, WM, WN, GATED>(fg, m0, n0, h, smem, t.slice, t.nslice, pt, ps, ar);
+      gemm_bf16_body<BM, BN, WM, WN, GATED, false, NS>(fg, m0, n0, h, smem, t.slice, t.nslice, pt,
+                                                       ps, ar);
   }
 }
 
 template <int BM, int BN, int WM, int WN, bool GATED, bool TALL>
 constexpr size_t tile_lds_bytes() {
-  return TALL ? cmax<bf16_lds_bytes<BM, BN, GATED>(),
-                     bf16_lds_bytes<BM + 32 * WM, BN / tall_split<WM, WN>(), GATED>()>()
-              : bf16_lds_bytes<BM, BN, GATED>();
+  constexpr int NS = kernel_stages<BM>();
+  return TALL ? cmax<bf16_lds_bytes<BM, BN, GATED, NS>(),
+                     bf16_lds_bytes<BM + 32 * WM, BN / tall_split<WM, WN>(), GATED, NS>()>()
+              : bf16_lds_bytes<BM, BN, GATED, NS>();
 }
 
 template <int BM, int BN, int WM, int WN, bool TALL>
