@@ -1,21 +1,30 @@
 #!/usr/bin/env python3
 """Throughput of one MoE layer's forward pass (route -> dispatch -> expert FFN -> combine)
-on one MI355X, on the Mixtral-shaped prefill workload (T=4096 tokens, h=4096, 8 experts,
-top-2 softmax, SwiGLU inter=14336, bf16 with fp32 accumulation, fp32 router, no capacity
-limit), seeded synthetic inputs resident in HBM.
+on one MI355X, seeded synthetic inputs resident in HBM.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME|all] [--no-cpu-baseline]
 
-A step is one moe_forward call: every kernel of the layer over one batch. Prints one
-JSON line. The dominant kernel (the gate/up grouped GEMM) is timed live with HIP events
-that the library records on its launch stream (moe_forward_traced) in the timed region.
-The CPU baseline times the fp64 oracle on a bounded sample of the same workload.
+Default workload: the Mixtral-shaped prefill layer (T=4096 tokens, h=4096, 8 experts, top-2
+softmax, SwiGLU inter=14336, bf16 with fp32 accumulation, fp32 router, no capacity limit).
+`--workload all` prints one JSON line per workload (Mixtral prefill, DeepSeek-V3 EP=8 share,
+Zipf-skewed with and without capacity, DeepSeek-V3 decode).
+
+A step is one moe_forward call: every kernel of the layer over one batch. `value` is the
+steady-state rate of K back-to-back steps. The same steps are then run again with the
+caches flushed before each one (a 1 GiB buffer is written, which evicts the 4 MB L2s and
+the 256 MB Infinity Cache), outside the stage events; `flushed` reports those stage times
+and the per-stage rates against the HBM / MFMA rooflines. Stage times come from HIP events
+the library records on its own launch stream (moe_forward_traced). The CPU baseline times
+the fp64 oracle on the same workload; its routing result also gives the near-tie count and
+the first-choice skew.
 """
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -25,42 +34,64 @@ sys.path.insert(0, ROOT)
 
 METRIC = "routed tokens/sec per MoE layer (route+dispatch+FFN+combine); % MFMA/HBM peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_gemm_mixtral_prefill_traffic.json")
+RIDGE_BF16 = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per byte
+ALL = ["mixtral_prefill", "dsv3_ep8", "skew_cap1", "skew_nodrop", "dsv3_decode"]
+FLUSH_BYTES = 1 << 30       # written before each flushed step: > L2 (8 x 4 MB) + 256 MB MALL
+CALIB_BYTES = 512 << 20     # the plain copy that scales rocprofv3's FETCH_SIZE / WRITE_SIZE
+PROFILES = os.path.join(ROOT, "profiles")
+
+# kernel name prefix -> stage of the layer
+STAGE_OF = [("router_", "route"), ("select_", "route"), ("logits_", "route"),
+            ("disp_", "dispatch"), ("ffn_prep", "ffn_prep"), ("ffn_gate_up", "ffn_gate_up"),
+            ("ffn_down", "ffn_down"), ("combine", "combine")]
 
 
-def _ffn_source_sha():
+def kernel_source_sha():
+    """Hash of every HIP source and header the library is built from."""
     h = hashlib.sha256()
-    for f in ("ffn.hip", "moe_internal.h"):
-        with open(os.path.join(ROOT, "expert_routing_amd", "csrc", f), "rb") as fh:
+    files = sorted(glob.glob(os.path.join(ROOT, "expert_routing_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "moe.h"))
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def _traffic(workload):
-    """HBM bytes per gate/up launch from the committed rocprofv3 counter summary, when it
-    was taken on the current kernel source; else None."""
+def traffic_file(workload):
+    return os.path.join(PROFILES, f"traffic_{workload}.json")
+
+
+def load_traffic(workload):
+    """Per-stage HBM bytes per launch from the committed rocprofv3 counter summary, when it
+    was taken on the current kernel sources; else None."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(traffic_file(workload)) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha") != _ffn_source_sha() or t.get("workload") != workload:
+    if t.get("source_sha") != kernel_source_sha() or t.get("workload") != workload:
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t.get("stages")
 
 
-CALIB_BYTES = 512 << 20   # the plain copy that scales rocprofv3's FETCH_SIZE / WRITE_SIZE
+def stage_of(kernel_name):
+    for prefix, stage in STAGE_OF:
+        if kernel_name.startswith(prefix):
+            return stage
+    return None
 
 
-def summarize_traffic(fetch_csv, write_csv, workload="mixtral_prefill"):
-    """Per-launch HBM bytes of the gate/up GEMM from two rocprofv3 --pmc runs of
-    `bench.py --calibrate-copy` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each
-    scaled by what the same counter reads for the CALIB_BYTES device copy in that run.
-    Writes the JSON that bench.py reports as roofline.traffic."""
+def summarize_traffic(fetch_csv, write_csv, workload, calls):
+    """HBM bytes per layer call of every stage from two rocprofv3 --pmc runs of
+    `bench.py --calibrate-copy --no-flush` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch),
+    each scaled by what the same counter reads for the CALIB_BYTES device copy in that run.
+    `calls`: layer calls in each run (warm-up + timed). Writes profiles/traffic_<w>.json."""
     import csv
 
-    def per_kernel(path, counter):
+    def per_stage(path, counter):
         rows = []
         with open(path) as fh:
             for r in csv.DictReader(fh):
@@ -68,102 +99,139 @@ def summarize_traffic(fetch_csv, write_csv, workload="mixtral_prefill"):
                     rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"],
                                  float(r["Counter_Value"]) * 1024.0))
         rows.sort()
-        first_gemm = min(d for d, n, _ in rows if "ffn_gate_up" in n)
-        # the calibration copy is the last device copy before the first layer call
-        copies = [v for d, n, v in rows if "copyBuffer" in n and d < first_gemm]
-        vals = {"gate_up": [v for _, n, v in rows if "ffn_gate_up" in n],
-                "down": [v for _, n, v in rows if "ffn_down" in n],
-                "copy": copies[-1:]}
-        return {k: (sum(x) / len(x) if x else None) for k, x in vals.items()}
+        first = min(d for d, n, _ in rows if stage_of(n) is not None)
+        copies = [v for d, n, v in rows if "copyBuffer" in n and d < first]
+        tot, kern = {}, {}
+        for _, n, v in rows:
+            s = stage_of(n)
+            if s is None:
+                continue
+            tot[s] = tot.get(s, 0.0) + v
+            kern.setdefault(n.split("(")[0], []).append(v)
+        return ({s: v / calls for s, v in tot.items()}, copies[-1],
+                {k: sum(v) / len(v) for k, v in kern.items()})
 
-    f = per_kernel(fetch_csv, "FETCH_SIZE")
-    w = per_kernel(write_csv, "WRITE_SIZE")
-    f_scale = f["copy"] / CALIB_BYTES
-    w_scale = w["copy"] / CALIB_BYTES
+    f, fcopy, fk = per_stage(fetch_csv, "FETCH_SIZE")
+    w, wcopy, wk = per_stage(write_csv, "WRITE_SIZE")
+    fs, ws_ = fcopy / CALIB_BYTES, wcopy / CALIB_BYTES
     out = {
         "workload": workload,
-        "source_sha": _ffn_source_sha(),
-        "calibration": {"copy_bytes": CALIB_BYTES, "fetch_counter_bytes": f["copy"],
-                        "write_counter_bytes": w["copy"], "fetch_scale": f_scale,
-                        "write_scale": w_scale},
-        "gate_up": {"fetch_bytes": f["gate_up"] / f_scale, "write_bytes": w["gate_up"] / w_scale},
-        "down": {"fetch_bytes": f["down"] / f_scale, "write_bytes": w["down"] / w_scale},
+        "source_sha": kernel_source_sha(),
+        "layer_calls_per_run": calls,
+        "calibration": {"copy_bytes": CALIB_BYTES, "fetch_counter_bytes": fcopy,
+                        "write_counter_bytes": wcopy, "fetch_scale": fs, "write_scale": ws_},
+        "stages": {s: {"fetch_bytes": f.get(s, 0.0) / fs, "write_bytes": w.get(s, 0.0) / ws_}
+                   for s in sorted(set(f) | set(w))},
+        "kernels_per_launch": {k: {"fetch_bytes": fk.get(k, 0.0) / fs,
+                                   "write_bytes": wk.get(k, 0.0) / ws_}
+                               for k in sorted(set(fk) | set(wk))},
     }
-    out["hbm_bytes_per_launch"] = out["gate_up"]["fetch_bytes"] + out["gate_up"]["write_bytes"]
-    with open(TRAFFIC_FILE, "w") as fh:
+    with open(traffic_file(workload), "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
 
 
-def cpu_baseline(cfg, inp, n_tokens, min_seconds=10.0):
-    """The fp64 oracle, untuned, on the first n_tokens tokens of the same workload, called
-    repeatedly until at least min_seconds of CPU time have passed."""
+def cpu_baseline(cfg, inp, ids_gpu, min_seconds=10.0):
+    """The fp64 oracle, untuned, on the whole workload, called repeatedly until at least
+    min_seconds have passed; its routing also gives the near-tie count, the number of
+    tokens whose GPU expert set differs, and the first-choice load skew."""
     import numpy as np
     import torch
 
     import oracle
+    from oracle import volumes as V
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()
                      if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    sub = cfg.with_(T=n_tokens)
-    host = {"T": n_tokens, "x": inp["x"][:n_tokens].cpu(), "w_router": inp["w_router"].cpu(),
+    host = {"T": cfg.T, "x": inp["x"].cpu(), "w_router": inp["w_router"].cpu(),
             "bias": None if inp["bias"] is None else inp["bias"].cpu(),
             "w13": inp["w13"].cpu(), "w2": inp["w2"].cpu(),
             "w13_sh": None if inp["w13_sh"] is None else inp["w13_sh"].cpu(),
             "w2_sh": None if inp["w2_sh"] is None else inp["w2_sh"].cpu()}
-    runs, dt = 0, 0.0
+    runs, dt, out = 0, 0.0, None
     while runs == 0 or dt < min_seconds:   # whole calls, at least min_seconds of CPU work
         t0 = time.perf_counter()
-        out = oracle.forward(sub, host)
+        out = oracle.forward(cfg, host)
         dt += time.perf_counter() - t0
         runs += 1
         assert np.isfinite(out["y"]).all()
+    rr = out["route"]
+    near = (rr.kth_gap < 1e-4) | (rr.group_gap < 1e-4)
+    diff = (ids_gpu != rr.ids).any(axis=1)
+    first = rr.keys.argmax(axis=1) if cfg.n_groups == 1 else None
+    check = {"near_tie_tokens": int(near.sum()),
+             "gpu_id_mismatch_tokens": int(diff.sum()),
+             "gpu_id_mismatch_off_near_tie": int((diff & ~near).sum())}
+    if first is not None:
+        check["first_choice_peak_to_mean"] = V.peak_to_mean(np.bincount(first, minlength=cfg.E))
     del host
     torch.cuda.empty_cache()
-    return {"value": runs * n_tokens / dt, "unit": "tokens/s", "cores": int(cores),
-            "kind": "oracle", "seconds": round(dt, 3), "calls": runs,
-            "sample": f"oracle.forward (fp64 numpy) on the first {n_tokens} of {cfg.T} tokens of "
-                      f"the same workload, {runs} call(s): routing, dispatch, all {cfg.E_local} "
-                      f"experts' SwiGLU FFN on their rows, combine"}
+    return ({"value": runs * cfg.T / dt, "unit": "tokens/s", "cores": int(cores),
+             "kind": "oracle", "seconds": round(dt, 3), "calls": runs,
+             "sample": f"oracle.forward (fp64 numpy) on all {cfg.T} tokens of the same "
+                       f"workload, {runs} call(s): routing, dispatch, the SwiGLU FFN of all "
+                       f"{cfg.E_local} local experts on their rows, combine"}, check)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixtral_prefill")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=0,
-                    help="tokens of the CPU-oracle sample (0: the whole workload)")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run one device copy of a known size (counter calibration)")
-    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
-    ap.add_argument("--materialize-xp", action="store_true",
-                    help="pass xp, so dispatch copies rows into it (default: no xp; the "
-                         "gate/up GEMM reads x through row_src)")
-    args = ap.parse_args()
-    if args.summarize_traffic:
-        summarize_traffic(*args.summarize_traffic, workload=args.workload)
-        return
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus > 1 or world > 1:
-        print(f"bench.py: this build runs one MoE layer on one GPU; --gpus {args.gpus} "
-              f"(WORLD_SIZE={world}) is not supported. Multi-GPU expert parallelism is "
-              "design-only here.", file=sys.stderr)
-        sys.exit(2)
+def stage_work(cfg, R, active, gather):
+    """Algorithmic bytes and flops of each stage of one layer call (what the method must
+    move: each operand read once, each result written once)."""
+    s = cfg.act_bytes
+    T, h, E, K, I = cfg.T, cfg.h, cfg.E, cfg.K, cfg.inter
+    sh = (T // cfg.n_ep) if cfg.n_shared else 0
+    Is = cfg.shared_inter
+    n_sh = 1 if cfg.n_shared else 0
+    w = {
+        "route": {"bytes": T * h * s + E * h * 4 + T * K * 8, "flops": 2.0 * T * h * E},
+        # gathered: dispatch moves only the layout (ids in; dest_row, row_src, counts out)
+        # and the token rows travel inside the gate/up GEMM's A loads
+        "dispatch": {"bytes": (8 * T * K + 4 * R + 4 * E) if gather
+                     else (T * h * s + R * h * s + 12 * T * K), "flops": 0.0},
+        "ffn_gate_up": {"bytes": 2 * I * h * s * active + 2 * Is * h * s * n_sh
+                        + R * h * s + sh * h * s
+                        + R * I * s + sh * Is * s,
+                        "flops": 4.0 * R * h * I + 4.0 * sh * h * Is},
+        "ffn_down": {"bytes": I * h * s * active + Is * h * s * n_sh + R * I * s + sh * Is * s
+                     + R * h * s + sh * h * s,
+                     "flops": 2.0 * R * I * h + 2.0 * sh * Is * h},
+        "combine": {"bytes": R * h * s + T * h * s + 8 * T * K + sh * h * s, "flops": 0.0},
+    }
+    return w
 
-    import numpy as np
-    import torch
 
-    import expert_routing_amd as moe
+def rate(work, ms, bound=None):
+    """Achieved GB/s and TFLOP/s of a stage, and its roofline fraction: against HBM when its
+    arithmetic intensity is below the bf16 ridge, else against bf16 MFMA (the router: fp32
+    vector when its flops outweigh its bytes at the fp32 ridge)."""
+    sec = ms * 1e-3
+    gbs = work["bytes"] / sec / 1e9
+    tfs = work["flops"] / sec / 1e12
+    if bound is None:
+        ai = work["flops"] / max(work["bytes"], 1)
+        bound = "mfma" if ai > RIDGE_BF16 else "hbm"
+    if bound == "hbm":
+        frac = gbs / PEAK_HBM_GBS
+    elif bound == "f32":
+        frac = tfs / PEAK_F32_TFLOPS
+    else:
+        frac = tfs / PEAK_BF16_TFLOPS
+    return {"us": round(ms * 1e3, 2), "GBps": round(gbs, 1), "TFLOPs": round(tfs, 2),
+            "bound": bound, "frac": round(frac, 4)}
+
+
+def route_bound(cfg):
+    # the fp32 router against fp32 vector peak once its flops outweigh its bytes there
+    w = 2.0 * cfg.T * cfg.h * cfg.E / (cfg.T * cfg.h * cfg.act_bytes)
+    return "f32" if w > PEAK_F32_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
+
+
+def run_workload(name, args, moe, torch, np):
     from synth import CONFIGS, make_inputs
 
-    torch.cuda.set_device(0)
-    cfg = CONFIGS[args.workload]
+    cfg = CONFIGS[name]
     inp = make_inputs(cfg, device="cuda")
     p = moe.problem_from_config(cfg)
     b = moe.alloc_buffers(p, "cuda")
@@ -173,7 +241,8 @@ def main():
     gather = not args.materialize_xp
     if gather:
         t["xp"] = None
-    npts = len(moe.TRACE_POINTS)
+    pts = moe.TRACE_POINTS
+    npts = len(pts)
     ev = moe.HipEvents(npts * args.steps)
 
     if args.calibrate_copy:
@@ -186,6 +255,14 @@ def main():
         moe.moe_forward(p, t, b["ws"])
     torch.cuda.synchronize()
 
+    def stage_means():
+        out = {n: 0.0 for n in pts[1:]}
+        for i in range(args.steps):
+            for j in range(1, npts):
+                out[pts[j]] += ev.elapsed(i * npts + j - 1, i * npts + j) / args.steps
+        return out
+
+    # steady state: K back-to-back steps
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -197,31 +274,66 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = start.elapsed_time(stop) / args.steps
+    steady = stage_means()
 
-    stage_ms = {name: 0.0 for name in moe.TRACE_POINTS[1:]}
-    for i in range(args.steps):
-        for j in range(1, npts):
-            stage_ms[moe.TRACE_POINTS[j]] += ev.elapsed(i * npts + j - 1, i * npts + j) / args.steps
+    # flushed: each step starts with cold L2 and Infinity Cache
+    flushed = None
+    if not args.no_flush:
+        flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        for i in range(args.steps):
+            flush.fill_(i & 0xff)
+            moe.moe_forward_traced(p, t, b["ws"], ev.handles[i * npts:(i + 1) * npts])
+        torch.cuda.synchronize()
+        flushed = stage_means()
+        del flush
     ev.close()
 
-    # Work actually done this step (the layout is deterministic, so any step's).
+    # work actually done (the layout is deterministic, so any step's)
     offsets = b["offsets"].cpu().numpy()
-    counts = b["counts"].cpu().numpy()
+    counts = b["counts"].cpu().numpy().astype(np.float64)
     R = int(offsets[-1])
-    sh = (cfg.T // cfg.n_ep) if cfg.n_shared else 0
-    s = cfg.act_bytes
-    T, h, E, K, I = cfg.T, cfg.h, cfg.E, cfg.K, cfg.inter
     active = int((np.diff(offsets) > 0).sum())
-    gate_up_flops = 4.0 * R * h * I + 4.0 * sh * h * cfg.shared_inter
-    down_flops = 2.0 * R * I * h + 2.0 * sh * cfg.shared_inter * h
-    route_bytes = T * h * s + E * h * 4 + T * K * 8
-    # gathered: dispatch only builds the layout (ids in; dest_row, row_src, counts out) and
-    # the rows travel inside the gate/up GEMM's A loads
-    dispatch_bytes = (8 * T * K + 4 * R) if gather else (T * h * s + R * h * s + 12 * T * K)
-    combine_bytes = R * h * s + T * h * s + 8 * T * K + sh * h * s
-    gu = stage_ms["ffn_gate_up"] * 1e-3
-    achieved = gate_up_flops / gu / 1e12
-    traffic = _traffic(args.workload)
+    dropped = int(b["n_dropped"].item())
+    work = stage_work(cfg, R, active, gather)
+    T, K = cfg.T, cfg.K
+    gu = work["ffn_gate_up"]
+    gu_bound = "mfma" if gu["flops"] / gu["bytes"] > RIDGE_BF16 else "hbm"
+    traffic = load_traffic(name)
+    gu_ms = steady["ffn_gate_up"]
+    if gu_bound == "mfma":
+        achieved = gu["flops"] / (gu_ms * 1e-3) / 1e12
+        roof = {"kernel": "ffn_gate_up_bf16 (grouped gate/up GEMM, fused silu*mul)",
+                "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS}
+    else:
+        achieved = gu["bytes"] / (gu_ms * 1e-3) / 1e9
+        roof = {"kernel": "ffn_gate_up_bf16 (grouped gate/up GEMM, fused silu*mul)",
+                "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    roof.update({"traffic": (traffic["ffn_gate_up"]["fetch_bytes"]
+                             + traffic["ffn_gate_up"]["write_bytes"]) if traffic else None,
+                 "algorithmic_flops": gu["flops"], "algorithmic_bytes": gu["bytes"],
+                 "avg_launch_ms": gu_ms})
+
+    def stage_rates(st):
+        r = {}
+        for sname in ("route", "dispatch", "ffn_gate_up", "ffn_down", "combine"):
+            r[sname] = rate(work[sname], st[sname],
+                            route_bound(cfg) if sname == "route" else
+                            ("hbm" if sname in ("dispatch", "combine") else None))
+        r["ffn_prep"] = {"us": round(st["ffn_prep"] * 1e3, 2)}
+        # route + dispatch + prep + combine against their summed roofline times
+        rdc_t = st["route"] + st["dispatch"] + st["ffn_prep"] + st["combine"]
+        roof_t = 0.0
+        for sname in ("route", "dispatch", "combine"):
+            wk = work[sname]
+            peak_f = PEAK_F32_TFLOPS if route_bound(cfg) == "f32" and sname == "route" \
+                else PEAK_BF16_TFLOPS
+            roof_t += max(wk["bytes"] / (PEAK_HBM_GBS * 1e9), wk["flops"] / (peak_f * 1e12))
+        r["route_dispatch_combine"] = {"us": round(rdc_t * 1e3, 2),
+                                       "roofline_us": round(roof_t * 1e6, 2),
+                                       "frac": round(roof_t * 1e3 / rdc_t, 4)}
+        return r
 
     result = {
         "metric": METRIC,
@@ -236,35 +348,81 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "T": T, "h": h, "E": E, "K": K, "inter": I,
-                   "score": cfg.score, "capacity_factor": cfg.capacity_factor,
+        "config": {"workload": cfg.name, "T": T, "h": cfg.h, "E": cfg.E, "K": K,
+                   "inter": cfg.inter, "score": cfg.score, "n_groups": cfg.n_groups,
+                   "topk_groups": cfg.topk_groups, "capacity_factor": cfg.capacity_factor,
                    "n_ep": cfg.n_ep, "n_shared": cfg.n_shared, "router": "fp32",
                    "xp": "gathered by the gate/up GEMM" if gather else "materialised"},
-        "roofline": {"kernel": "ffn_gemm_bf16 gate/up (fused silu*mul)", "bound": "mfma",
-                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "flops_per_launch": gate_up_flops,
-                     "avg_launch_ms": stage_ms["ffn_gate_up"]},
-        "routed_pairs_per_s": (T * K - int(b["n_dropped"].item())) / (ms * 1e-3),
-        "layer_tflops": (gate_up_flops + down_flops) / (ms * 1e-3) / 1e12,
-        "stages_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
-        "stage_rates": {
-            "route_GBps": route_bytes / (stage_ms["route"] * 1e-3) / 1e9,
-            "dispatch_GBps": dispatch_bytes / (stage_ms["dispatch"] * 1e-3) / 1e9,
-            "gate_up_TFLOPs": achieved,
-            "down_TFLOPs": down_flops / (stage_ms["ffn_down"] * 1e-3) / 1e12,
-            "combine_GBps": combine_bytes / (stage_ms["combine"] * 1e-3) / 1e9,
-        },
-        "layout": {"rows": R, "active_local_experts": active,
+        "roofline": roof,
+        "routed_pairs_per_s": (T * K - dropped) / (ms * 1e-3),
+        "layer_tflops": (gu["flops"] + work["ffn_down"]["flops"]) / (ms * 1e-3) / 1e12,
+        "stages_us": {k: round(v * 1e3, 2) for k, v in steady.items()},
+        "stage_rates": stage_rates(steady),
+        "flushed": None if flushed is None else {
+            "ms_per_step": sum(flushed.values()),
+            "stages_us": {k: round(v * 1e3, 2) for k, v in flushed.items()},
+            "stage_rates": stage_rates(flushed)},
+        "layout": {"rows": R, "active_local_experts": active, "dropped": dropped,
                    "balancedness": float(counts.mean() / max(counts.max(), 1)),
-                   "dropped": int(b["n_dropped"].item())},
+                   "peak_to_mean": float(counts.max() / max(counts.mean(), 1e-30)),
+                   "idle_experts": int((counts == 0).sum())},
         "wall_s_timed": round(wall, 4),
     }
+    if cfg.bias == "zipf":
+        # popularity law of the bias alone: E / H_{E,s}
+        H = sum(r ** -cfg.zipf_s for r in range(1, cfg.E + 1))
+        result["layout"]["zipf_popularity_peak_to_mean"] = cfg.E / H
+    if cfg.T % cfg.n_ep == 0 and b["send_bytes"] is not None and cfg.n_ep > 1:
+        sb = b["send_bytes"].cpu().numpy()
+        result["layout"]["send_bytes_row_sum_mean"] = float(sb.sum(1).mean())
+        result["layout"]["send_zero_pair_fraction"] = float((sb == 0).mean())
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, min(args.cpu_tokens or T, T))
+        ids = b["topk_ids"].cpu().numpy()
+        result["cpu_baseline"], result["routing_check"] = cpu_baseline(cfg, inp, ids)
     else:
         result["cpu_baseline"] = None
-    print(json.dumps(result), flush=True)
+    del b, t, inp
+    torch.cuda.empty_cache()
+    return result
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill",
+                    help="a workload name, or 'all' for one line per workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the cache-flushed repetition of the timed steps")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one device copy of a known size (counter calibration)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--materialize-xp", action="store_true",
+                    help="pass xp, so dispatch copies rows into it (default: no xp; the "
+                         "gate/up GEMM reads x through row_src)")
+    args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, workload=args.workload,
+                          calls=args.warmup + args.steps)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print(f"bench.py: this build runs one MoE layer on one GPU; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported. Multi-GPU expert parallelism is "
+              "design-only here.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import expert_routing_amd as moe
+
+    torch.cuda.set_device(0)
+    names = ALL if args.workload == "all" else [args.workload]
+    for name in names:
+        print(json.dumps(run_workload(name, args, moe, torch, np)), flush=True)
 
 
 if __name__ == "__main__":

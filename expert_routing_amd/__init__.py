@@ -14,7 +14,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# EXPERT_ROUTING_AMD_LIB may name another build of the same library (for example one built
+# with different tile settings); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("EXPERT_ROUTING_AMD_LIB") or os.path.join(_HERE, "libmoe.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python expert_routing_amd/build.py`")

@@ -191,24 +191,23 @@ __global__ __launch_bounds__(256) void disp_copy(const uint4* __restrict__ x,
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  int dst[16];
-  int nd = 0;
-  for (int k = 0; k < K; ++k) {
-    const int d = dest_row[t * K + k];
-    if (d >= 0) dst[nd++] = d;
-  }
-  if (nd == 0) return;
+  // the token's rows here (a compacted list would live in scratch memory: dynamic index)
+  bool any = false;
+  for (int k = 0; k < K; ++k) any = any || dest_row[t * K + k] >= 0;
+  if (!any) return;
   const uint4* src = x + t * row_chunks;
   {
     const int base = blockIdx.y * 64 * CP_UNROLL;   // this wave's row segment
     uint4 v[CP_UNROLL];
 #pragma unroll
-    for (int u = 0; u < CP_UNROLL; ++u) {
+    for (int u = 0; u < CP_UNROLL; ++u) {   // unconditional (clamped) loads keep v in VGPRs
       const int i = base + u * 64 + lane;
-      if (i < row_chunks) v[u] = src[i];
+      v[u] = src[i < row_chunks ? i : row_chunks - 1];
     }
-    for (int j = 0; j < nd; ++j) {
-      uint4* out = xp + (int64_t)dst[j] * row_chunks;
+    for (int k = 0; k < K; ++k) {
+      const int d = dest_row[t * K + k];
+      if (d < 0) continue;
+      uint4* out = xp + (int64_t)d * row_chunks;
 #pragma unroll
       for (int u = 0; u < CP_UNROLL; ++u) {
         const int i = base + u * 64 + lane;

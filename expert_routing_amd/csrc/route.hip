@@ -6,9 +6,13 @@
 // significant bits, so every remainder is representable), and x*hi + x*mid + x*lo are
 // summed into fp32 accumulators. Every product of bf16 operands is exact in fp32, so
 // this is an fp32 GEMM with exact operands and fp32 accumulation, at bf16 MFMA rate.
-// fp32 activations take a plain VALU GEMM. The reduction is split along h into k-slices
-// (enough blocks for the chip) whose partial logits are added in slice order before, or
-// while, selecting.
+// fp32 activations take a plain VALU GEMM.
+//
+// Three shapes of router: up to 16 experts (bf16), one fused kernel computes a group of
+// tokens' logits and selects in its epilogue, so the logits never reach HBM; batches of at
+// most 64 tokens stream the router weight once (it outweighs x) into k-slabs of partial
+// logits; everything else runs a tiled GEMM whose k-slices write slabs of partial logits.
+// Slabs are added in slab order by the selection kernel (deterministic).
 #include "moe_internal.h"
 
 namespace moe {
@@ -56,31 +60,30 @@ __global__ __launch_bounds__(256) void router_gemm_bf16(const bf16_t* __restrict
   // Global loads of the next k-step go to registers while the MFMAs run on the current
   // one, so a block always has one stage in flight.
   constexpr int WPT = BE * 16 / 256;         // float4 of W per thread per k-step
-  uint4 xr[2];
+  uint4 xr0, xr1;       // (two named registers: an array here was kept in scratch)
   float4 wr[WPT];
+  // x tile: 64 rows x 8 chunks = 512 chunks, 2 per thread (rows r and r + 32)
+  const int xr_r = tid >> 3, xr_c = tid & 7;
+  const int xt0 = t0 + xr_r < T ? t0 + xr_r : T - 1;
+  const int xt1 = t0 + xr_r + 32 < T ? t0 + xr_r + 32 : T - 1;
   auto load = [&](int k0) __attribute__((always_inline)) {
-    // x tile: 64 rows x 8 chunks = 512 chunks, 2 per thread
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int id = tid + i * 256, r = id >> 3, c = id & 7;
-      const int t = t0 + r < T ? t0 + r : T - 1;
-      xr[i] = *reinterpret_cast<const uint4*>(x + (size_t)t * h + k0 + c * 8);
-    }
+    xr0 = *reinterpret_cast<const uint4*>(x + (size_t)xt0 * h + k0 + xr_c * 8);
+    xr1 = *reinterpret_cast<const uint4*>(x + (size_t)xt1 * h + k0 + xr_c * 8);
     // w tile: BE rows x 64 fp32 = BE*16 float4
 #pragma unroll
     for (int i = 0; i < WPT; ++i) {
       const int id = tid + i * 256, r = id >> 4, q = id & 15;
       const int e = ebase + r;
-      wr[i] = e < E ? *reinterpret_cast<const float4*>(w + (size_t)e * h + k0 + q * 4)
-                    : float4{0.f, 0.f, 0.f, 0.f};
+      // rows past E load row E - 1 and are zeroed after the load (a lane-divergent load
+      // would keep wr out of registers)
+      const float4 v =
+          *reinterpret_cast<const float4*>(w + (size_t)(e < E ? e : E - 1) * h + k0 + q * 4);
+      wr[i] = e < E ? v : float4{0.f, 0.f, 0.f, 0.f};
     }
   };
   auto store = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int id = tid + i * 256, r = id >> 3, c = id & 7;
-      xs[swz(r, c)] = xr[i];
-    }
+    xs[swz(xr_r, xr_c)] = xr0;
+    xs[swz(xr_r + 32, xr_c)] = xr1;
     // W split into 3 bf16 planes; 4 bf16 = half a 16-byte chunk
 #pragma unroll
     for (int i = 0; i < WPT; ++i) {
@@ -181,10 +184,387 @@ __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
+// ---- selection of one token by a segment of SEG lanes --------------------------------
+// Lane j of the segment holds experts j, j + SEG, ... (KPL keys per lane; KPL * SEG >= E).
+// Scoring, group limit, K rounds of a segment-wide (key desc, index asc) arg-max with
+// shuffles, weights, and the ids written in ascending order with weights aligned. A key of
+// -inf is an ordinary candidate (after every finite key, by index); the group limit removes
+// experts through a mask. When the group limit is on, every thread of the block must call
+// this (it synchronises the block); `active` says whether the segment has a token.
+// ks / gs / ga: this token's LDS rows for keys [E], group scores and flags [n_groups].
+template <int SEG, int KPL>
+__device__ __forceinline__ void select_token(
+    const float (&Lin)[KPL], bool active, const float* __restrict__ bias, int E, int K,
+    int score, int renorm, int n_groups, int topk_groups, float* ks, float* gs, int* ga,
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+  const int lane = threadIdx.x & 63;
+  const int sl = lane & (SEG - 1), base = lane & ~(SEG - 1);
+  float L[KPL], key[KPL], raw[KPL];
+  uint32_t allow = 0;   // bit j: expert j*SEG + sl is a candidate
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int e = j * SEG + sl;
+    float l = -INFINITY, k = -INFINITY, r = 0.f;
+    if (active && e < E) {
+      allow |= 1u << j;
+      l = Lin[j];
+      const float b = bias ? bias[e] : 0.f;
+      if (score == MOE_SCORE_SOFTMAX) {
+        l += b;
+        k = l;
+      } else {
+        r = 1.f / (1.f + expf(-l));
+        k = r + b;
+      }
+    }
+    L[j] = l; key[j] = k; raw[j] = r;
+  }
+  if (n_groups > 1 && topk_groups < n_groups) {
+    const int gsz = E / n_groups;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int e = j * SEG + sl;
+      if (e < E) ks[e] = key[j];
+    }
+    __syncthreads();
+    for (int g = sl; g < n_groups; g += SEG) {
+      float b1 = -INFINITY, b2 = -INFINITY;
+      for (int i = 0; i < gsz; ++i) {
+        const float v = ks[g * gsz + i];
+        if (v > b1) { b2 = b1; b1 = v; } else if (v > b2) { b2 = v; }
+      }
+      gs[g] = gsz > 1 ? b1 + b2 : b1;
+    }
+    __syncthreads();
+    for (int g = sl; g < n_groups; g += SEG) {
+      const float sg = gs[g];
+      int rank = 0;
+      for (int q = 0; q < n_groups; ++q) rank += better(gs[q], q, sg, g) ? 1 : 0;
+      ga[g] = rank < topk_groups;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int e = j * SEG + sl;
+      if (e < E && !ga[e / gsz]) allow &= ~(1u << j);
+    }
+  }
+  if (!active) return;
+
+  // K rounds of a segment-wide arg-max over the remaining candidates; the sentinel (index
+  // INT_MAX) loses to every candidate, -inf keys included.
+  int win_e = -1;        // segment lane k < K keeps the k-th winner
+  float win_L = 0.f, win_r = 0.f;
+  for (int k = 0; k < K; ++k) {
+    float bk = -INFINITY; int bi = 0x7fffffff; float bl = 0.f, br = 0.f;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int e = j * SEG + sl;
+      if ((allow >> j & 1u) && better(key[j], e, bk, bi)) {
+        bk = key[j]; bi = e; bl = L[j]; br = raw[j];
+      }
+    }
+#pragma unroll
+    for (int off = SEG / 2; off > 0; off >>= 1) {
+      const float ok = __shfl_xor(bk, off);
+      const int oi = __shfl_xor(bi, off);
+      const float ol = __shfl_xor(bl, off);
+      const float orr = __shfl_xor(br, off);
+      if (better(ok, oi, bk, bi)) { bk = ok; bi = oi; bl = ol; br = orr; }
+    }
+    if (bi < E && (bi & (SEG - 1)) == sl) allow &= ~(1u << (bi / SEG));
+    if (sl == k) { win_e = bi; win_L = bl; win_r = br; }
+  }
+  // Weights of the K winners (segment lanes 0..K-1).
+  float wv = 0.f;
+  if (score == MOE_SCORE_SOFTMAX) {
+    if (renorm) {
+      const float m = __shfl(win_L, base);   // first winner has the largest logit
+      const float ex = sl < K ? expf(win_L - m) : 0.f;
+      float z = ex;
+#pragma unroll
+      for (int off = SEG / 2; off > 0; off >>= 1) z += __shfl_xor(z, off);
+      wv = ex / z;
+    } else {
+      float m = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) m = fmaxf(m, L[j]);
+#pragma unroll
+      for (int off = SEG / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      float z = 0.f;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        const int e = j * SEG + sl;
+        if (e < E) z += expf(L[j] - m);
+      }
+#pragma unroll
+      for (int off = SEG / 2; off > 0; off >>= 1) z += __shfl_xor(z, off);
+      wv = expf(win_L - m) / z;
+    }
+  } else {
+    if (renorm) {
+      float z = sl < K ? win_r : 0.f;
+#pragma unroll
+      for (int off = SEG / 2; off > 0; off >>= 1) z += __shfl_xor(z, off);
+      wv = win_r / z;
+    } else {
+      wv = win_r;
+    }
+  }
+  // Ascending-id order: position = number of winners with a smaller id.
+  int pos = 0;
+  for (int q = 0; q < K; ++q) {
+    const int oe = __shfl(win_e, base + q);
+    pos += (oe < win_e) ? 1 : 0;
+  }
+  if (sl < K) {
+    ids_out[pos] = win_e;
+    w_out[pos] = wv;
+  }
+}
+
+// ---- fused router for E <= 16 (bf16 activations) -------------------------------------
+// One block of 16 waves per group of 16 tokens (grid-stride over groups). The waves split
+// h into k32 steps (wave w takes steps w, w + 16, ...): per step a lane loads 16 bytes of
+// one token's row of x and 8 fp32 of one expert's router row, splits the latter into bf16
+// hi / mid / lo parts, and runs bf16 MFMA 16x16x32 with the tokens as rows. With E <= 8
+// the 16 MFMA columns hold hi (experts 0..7) and mid (the same experts), the lo part
+// rides in a second MFMA, so each step takes two MFMAs. Columns past E compute values
+// nobody reads. With E <= 8 the two lanes of an expert (columns n and n + 8) each load and
+// split half of the step's 8 values and swap parts through DPP. The waves' partial logits
+// meet in LDS and are added in wave order; then
+// each wave selects for 4 tokens, 16 lanes per token. The logits never leave the chip.
+// The next batch of loads is issued before the current batch's MFMAs.
+constexpr int RS_NW = 16;     // waves per block
+
+// Steps per load batch: the paired layout holds 16 bytes of x and 16 of W per step and lane,
+// the other one 16 + 32 (within the 128 VGPRs of 16 waves per CU).
+template <bool PAIRED>
+constexpr int rs_u() { return PAIRED ? 8 : 4; }
+
+// W: with PAIRED, lane n < 8 loads k-values 0..3 of the lane's 8-value chunk and lane n + 8
+// loads 4..7 (a float4 each); otherwise a lane loads all 8 (two float4).
+template <bool PAIRED, int U>
+__device__ __forceinline__ void rs_load(uint4 (&xv)[U], float4 (&wv)[U][PAIRED ? 1 : 2],
+                                        const bf16_t* __restrict__ xrow,
+                                        const float* __restrict__ wrow, int s0, int S) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    int s = s0 + u * RS_NW;
+    s = s < S ? s : S - 1;      // past the end: a valid address, never used
+    xv[u] = *reinterpret_cast<const uint4*>(xrow + s * 32);
+    wv[u][0] = *reinterpret_cast<const float4*>(wrow + s * 32);
+    if (!PAIRED) wv[u][PAIRED ? 0 : 1] = *reinterpret_cast<const float4*>(wrow + s * 32 + 4);
+  }
+}
+
+// Packs the bf16 hi / mid / lo parts of two fp32 values into one dword per part.
+__device__ __forceinline__ void split3_pair(float a, float b, uint32_t& ph, uint32_t& pm,
+                                            uint32_t& pl) {
+  bf16_t h0, m0, l0, h1, m1, l1;
+  split3(a, h0, m0, l0);
+  split3(b, h1, m1, l1);
+  ph = (uint32_t)h0 | ((uint32_t)h1 << 16);
+  pm = (uint32_t)m0 | ((uint32_t)m1 << 16);
+  pl = (uint32_t)l0 | ((uint32_t)l1 << 16);
+}
+
+// Value of the lane 8 positions away within the lane's row of 16 (DPP row rotate by 8).
+__device__ __forceinline__ uint32_t row_swap8(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xf, 0xf, false);
+}
+
+template <bool PAIRED, int U>
+__device__ __forceinline__ void rs_compute(floatx4& acc, const uint4 (&xv)[U],
+                                           const float4 (&wv)[U][PAIRED ? 1 : 2], int s0,
+                                           int S, bool hi_col) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (s0 + u * RS_NW < S) {
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xv[u]);
+      if (PAIRED) {
+        // this lane splits its 4 values; the partner lane (n xor 8) split the other 4 of
+        // the same expert's chunk. Column n < 8 takes hi (+ lo in the second MFMA) of all 8
+        // values, column n + 8 takes mid.
+        uint32_t h[2], m[2], l[2];
+        split3_pair(wv[u][0].x, wv[u][0].y, h[0], m[0], l[0]);
+        split3_pair(wv[u][0].z, wv[u][0].w, h[1], m[1], l[1]);
+        uint32_t hp[2], mp[2], lp[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          hp[q] = row_swap8(h[q]);
+          mp[q] = row_swap8(m[q]);
+          lp[q] = row_swap8(l[q]);
+        }
+        // hi lanes own k 0..3 (partner 4..7); mid lanes own k 4..7 (partner 0..3)
+        uint4 b1, b2;
+        b1.x = hi_col ? h[0] : mp[0]; b1.y = hi_col ? h[1] : mp[1];
+        b1.z = hi_col ? hp[0] : m[0]; b1.w = hi_col ? hp[1] : m[1];
+        b2.x = hi_col ? l[0] : 0u;    b2.y = hi_col ? l[1] : 0u;
+        b2.z = hi_col ? lp[0] : 0u;   b2.w = hi_col ? lp[1] : 0u;
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, b2), acc,
+                                                      0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, b1), acc,
+                                                      0, 0, 0);
+      } else {
+        const float f[8] = {wv[u][0].x, wv[u][0].y, wv[u][0].z, wv[u][0].w,
+                            wv[u][PAIRED ? 0 : 1].x, wv[u][PAIRED ? 0 : 1].y,
+                            wv[u][PAIRED ? 0 : 1].z, wv[u][PAIRED ? 0 : 1].w};
+        uint32_t ph[4], pm[4], pl[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) split3_pair(f[2 * q], f[2 * q + 1], ph[q], pm[q], pl[q]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            a, __builtin_bit_cast(bf16x8_t, uint4{pl[0], pl[1], pl[2], pl[3]}), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            a, __builtin_bit_cast(bf16x8_t, uint4{pm[0], pm[1], pm[2], pm[3]}), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            a, __builtin_bit_cast(bf16x8_t, uint4{ph[0], ph[1], ph[2], ph[3]}), acc, 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <bool PAIRED>
+__global__ __launch_bounds__(64 * RS_NW) void router_small_e(
+    const bf16_t* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
+    int32_t* __restrict__ ids, float* __restrict__ wout, int T, int h, int E, int K,
+    int score, int renorm, int n_groups, int topk_groups) {
+  __shared__ float red[RS_NW][16][17];
+  __shared__ float lg[16][17];
+  __shared__ float sel_k[4 * RS_NW][16];
+  __shared__ float sel_g[4 * RS_NW][16];
+  __shared__ int sel_a[4 * RS_NW][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, kq = lane >> 4;
+  int e_row = PAIRED ? (n & 7) : n;
+  e_row = e_row < E ? e_row : E - 1;                  // columns past E: ignored results
+  const bool hi_col = n < 8;
+  const int S = h / 32;                               // k32 steps
+  const int ngroups = (T + 15) / 16;
+  const float* wrow = w + (size_t)e_row * h + kq * 8 + ((PAIRED && !hi_col) ? 4 : 0);
+  constexpr int RS_U = rs_u<PAIRED>();
+  constexpr int STRIDE = RS_NW * RS_U;
+  for (int grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
+    const int t0 = grp * 16;
+    const int tok = t0 + n < T ? t0 + n : T - 1;      // MFMA row = token
+    const bf16_t* xrow = x + (size_t)tok * h + kq * 8;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    uint4 xa[RS_U];
+    float4 wa[RS_U][PAIRED ? 1 : 2];
+    // one batch of RS_U steps in flight per wave: with 16 waves that is all of h <= 4096
+    for (int s0 = wave; s0 < S; s0 += STRIDE) {
+      rs_load<PAIRED>(xa, wa, xrow, wrow, s0, S);
+      rs_compute<PAIRED>(acc, xa, wa, s0, S, hi_col);
+    }
+    // acc[j]: token 4*kq + j, column n (PAIRED: columns n and n + 8 hold one expert)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float v = acc[j];
+      if (PAIRED) v += __shfl_xor(v, 8);
+      red[wave][4 * kq + j][n] = v;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      const int tk = tid >> 4, e = tid & 15;
+      float s = red[0][tk][e];
+#pragma unroll
+      for (int q = 1; q < RS_NW; ++q) s += red[q][tk][e];
+      lg[tk][e] = s;
+    }
+    __syncthreads();
+    // selection: wave w takes tokens 4w .. 4w + 3 of the group (waves 4.. have none but
+    // still pass the group limit's barriers), 16 lanes per token
+    const int slot = wave * 4 + kq;
+    const bool active = slot < 16 && t0 + slot < T;
+    const float L[1] = {active ? lg[slot][n] : 0.f};
+    const size_t t = (size_t)(t0 + (active ? slot : 0));
+    select_token<16, 1>(L, active, bias, E, K, score, renorm, n_groups, topk_groups,
+                        sel_k[slot], sel_g[slot], sel_a[slot], ids + t * K, wout + t * K);
+    __syncthreads();
+  }
+}
+
+// ---- router for small batches (T <= 64, bf16 activations) ----------------------------
+// The router weight (E x h fp32) is the bulk of the bytes: every block streams a slab of
+// 16 experts x kslice of it once, with the batch's x columns for that k range staged in
+// LDS. 16 threads per expert split the k range in float4 steps, each holding TB token
+// accumulators (fp32 FMA on exact bf16 -> fp32 activations); a butterfly over those 16
+// lanes adds them, and the block's partial logits go to slab blockIdx.y, which select adds
+// in slab order.
+constexpr int GV_EB = 16;
+constexpr int GV_MAXI = 16;   // float4 steps per thread: kslice <= 16 * 64 = 1024
+
+template <int TB>
+__global__ __launch_bounds__(256) void router_gemv(const bf16_t* __restrict__ x,
+                                                   const float* __restrict__ w,
+                                                   float* __restrict__ logits, int T, int h,
+                                                   int E, int kslice) {
+  extern __shared__ uint4 xs_raw[];                   // [TB][kslice] bf16
+  bf16_t* xs = reinterpret_cast<bf16_t*>(xs_raw);
+  const int tid = threadIdx.x, kl = tid & 15;
+  const int e = blockIdx.x * GV_EB + (tid >> 4);
+  const int kb = blockIdx.y * kslice;
+  const int klen = kb + kslice <= h ? kslice : h - kb;   // a multiple of 64
+  // the thread's float4 steps of its expert's row (k = 4*kl + 64*i), all issued before x
+  // is staged, so one memory round trip covers both; steps past klen load a valid
+  // address and are never used
+  const float* wr = w + (size_t)(e < E ? e : E - 1) * h + kb;
+  float4 wv[GV_MAXI];
+#pragma unroll
+  for (int i = 0; i < GV_MAXI; ++i) {
+    const int k0 = 4 * kl + 64 * i;
+    wv[i] = *reinterpret_cast<const float4*>(wr + (k0 < klen ? k0 : 4 * kl));
+  }
+  // stage x[0..T)[kb, kb + klen) as 16-byte chunks; rows past T are zero
+  const int cpr = klen / 8;
+  for (int i = tid; i < TB * cpr; i += 256) {
+    const int t = i / cpr, c = i % cpr;
+    uint4 v = uint4{0, 0, 0, 0};
+    if (t < T) v = *reinterpret_cast<const uint4*>(x + (size_t)t * h + kb + c * 8);
+    *reinterpret_cast<uint4*>(xs + (size_t)t * kslice + c * 8) = v;
+  }
+  __syncthreads();
+  float acc[TB];
+#pragma unroll
+  for (int t = 0; t < TB; ++t) acc[t] = 0.f;
+#pragma unroll
+  for (int i = 0; i < GV_MAXI; ++i) {
+    const int k0 = 4 * kl + 64 * i;
+    if (k0 >= klen) break;
+    const float4 v4 = wv[i];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      const uint2 xv = *reinterpret_cast<const uint2*>(xs + (size_t)t * kslice + k0);
+      float a = acc[t];
+      a = fmaf(v4.x, __uint_as_float(xv.x << 16), a);
+      a = fmaf(v4.y, __uint_as_float(xv.x & 0xffff0000u), a);
+      a = fmaf(v4.z, __uint_as_float(xv.y << 16), a);
+      a = fmaf(v4.w, __uint_as_float(xv.y & 0xffff0000u), a);
+      acc[t] = a;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TB; ++t) {
+    float v = acc[t];
+    v += __shfl_xor(v, 8);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 1);
+    acc[t] = v;
+  }
+  if (e < E) {
+    float* out = logits + (size_t)blockIdx.y * T * E;
+#pragma unroll
+    for (int t = 0; t < TB; ++t)
+      if ((t & 15) == kl && t < T) out[(size_t)t * E + e] = acc[t];
+  }
+}
+
 constexpr int SEL_KPL = 8;     // keys per lane: E <= 512
 constexpr int SEL_TOK = 4;     // tokens (waves) per block
 
-// One wave per token. Lane l holds experts l, l+64, ...
+// One wave per token. Lane l holds experts l, l+64, ... Partial logits of nsplit slabs
+// are added in slab order, then select_token scores and selects.
 __global__ __launch_bounds__(256) void select_topk(const float* __restrict__ logits,
                                                    const float* __restrict__ bias,
                                                    int32_t* __restrict__ ids,
@@ -197,142 +577,34 @@ __global__ __launch_bounds__(256) void select_topk(const float* __restrict__ log
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * SEL_TOK + wave;
   const bool active = t < T;
+  // partial logits of the nsplit slabs added in slab order; every load of a chunk of 8
+  // slabs is issued before the additions (lanes past E read a valid address)
   const int kpl = (E + 63) >> 6;
-  float L[SEL_KPL], key[SEL_KPL], raw[SEL_KPL];
+  const int64_t tr = active ? t : 0;
+  float L[SEL_KPL];
 #pragma unroll
-  for (int j = 0; j < SEL_KPL; ++j) {
-    const int e = j * 64 + lane;
-    float l = -INFINITY, k = -INFINITY, r = 0.f;
-    if (active && j < kpl && e < E) {
-      l = logits[t * E + e];
-      // partial logits added in slice order; loads in groups of 8 so they overlap
-      for (int z0 = 1; z0 < nsplit; z0 += 8) {
-        float v[8];
+  for (int j = 0; j < SEL_KPL; ++j) L[j] = 0.f;
+  for (int z0 = 0; z0 < nsplit; z0 += 8) {
+    float v[8][SEL_KPL];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          v[u] = z0 + u < nsplit ? logits[(size_t)(z0 + u) * T * E + t * E + e] : 0.f;
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (z0 + u < nsplit) l += v[u];
-      }
-      const float b = bias ? bias[e] : 0.f;
-      if (score == MOE_SCORE_SOFTMAX) {
-        l += b;
-        k = l;
-      } else {
-        r = 1.f / (1.f + __expf(-l));
-        k = r + b;
-      }
-    }
-    L[j] = l; key[j] = k; raw[j] = r;
-  }
-  const bool glimit = n_groups > 1 && topk_groups < n_groups;
-  if (glimit) {   // uniform across the block: every wave takes the same barriers
-    const int gsz = E / n_groups;
-#pragma unroll
-    for (int j = 0; j < SEL_KPL; ++j) {
-      const int e = j * 64 + lane;
-      if (j < kpl && e < E) keys_s[wave][e] = key[j];
-    }
-    __syncthreads();
-    for (int g = lane; g < n_groups; g += 64) {
-      float b1 = -INFINITY, b2 = -INFINITY;
-      for (int i = 0; i < gsz; ++i) {
-        const float v = keys_s[wave][g * gsz + i];
-        if (v > b1) { b2 = b1; b1 = v; } else if (v > b2) { b2 = v; }
-      }
-      gscore_s[wave][g] = gsz > 1 ? b1 + b2 : b1;
-    }
-    __syncthreads();
-    for (int g = lane; g < n_groups; g += 64) {
-      const float sg = gscore_s[wave][g];
-      int rank = 0;
-      for (int q = 0; q < n_groups; ++q) {
-        const float sq = gscore_s[wave][q];
-        rank += (sq > sg || (sq == sg && q < g)) ? 1 : 0;
-      }
-      gallow_s[wave][g] = rank < topk_groups;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < SEL_KPL; ++j) {
-      const int e = j * 64 + lane;
-      if (j < kpl && e < E && !gallow_s[wave][e / gsz]) key[j] = -INFINITY;
-    }
-  }
-  if (!active) return;
-
-  // K rounds of a wave-wide arg-max over the remaining allowed experts.
-  uint32_t taken = 0;
-  int win_e = -1;        // lane k < K keeps the k-th winner
-  float win_L = 0.f, win_r = 0.f;
-  for (int k = 0; k < K; ++k) {
-    float bk = -INFINITY; int bi = 0x7fffffff; float bl = 0.f, br = 0.f;
-#pragma unroll
-    for (int j = 0; j < SEL_KPL; ++j) {
-      const int e = j * 64 + lane;
-      if (j < kpl && e < E && !(taken >> j & 1u) && key[j] != -INFINITY &&
-          better(key[j], e, bk, bi)) {
-        bk = key[j]; bi = e; bl = L[j]; br = raw[j];
-      }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ok = __shfl_xor(bk, off);
-      const int oi = __shfl_xor(bi, off);
-      const float ol = __shfl_xor(bl, off);
-      const float orr = __shfl_xor(br, off);
-      if (better(ok, oi, bk, bi)) { bk = ok; bi = oi; bl = ol; br = orr; }
-    }
-    if (bi < E && (bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == k) { win_e = bi; win_L = bl; win_r = br; }
-  }
-  // Weights of the K winners (lanes 0..K-1).
-  float wv = 0.f;
-  if (score == MOE_SCORE_SOFTMAX) {
-    if (renorm) {
-      const float m = __shfl(win_L, 0);      // first winner has the largest logit
-      const float ex = lane < K ? __expf(win_L - m) : 0.f;
-      float z = ex;
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
-      wv = ex / z;
-    } else {
-      float m = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < SEL_KPL; ++j) m = fmaxf(m, L[j]);
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-      float z = 0.f;
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
       for (int j = 0; j < SEL_KPL; ++j) {
         const int e = j * 64 + lane;
-        if (j < kpl && e < E) z += __expf(L[j] - m);
+        v[u][j] = (z0 + u < nsplit && j < kpl)
+                      ? logits[(size_t)(z0 + u) * T * E + tr * E + (e < E ? e : E - 1)]
+                      : 0.f;
       }
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
-      wv = __expf(win_L - m) / z;
-    }
-  } else {
-    if (renorm) {
-      float z = lane < K ? win_r : 0.f;
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
-      wv = win_r / z;
-    } else {
-      wv = win_r;
-    }
+      for (int j = 0; j < SEL_KPL; ++j)
+        if (z0 + u < nsplit) L[j] = (z0 + u == 0) ? v[u][j] : L[j] + v[u][j];
   }
-  // Ascending-id order: position = number of winners with a smaller id.
-  int pos = 0;
-  for (int q = 0; q < K; ++q) {
-    const int oe = __shfl(win_e, q);
-    pos += (oe < win_e) ? 1 : 0;
-  }
-  if (lane < K) {
-    ids[t * K + pos] = win_e;
-    wout[t * K + pos] = wv;
-  }
+  const int64_t tt = active ? t : 0;
+  select_token<64, SEL_KPL>(L, active, bias, E, K, score, renorm, n_groups, topk_groups,
+                            keys_s[wave], gscore_s[wave], gallow_s[wave], ids + tt * K,
+                            wout + tt * K);
 }
 
 // Partial logits of the k-slices added in slice order into slab 0, one thread per
@@ -357,16 +629,52 @@ __global__ __launch_bounds__(256) void logits_reduce(float* __restrict__ logits,
 
 }  // namespace
 
+// Which router a problem takes: the fused small-expert-count router, the weight-streaming
+// router for small batches, or the tiled GEMM with k-slices plus a selection kernel.
+enum class RouterPath { Fused, Gemv, Gemm };
+
+static RouterPath router_path(const Dims& d) {
+  if (d.bf16 && d.E <= 16) return RouterPath::Fused;
+  if (d.bf16 && d.T <= 64) return RouterPath::Gemv;
+  return RouterPath::Gemm;
+}
+
+static int gemv_tb(const Dims& d) { return d.T <= 32 ? 32 : 64; }
+
+// k-slice length of the small-batch router: about 256 blocks, slices a multiple of 64
+// along h whose staged x (tb rows) fits 64 KB of LDS.
+static int gemv_kslice(const Dims& d) {
+  const int eb = (d.E + GV_EB - 1) / GV_EB;
+  int z = (256 + eb - 1) / eb;
+  const int zmax = d.h / 64;
+  z = z < 1 ? 1 : (z > zmax ? zmax : z);
+  int ks = ((d.h + z - 1) / z + 63) / 64 * 64;
+  const int ks_max = (64 * 1024) / (2 * gemv_tb(d));
+  return ks > ks_max ? ks_max : ks;
+}
+
 // K-slices of the router GEMM: enough blocks for about four per CU (each keeps one
 // k-step of loads in flight, so four hide most of the memory latency), slices of at
 // least 256 along h (a multiple of the 64-wide k-step).
-int route_split(const Dims& d) {
+static int gemm_split(const Dims& d) {
   const int64_t tiles = ((d.T + RT_BM - 1) / RT_BM) *
                         ((d.E + 63) / 64 > 0 ? (d.E + 63) / 64 : 1);
   int s = tiles > 0 ? (int)((1024 + tiles - 1) / tiles) : 1;
   const int smax = d.h / 256 > 1 ? d.h / 256 : 1;
   s = s < 1 ? 1 : (s > smax ? smax : s);
   return s;
+}
+
+// Slabs of partial logits [T][E] fp32 the router leaves in the workspace.
+int route_split(const Dims& d) {
+  switch (router_path(d)) {
+    case RouterPath::Fused: return 0;
+    case RouterPath::Gemv: {
+      const int ks = gemv_kslice(d);
+      return (d.h + ks - 1) / ks;
+    }
+    default: return gemm_split(d);
+  }
 }
 
 static int select_with(const moe_problem* p, const Dims& d, const float* logits, int nsplit,
@@ -385,19 +693,45 @@ int launch_select(const moe_problem* p, const Dims& d, const float* logits, cons
 
 int launch_route(const moe_problem* p, const Dims& d, const void* x, const float* w_router,
                  const float* bias, int32_t* ids, float* w, float* logits, hipStream_t st) {
+  const bf16_t* xb = static_cast<const bf16_t*>(x);
+  const RouterPath path = router_path(d);
+  if (path == RouterPath::Fused) {
+    const int64_t groups = (d.T + 15) / 16;
+    const unsigned grid = (unsigned)(groups < 2048 ? groups : 2048);
+    if (d.E <= 8)
+      hipLaunchKernelGGL(router_small_e<true>, dim3(grid), dim3(64 * RS_NW), 0, st, xb,
+                         w_router, bias, ids, w, (int)d.T, d.h, d.E, d.K, p->score, p->renorm,
+                         p->n_groups, p->topk_groups);
+    else
+      hipLaunchKernelGGL(router_small_e<false>, dim3(grid), dim3(64 * RS_NW), 0, st, xb,
+                         w_router, bias, ids, w, (int)d.T, d.h, d.E, d.K, p->score, p->renorm,
+                         p->n_groups, p->topk_groups);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+  }
+  if (path == RouterPath::Gemv) {
+    const int ks = gemv_kslice(d);
+    const int z = (d.h + ks - 1) / ks;
+    const int tb = gemv_tb(d);
+    const dim3 grid((unsigned)((d.E + GV_EB - 1) / GV_EB), (unsigned)z);
+    const size_t lds = (size_t)tb * ks * 2;
+    if (tb == 32)
+      hipLaunchKernelGGL(router_gemv<32>, grid, dim3(256), lds, st, xb, w_router, logits,
+                         (int)d.T, d.h, d.E, ks);
+    else
+      hipLaunchKernelGGL(router_gemv<64>, grid, dim3(256), lds, st, xb, w_router, logits,
+                         (int)d.T, d.h, d.E, ks);
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
+    return select_with(p, d, logits, z, bias, ids, w, st);
+  }
   const unsigned gt = (unsigned)((d.T + RT_BM - 1) / RT_BM);
   const int S = d.route_split;
   // k-slice length: a multiple of 64 covering h in S slices
   const int kslice = ((d.h + S - 1) / S + 63) / 64 * 64;
   const unsigned gz = (unsigned)((d.h + kslice - 1) / kslice);
   if (d.bf16) {
-    const int be = d.E <= 16 ? 16 : (d.E <= 32 ? 32 : 64);
+    const int be = d.E <= 32 ? 32 : 64;
     const dim3 grid(gt, (unsigned)((d.E + be - 1) / be), gz);
-    const bf16_t* xb = static_cast<const bf16_t*>(x);
-    if (be == 16)
-      hipLaunchKernelGGL(router_gemm_bf16<16>, grid, dim3(256), 0, st, xb, w_router, logits,
-                         (int)d.T, d.h, d.E, kslice);
-    else if (be == 32)
+    if (be == 32)
       hipLaunchKernelGGL(router_gemm_bf16<32>, grid, dim3(256), 0, st, xb, w_router, logits,
                          (int)d.T, d.h, d.E, kslice);
     else

@@ -77,8 +77,14 @@ def rel_errors(got, ref):
 # and 5e-3 mean-relative (fp32 accumulation, one bf16 rounding of the gated product and
 # one of each output).
 TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 5e-3)}
-# Routing weights: fp32 logits (<= ~1e-6 relative error on h <= 7168 accumulations)
-# moved through exp / sigmoid and a normalisation.
+# Routing weights. From given fp32 logits (moe_select) only the kernels' exp, sigmoid and
+# division round: a few ulp, so 1e-6 relative. From x (moe_route) the weights also carry
+# the fp32 logits' accumulation error: a weight moves by at most 2 max_e |dL_e| relative
+# (softmax over the selection, or sigmoid renormalised). The router's partial sums stay
+# O(1) (x ~ N(0,1), W_r ~ N(0,1/h)), so a length-h fp32 sum errs by about u sqrt(h) in
+# probability (u = 2^-24; 5e-6 at h = 7168), i.e. weights within ~1e-5; 1e-4 leaves a
+# margin of ten for the tails over tens of thousands of weights.
+W_RTOL_SELECT = 1e-6
 W_RTOL = 1e-4
 
 
