@@ -94,11 +94,14 @@ _layout_stats = _sig("moe_layout_stats", [_P, _V, _V, _V, _V, _V, _V, _SZ, _V])
 _forward = _sig("moe_forward", [_P, ctypes.POINTER(Tensors), _V, _SZ, _V])
 _forward_traced = _sig("moe_forward_traced",
                        [_P, ctypes.POINTER(Tensors), _V, _SZ, _V, ctypes.POINTER(_V)])
+_forward_noalloc = _sig("moe_forward_noalloc", [_P, ctypes.POINTER(Tensors), _V])
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 TRACE_POINTS = ["begin", "route", "dispatch", "ffn_prep", "ffn_gate_up", "ffn_down", "combine"]
 
 EXPORTED = ["moe_check_problem", "moe_capacity", "moe_max_rows", "moe_workspace_bytes",
             "moe_status_string", "moe_route", "moe_select", "moe_dispatch", "moe_expert_ffn",
-            "moe_combine", "moe_layout_stats", "moe_forward", "moe_forward_traced"]
+            "moe_combine", "moe_layout_stats", "moe_forward", "moe_forward_traced",
+            "moe_forward_noalloc"]
 
 
 class MoeError(RuntimeError):
@@ -197,6 +200,13 @@ def moe_forward(p, t: dict, ws, stream=None):
     ts = Tensors(**{k: _ptr(t.get(k)) for k, _ in Tensors._fields_})
     wp, wn = _ws(ws)
     _ok(_forward(ctypes.byref(p), ctypes.byref(ts), wp, wn, _stream(stream)), "moe_forward")
+
+
+def moe_forward_noalloc(p, t: dict, stream=None):
+    """moe_forward with the library's own device scratch array as workspace (no ws)."""
+    ts = Tensors(**{k: _ptr(t.get(k)) for k, _ in Tensors._fields_})
+    _ok(_forward_noalloc(ctypes.byref(p), ctypes.byref(ts), _stream(stream)),
+        "moe_forward_noalloc")
 
 
 def moe_forward_traced(p, t: dict, ws, events, stream=None):

@@ -4,6 +4,9 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -350,6 +353,51 @@ int moe_forward_traced(const moe_problem* p, const moe_tensors* t, void* ws, siz
                        void* stream, void* const* events) {
   if (!events) return MOE_ERR_INVALID;
   return forward_impl(p, t, ws, ws_bytes, stream, events);
+}
+
+}  // extern "C"
+
+// ---- allocation-free forward --------------------------------------------------------
+// The workspace of moe_forward_noalloc is this file-scope device array: every GPU the
+// library runs on holds one copy (at its own address) until the process ends. In host
+// code `scratch` names a host-side stand-in, so kernels get the device address found by
+// hipGetSymbolAddress, once per device, with that device current.
+namespace moe {
+namespace {
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of this device's scratch array (nullptr if the runtime refuses).
+void* scratch_ptr(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!ptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
+}  // namespace
+}  // namespace moe
+
+extern "C" {
+
+int moe_forward_noalloc(const moe_problem* p, const moe_tensors* t, void* stream) {
+  Dims d;
+  int st = make_dims(p, &d);
+  if (st != MOE_OK) return st;
+  if (ws_layout(p, d).total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_LAUNCH;
+  void* ws = scratch_ptr(dev);
+  if (!ws) return MOE_ERR_LAUNCH;
+  return forward_impl(p, t, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 }  // extern "C"

@@ -262,6 +262,23 @@ enum moe_trace_point {
 int moe_forward_traced(const moe_problem* p, const moe_tensors* t, void* ws, size_t ws_bytes,
                        void* stream, void* const* events);
 
+/* ---- allocation-free forward ------------------------------------------------------
+ * For callers that cannot allocate device memory or pass a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): moe_forward with its
+ * workspace taken from a device array of MOE_NOALLOC_SCRATCH_BYTES that the library holds
+ * on every GPU it runs on, until the process ends. The caller still passes every input and
+ * output in `t`, exactly as for moe_forward, and gets bit-identical results.
+ *   - Problems whose moe_workspace_bytes() exceeds MOE_NOALLOC_SCRATCH_BYTES are refused
+ *     with MOE_ERR_WORKSPACE before anything is enqueued (64 MiB fits, for example, a
+ *     decode batch of up to ~1000 tokens with 256 experts of DeepSeek-V3 shape resident).
+ *   - The call allocates nothing. Its first call on a device looks up that device's copy
+ *     of the array (MOE_ERR_LAUNCH if the runtime refuses).
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap in time on one
+ *     GPU (other streams, other host threads) race and must be serialised by the caller.
+ *     A call needs nothing in the array to start at zero.                               */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_forward_noalloc(const moe_problem* p, const moe_tensors* t, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -138,3 +138,13 @@ def test_empty_batch_is_a_no_op():
     assert moe._route(b, None, None, None, None, None, None, 0, None) == 0
     assert moe._select(b, None, None, None, None, None) == 0
     assert moe._combine(b, None, None, None, None, None, None) == 0
+
+
+def test_noalloc_refuses_problems_beyond_its_scratch():
+    # the Mixtral-shaped layer needs ~288 MiB of workspace: refused before any launch
+    p = moe.problem_from_config(CONFIGS["mixtral_prefill"])
+    assert moe.workspace_bytes(p) > moe.NOALLOC_SCRATCH_BYTES
+    assert moe._forward_noalloc(moe.ctypes.byref(p), None, None) == -3
+    # invalid problems are reported as such first
+    bad = moe.Problem(T=32, h=64, E=8, K=9, inter=64)
+    assert moe._forward_noalloc(moe.ctypes.byref(bad), None, None) == -1
