@@ -10,11 +10,13 @@ softmax, SwiGLU inter=14336, bf16 with fp32 accumulation, fp32 router, no capaci
 Zipf-skewed with and without capacity, DeepSeek-V3 decode).
 
 A step is one moe_forward call: every kernel of the layer over one batch. `value` is the
-steady-state rate of K back-to-back steps. The same steps are then run again with the
-caches flushed before each one (a 1 GiB buffer is written, which evicts the 4 MB L2s and
-the 256 MB Infinity Cache), outside the stage events; `flushed` reports those stage times
-and the per-stage rates against the HBM / MFMA rooflines. Stage times come from HIP events
-the library records on its own launch stream (moe_forward_traced). The CPU baseline times
+steady-state rate of K back-to-back steps. Stage times come from HIP events the library
+records on its own launch stream between the stages (moe_forward_traced), minus the
+measured cost of an empty event pair (`event_pair_us`; an event record occupies the GPU for
+a few microseconds); `stages_traced_us` keeps the raw values. The traced steps are run again
+with the caches flushed before each one (a 1 GiB buffer is written, which evicts the 4 MB
+L2s and the 256 MB Infinity Cache), outside the stage events; `flushed` reports those stage
+times and the per-stage rates against the HBM / MFMA rooflines. The CPU baseline times
 the fp64 oracle on the same workload; its routing result also gives the near-tie count and
 the first-choice skew.
 """
@@ -262,19 +264,36 @@ def run_workload(name, args, moe, torch, np):
                 out[pts[j]] += ev.elapsed(i * npts + j - 1, i * npts + j) / args.steps
         return out
 
-    # steady state: K back-to-back steps
+    # steady state: K back-to-back untraced steps (the headline rate)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
-        moe.moe_forward_traced(p, t, b["ws"], ev.handles[i * npts:(i + 1) * npts])
+        moe.moe_forward(p, t, b["ws"])
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = start.elapsed_time(stop) / args.steps
+
+    # the same steps with HIP events between the stages (recorded by the library on its
+    # launch stream); each event record itself occupies the GPU for a few microseconds
+    for i in range(args.steps):
+        moe.moe_forward_traced(p, t, b["ws"], ev.handles[i * npts:(i + 1) * npts])
+    torch.cuda.synchronize()
     steady = stage_means()
+    # cost of one event pair with nothing between: measured, then taken off each stage
+    pairs = moe.HipEvents(2 * args.steps)
+    for i in range(args.steps):
+        pairs.record(2 * i)
+        pairs.record(2 * i + 1)
+    torch.cuda.synchronize()
+    overhead = sorted(pairs.elapsed(2 * i, 2 * i + 1) for i in range(args.steps))[args.steps // 2]
+    pairs.close()
+
+    def net(st):
+        return {k: max(v - overhead, 0.0) for k, v in st.items()}
 
     # flushed: each step starts with cold L2 and Infinity Cache
     flushed = None
@@ -299,7 +318,7 @@ def run_workload(name, args, moe, torch, np):
     gu = work["ffn_gate_up"]
     gu_bound = "mfma" if gu["flops"] / gu["bytes"] > RIDGE_BF16 else "hbm"
     traffic = load_traffic(name)
-    gu_ms = steady["ffn_gate_up"]
+    gu_ms = net(steady)["ffn_gate_up"]
     if gu_bound == "mfma":
         achieved = gu["flops"] / (gu_ms * 1e-3) / 1e12
         roof = {"kernel": "ffn_gate_up_bf16 (grouped gate/up GEMM, fused silu*mul)",
@@ -321,7 +340,7 @@ def run_workload(name, args, moe, torch, np):
             r[sname] = rate(work[sname], st[sname],
                             route_bound(cfg) if sname == "route" else
                             ("hbm" if sname in ("dispatch", "combine") else None))
-        r["ffn_prep"] = {"us": round(st["ffn_prep"] * 1e3, 2)}
+        r["ffn_prep"] = {"us": round(st["ffn_prep"] * 1e3, 2)}   # 0: built by dispatch
         # route + dispatch + prep + combine against their summed roofline times
         rdc_t = st["route"] + st["dispatch"] + st["ffn_prep"] + st["combine"]
         roof_t = 0.0
@@ -356,12 +375,15 @@ def run_workload(name, args, moe, torch, np):
         "roofline": roof,
         "routed_pairs_per_s": (T * K - dropped) / (ms * 1e-3),
         "layer_tflops": (gu["flops"] + work["ffn_down"]["flops"]) / (ms * 1e-3) / 1e12,
-        "stages_us": {k: round(v * 1e3, 2) for k, v in steady.items()},
-        "stage_rates": stage_rates(steady),
+        "event_pair_us": round(overhead * 1e3, 2),
+        "stages_traced_us": {k: round(v * 1e3, 2) for k, v in steady.items()},
+        "stages_us": {k: round(v * 1e3, 2) for k, v in net(steady).items()},
+        "stage_rates": stage_rates(net(steady)),
         "flushed": None if flushed is None else {
-            "ms_per_step": sum(flushed.values()),
-            "stages_us": {k: round(v * 1e3, 2) for k, v in flushed.items()},
-            "stage_rates": stage_rates(flushed)},
+            "ms_per_step": sum(net(flushed).values()),
+            "stages_traced_us": {k: round(v * 1e3, 2) for k, v in flushed.items()},
+            "stages_us": {k: round(v * 1e3, 2) for k, v in net(flushed).items()},
+            "stage_rates": stage_rates(net(flushed))},
         "layout": {"rows": R, "active_local_experts": active, "dropped": dropped,
                    "balancedness": float(counts.mean() / max(counts.max(), 1)),
                    "peak_to_mean": float(counts.max() / max(counts.mean(), 1e-30)),

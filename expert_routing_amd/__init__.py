@@ -234,6 +234,12 @@ class HipEvents:
                 raise RuntimeError("hipEventCreate failed")
             self.handles.append(e.value)
 
+    def record(self, i, stream=None):
+        """hipEventRecord of handle i on `stream` (default: torch's current stream)."""
+        self._hip.hipEventRecord.argtypes = [_V, _V]
+        if self._hip.hipEventRecord(self.handles[i], _stream(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
     def elapsed(self, a, b):
         ms = ctypes.c_float()
         if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.handles[a], self.handles[b]) != 0:

@@ -4,10 +4,11 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
-#include "moe_internal.h"
+#include "ffn_sched.h"
 
 namespace moe {
 
@@ -101,8 +102,11 @@ WsLayout ws_layout(const moe_problem* p, const Dims& d) {
   WsLayout L;
   size_t off = 0;
   const size_t n_chunks = (size_t)((d.T + kDispatchChunk - 1) / kDispatchChunk);
+  // pair-count rows: dispatch's 256-token chunks, or the router's smaller token groups
+  const int rt = route_count_tokens(d);
+  const size_t n_count_rows = std::max(n_chunks, (size_t)((d.T + rt - 1) / rt));
   L.logits = off;       off = align256(off + (size_t)d.route_split * d.T * d.E * 4);
-  L.chunk_counts = off; off = align256(off + n_chunks * d.E * 4);
+  L.chunk_counts = off; off = align256(off + n_count_rows * d.E * 4);
   L.chunk_base = off;   off = align256(off + n_chunks * d.E * 4);
   L.kept = off;         off = align256(off + (size_t)d.E * 4);
   L.sched = off;        off = align256(off + ffn_sched_bytes(d));
@@ -228,7 +232,7 @@ int moe_route(const moe_problem* p, const void* x, const float* w_router, const 
   if (d.T == 0) return MOE_OK;
   WsLayout L = ws_layout(p, d);
   return launch_route(p, d, x, w_router, bias, topk_ids, topk_w,
-                      (float*)((char*)ws + L.logits), (hipStream_t)stream);
+                      (float*)((char*)ws + L.logits), nullptr, (hipStream_t)stream);
 }
 
 int moe_select(const moe_problem* p, const float* logits, const float* bias,
@@ -324,18 +328,25 @@ static int forward_impl(const moe_problem* p, const moe_tensors* t, void* ws, si
   const WsLayout L = ws_layout(p, d);
   char* w = (char*)ws;
   if (!mark(MOE_TRACE_BEGIN)) return MOE_ERR_LAUNCH;
+  // the router also leaves dispatch's pair counts in the workspace
+  int32_t* chunk_counts = reinterpret_cast<int32_t*>(w + L.chunk_counts);
   if (d.T > 0 && (st = launch_route(p, d, t->x, t->w_router, t->bias, t->topk_ids, t->topk_w,
-                                    (float*)(w + L.logits), s)) != MOE_OK)
+                                    (float*)(w + L.logits), chunk_counts, s)) != MOE_OK)
     return st;
   if (!mark(MOE_TRACE_ROUTE)) return MOE_ERR_LAUNCH;
+  // dispatch also builds the expert FFN's tile table from the offsets it produces
+  FfnPrepArgs fa;
+  if ((st = ffn_prep_args(p, d, t->xp, t->w13, t->w2, t->x, t->w13_sh, t->w2_sh, t->yp,
+                          t->y_sh, w, L, gather ? t->row_src : nullptr, &fa)) != MOE_OK)
+    return st;
   if ((st = launch_dispatch(p, d, gather ? nullptr : t->x, t->topk_ids, t->counts, t->offsets,
                             t->dest_row, t->row_src, t->send_bytes, t->n_dropped, t->xp, w, L,
-                            s)) != MOE_OK)
+                            s, &fa, route_count_tokens(d))) != MOE_OK)
     return st;
   if (!mark(MOE_TRACE_DISPATCH)) return MOE_ERR_LAUNCH;
   if ((st = launch_ffn(p, d, t->xp, t->offsets, t->w13, t->w2, t->x, t->w13_sh, t->w2_sh, t->yp,
                        t->y_sh, w, L, s, ev ? ev + MOE_TRACE_FFN_PREP : nullptr,
-                       gather ? t->row_src : nullptr)) != MOE_OK)
+                       gather ? t->row_src : nullptr, &fa)) != MOE_OK)
     return st;
   if (d.T > 0 && (st = launch_combine(p, d, t->yp, t->dest_row, t->topk_w, t->y_sh, t->y, s)) !=
                      MOE_OK)

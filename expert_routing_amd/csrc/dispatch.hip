@@ -15,7 +15,7 @@
 //           it to each of the token's rows (skipped when the caller passes no xp);
 //   stats   (moe_layout_stats) the same ranks and kept flags, reduced to per-token
 //           target ranks instead of rows.
-#include "moe_internal.h"
+#include "ffn_sched.h"
 
 namespace moe {
 namespace {
@@ -156,6 +156,243 @@ __global__ __launch_bounds__(CH) void disp_layout(
   }
 }
 
+// ---- two-launch dispatch -------------------------------------------------------------
+// count: per chunk of 256 tokens an LDS-atomic histogram (chunk_counts[c][E]); block 0 also
+// zeroes the send matrix the placement adds into. At least one block runs (T = 0 included).
+__global__ __launch_bounds__(CH) void disp_count(const int32_t* __restrict__ ids,
+                                                 int32_t* __restrict__ chunk_counts, int T,
+                                                 int K, int E, int n_chunks,
+                                                 int64_t* __restrict__ send_bytes, int n_send) {
+  __shared__ int cnt[512];
+  const int c = blockIdx.x;
+  if (c == 0 && send_bytes)
+    for (int i = threadIdx.x; i < n_send; i += CH) send_bytes[i] = 0;
+  if (c >= n_chunks) return;
+  for (int e = threadIdx.x; e < E; e += CH) cnt[e] = 0;
+  __syncthreads();
+  const int64_t t = (int64_t)c * CH + threadIdx.x;
+  if (t < T) {
+    for (int k = 0; k < K; ++k) {
+      const int e = ids[t * K + k];
+      if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += CH) chunk_counts[(size_t)c * E + e] = cnt[e];
+}
+
+// How the placement fills the send matrix.
+enum SendMode { kSendNone = 0, kSendAtomic = 1, kSendFromCounts = 2 };
+
+// place: every block derives what it needs of the global scan from the pair counts itself
+// (the per-expert totals and the sums over earlier tokens), so no scan kernel runs between
+// the histogram and the placement: capacity and kept counts, the local experts' row offsets
+// (exclusive scan), then its chunk's ranks, dest_row / row_src and send counts as
+// disp_layout computes them, and row_src = -1 for its share of the unclaimed rows. Block 0
+// writes counts, offsets, kept and n_dropped; two other blocks (extra ones when there are
+// fewer chunks) derive the send matrix and build the expert FFN's tile table, in parallel.
+// The counts come in n_rows rows of gtok tokens (gtok divides 256: the histogram kernel's
+// 256-token chunks, or the fused router's 16-token groups). Send matrix: kSendAtomic adds
+// into a send_bytes zeroed by disp_count; kSendFromCounts (every row inside one source
+// rank) lets block 0 derive it from the counts: a row's kept pairs on expert e are those
+// ranked below cap, i.e. clamp(cap - earlier pairs on e, 0, pairs).
+__global__ __launch_bounds__(CH) void disp_place(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ chunk_counts, int n_rows,
+    int gtok, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ kept_out, int32_t* __restrict__ n_dropped,
+    int32_t* __restrict__ dest_row, int32_t* __restrict__ row_src,
+    int64_t* __restrict__ send_bytes, int send_mode, int T, int K, int E, int El, int e0,
+    int64_t cap, int pad, int64_t R_max, int64_t tpr, int N, int64_t row_bytes, int lds_span,
+    int send_block, int do_ffn, int ffn_block, FfnPrepArgs ffn) {
+  __shared__ unsigned long long masks[CH / 64][512];
+  __shared__ int base_s[512];
+  __shared__ int kept_s[512];
+  __shared__ int off_s[513];
+  __shared__ int wsum[CH / 64];
+  __shared__ int drop_s[CH / 64];
+  extern __shared__ int ncount[];   // kSendAtomic: [lds_span][N]; kSendFromCounts: [N][N]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x;
+  const int g0 = c * (CH / gtok);   // first count row of this block's tokens
+  const bool lds_send = send_mode == kSendAtomic && lds_span > 0;
+  // Row walks per expert are split over P consecutive lanes (P a power of two, P * E <= 256
+  // when E < 256), each taking a contiguous range of rows; lane sums meet by shuffles.
+  int P = 1;
+  while (P < 64 && P * 2 * E <= CH) P *= 2;
+  // (a) per expert: total over all rows, and the sum over rows before this chunk
+  int drop = 0;
+  for (int eb = 0; eb < E; eb += CH / P) {
+    const int e = eb + tid / P, p = tid % P;
+    const bool ok = e < E;
+    const int r0 = (int)((int64_t)p * n_rows / P), r1 = (int)((int64_t)(p + 1) * n_rows / P);
+    int tot = 0, bs = 0;
+    if (ok) {
+      int r = r0;
+      for (; r + 8 <= r1; r += 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = chunk_counts[(size_t)(r + u) * E + e];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          tot += v[u];
+          bs += r + u < g0 ? v[u] : 0;
+        }
+      }
+      for (; r < r1; ++r) {
+        const int v = chunk_counts[(size_t)r * E + e];
+        tot += v;
+        bs += r < g0 ? v : 0;
+      }
+    }
+    for (int off = P / 2; off > 0; off >>= 1) {
+      tot += __shfl_xor(tot, off);
+      bs += __shfl_xor(bs, off);
+    }
+    if (ok && p == 0) {
+      base_s[e] = bs;
+      const int kept = (cap < 0 || tot < cap) ? tot : (int)cap;
+      kept_s[e] = kept;
+      drop += tot - kept;
+      if (c == 0) {
+        counts[e] = tot;
+        kept_out[e] = kept;
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) drop += __shfl_xor(drop, off);
+  if (lane == 0) drop_s[wave] = drop;
+  __syncthreads();
+  // (b) exclusive scan of the local experts' rows (El <= 2 * CH: two per thread)
+  const int el0 = 2 * tid;
+  const int v0 = el0 < El ? (pad ? (int)cap : kept_s[e0 + el0]) : 0;
+  const int v1 = el0 + 1 < El ? (pad ? (int)cap : kept_s[e0 + el0 + 1]) : 0;
+  int rows_total = 0;
+  const int excl = block_inclusive_scan<CH>(v0 + v1, wsum, &rows_total) - v0 - v1;
+  if (el0 < El) off_s[el0] = excl;
+  if (el0 + 1 < El) off_s[el0 + 1] = excl + v0;
+  if (tid == 0) off_s[El] = rows_total;
+  // (c) clear the rank masks and the send counters
+  for (int i = tid; i < (CH / 64) * E; i += CH) masks[i / E][i % E] = 0ull;
+  if (lds_send)
+    for (int i = tid; i < lds_span * N; i += CH) ncount[i] = 0;
+  if (send_mode == kSendFromCounts && c == send_block)
+    for (int i = tid; i < N * N; i += CH) ncount[i] = 0;
+  __syncthreads();
+  if (c == 0) {
+    for (int i = tid; i <= El; i += CH) offsets[i] = off_s[i];
+    if (tid == 0) {
+      int dsum = 0;
+      for (int w = 0; w < CH / 64; ++w) dsum += drop_s[w];
+      *n_dropped = dsum;
+    }
+  }
+  // (d) ranks of this chunk's pairs: earlier chunks (base_s), earlier waves, earlier lanes
+  const int64_t tfirst = (int64_t)c * CH;
+  const int64_t t = tfirst + tid;
+  int ev[16];
+  for (int k = 0; k < K; ++k) {
+    int e = t < T ? ids[t * K + k] : -1;
+    if (e < 0 || e >= E) e = -1;
+    ev[k] = e;
+    if (e >= 0) atomicOr(&masks[wave][e], 1ull << lane);
+  }
+  __syncthreads();
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int64_t src_rank = (send_mode == kSendAtomic && tpr > 0) ? t / tpr : 0;
+  const int64_t src_first = (send_mode == kSendAtomic && tpr > 0) ? tfirst / tpr : 0;
+  for (int k = 0; k < K && t < T; ++k) {
+    const int e = ev[k];
+    int dr = -1;
+    if (e >= 0) {
+      int rank = base_s[e] + __popcll(masks[wave][e] & below);
+      for (int w = 0; w < wave; ++w) rank += __popcll(masks[w][e]);
+      const bool kept = cap < 0 || rank < cap;
+      if (kept) {
+        if (e >= e0 && e < e0 + El) {
+          dr = off_s[e - e0] + rank;
+          row_src[dr] = (int32_t)(t * K + k);
+        }
+        if (send_mode == kSendAtomic) {
+          const int dst = e / El;
+          if (lds_span > 0)
+            atomicAdd(&ncount[(src_rank - src_first) * N + dst], 1);
+          else
+            atomicAdd(reinterpret_cast<unsigned long long*>(&send_bytes[src_rank * N + dst]),
+                      (unsigned long long)row_bytes);
+        }
+      }
+    }
+    dest_row[t * K + k] = dr;
+  }
+  // (e) unclaimed rows: past the last local expert's rows, or (padded) past an expert's
+  // kept rows within its cap-row block; the blocks share them in a grid stride
+  const int64_t stride = (int64_t)gridDim.x * CH;
+  if (pad) {
+    for (int64_t r = tfirst + tid; r < R_max; r += stride) {
+      const int64_t el = r / cap;
+      if (r - el * cap >= kept_s[e0 + el]) row_src[r] = -1;
+    }
+  } else {
+    for (int64_t r = off_s[El] + tfirst + tid; r < R_max; r += stride) row_src[r] = -1;
+  }
+  if (lds_send) {
+    __syncthreads();
+    for (int i = tid; i < lds_span * N; i += CH) {
+      const int n = ncount[i];
+      const int64_t src = src_first + i / N;
+      if (n > 0 && src < N)
+        atomicAdd(reinterpret_cast<unsigned long long*>(&send_bytes[src * N + (i % N)]),
+                  (unsigned long long)((int64_t)n * row_bytes));
+    }
+  }
+  if (send_mode == kSendFromCounts && c == send_block) {
+    // n_ij from the counts: each expert's rows in token order, split over its P lanes; a
+    // lane starts from the pairs on e before its range (an exclusive scan of the lane sums)
+    for (int eb = 0; eb < E; eb += CH / P) {
+      const int e = eb + tid / P, p = tid % P;
+      const bool ok = e < E;
+      const int r0 = (int)((int64_t)p * n_rows / P), r1 = (int)((int64_t)(p + 1) * n_rows / P);
+      int sum = 0;
+      if (ok)
+        for (int r = r0; r < r1; ++r) sum += chunk_counts[(size_t)r * E + e];
+      int incl = sum;
+      for (int off = 1; off < P; off <<= 1) {
+        const int v = __shfl_up(incl, off, P);
+        if (p >= off) incl += v;
+      }
+      if (ok) {
+        int before = incl - sum, cur = -1, acc = 0;
+        const int dst = e / El;
+        for (int r = r0; r < r1; ++r) {
+          const int v = chunk_counts[(size_t)r * E + e];
+          int kept = v;
+          if (cap >= 0) {
+            const int64_t room = cap - before;
+            kept = room <= 0 ? 0 : (room < v ? (int)room : v);
+          }
+          before += v;
+          const int src = (int)(((int64_t)r * gtok) / tpr);
+          if (src != cur) {
+            if (acc > 0) atomicAdd(&ncount[cur * N + dst], acc);
+            cur = src;
+            acc = 0;
+          }
+          acc += kept;
+        }
+        if (acc > 0) atomicAdd(&ncount[cur * N + dst], acc);
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < N * N; i += CH) send_bytes[i] = (int64_t)ncount[i] * row_bytes;
+  }
+  // (f) the expert FFN's tile table from the offsets (block-uniform branch)
+  if (do_ffn && c == ffn_block) {
+    __syncthreads();
+    ffn_build_sched<CH>(ffn, off_s, wsum);
+  }
+}
+
 // One wave per row r < R_max: unclaimed rows get row_src = -1; pad rows zero xp.
 __global__ __launch_bounds__(256) void disp_fill(const int32_t* __restrict__ offsets,
                                                  const int32_t* __restrict__ kept,
@@ -288,39 +525,78 @@ __global__ __launch_bounds__(256) void max_u64(const unsigned long long* __restr
 
 }  // namespace
 
+// The placement re-reads chunk_counts in every block: n_chunks * E values each, so the
+// one-pass path is taken up to this product (for example 128 chunks of 256 tokens x 256
+// experts); larger problems run histogram, one-block scan and layout as three kernels.
+constexpr int64_t kPlaceMaxScan = 32768;
+
 int launch_dispatch(const moe_problem* p, const Dims& d, const void* x, const int32_t* ids,
                     int32_t* counts, int32_t* offsets, int32_t* dest_row, int32_t* row_src,
                     int64_t* send_bytes, int32_t* n_dropped, void* xp, char* ws,
-                    const WsLayout& L, hipStream_t st) {
+                    const WsLayout& L, hipStream_t st, const FfnPrepArgs* ffn,
+                    int counted_rows) {
   const int n_chunks = (int)((d.T + CH - 1) / CH);
   int32_t* chunk_counts = reinterpret_cast<int32_t*>(ws + L.chunk_counts);
   int32_t* chunk_base = reinterpret_cast<int32_t*>(ws + L.chunk_base);
   int32_t* kept = reinterpret_cast<int32_t*>(ws + L.kept);
   const int pad = p->pad_to_capacity;
-  if (n_chunks > 0)
-    hipLaunchKernelGGL(disp_hist, dim3(n_chunks), dim3(CH), 0, st, ids, chunk_counts, (int)d.T,
-                       d.K, d.E);
-  hipLaunchKernelGGL(disp_scan, dim3(1), dim3(1024), 0, st, chunk_counts, chunk_base, counts,
-                     kept, offsets, n_dropped, send_bytes, n_chunks, d.E, d.El, d.e0, d.cap, pad,
-                     d.N);
-  if (n_chunks > 0) {
-    // LDS counters for the send matrix: the source ranks one chunk spans times N.
-    int lds_span = 0;
-    if (send_bytes && d.tpr > 0) {
-      const int64_t span = (CH + d.tpr - 1) / d.tpr + 1;
-      const int64_t s = span < d.N ? span : d.N;
-      if (s * d.N <= 8192) lds_span = (int)s;
-    }
-    const size_t lds = (size_t)lds_span * d.N * sizeof(int);
-    hipLaunchKernelGGL(disp_layout, dim3(n_chunks), dim3(CH), lds, st, ids, chunk_base, offsets,
-                       dest_row, row_src, send_bytes, (int)d.T, d.K, d.E, d.El, d.e0, d.cap,
-                       d.tpr, d.N, (int64_t)d.h * d.s, lds_span);
+  // LDS counters for the send matrix: the source ranks one chunk spans times N.
+  int lds_span = 0;
+  if (send_bytes && d.tpr > 0) {
+    const int64_t span = (CH + d.tpr - 1) / d.tpr + 1;
+    const int64_t s = span < d.N ? span : d.N;
+    if (s * d.N <= 8192) lds_span = (int)s;
   }
+  const size_t lds = (size_t)lds_span * d.N * sizeof(int);
   const int row_chunks = d.h * d.s / 16;
-  if (d.R_max > 0)
-    hipLaunchKernelGGL(disp_fill, dim3((unsigned)((d.R_max + 3) / 4)), dim3(256), 0, st, offsets,
-                       kept, row_src, static_cast<uint4*>(xp), d.R_max, d.El, d.e0, d.cap, pad,
-                       row_chunks);
+  // count rows: the router's (counted_rows tokens each) or disp_count's 256-token chunks
+  int gtok = counted_rows > 0 ? counted_rows : CH;
+  int64_t n_rows = (d.T + gtok - 1) / gtok;
+  if (n_rows * d.E <= kPlaceMaxScan && n_chunks * (int64_t)d.E <= kPlaceMaxScan) {
+    // the send matrix from the counts needs every row inside one source rank
+    auto rows_in_one_rank = [&](int gt) { return d.tpr > 0 && (d.N == 1 || d.tpr % gt == 0); };
+    const bool from_counts = send_bytes && rows_in_one_rank(gtok) && d.N * d.N <= 4096;
+    if (counted_rows == 0 || (send_bytes && !from_counts)) {
+      gtok = CH;
+      n_rows = n_chunks;
+      hipLaunchKernelGGL(disp_count, dim3((unsigned)(n_chunks > 0 ? n_chunks : 1)), dim3(CH),
+                         0, st, ids, chunk_counts, (int)d.T, d.K, d.E, n_chunks, send_bytes,
+                         d.N * d.N);
+    }
+    const bool counts_mode = send_bytes && rows_in_one_rank(gtok) && d.N * d.N <= 4096;
+    const int send_mode = !send_bytes ? kSendNone : (counts_mode ? kSendFromCounts : kSendAtomic);
+    const size_t plds = send_mode == kSendFromCounts ? (size_t)d.N * d.N * sizeof(int)
+                        : (send_mode == kSendAtomic ? lds : 0);
+    // blocks: one per chunk, and at least three so the send matrix (last block) and the
+    // tile table (the one before) are derived beside block 0's outputs
+    const int grid = n_chunks > 3 ? n_chunks : 3;
+    hipLaunchKernelGGL(disp_place, dim3((unsigned)grid), dim3(CH), plds, st, ids, chunk_counts,
+                       (int)n_rows, gtok, counts, offsets, kept, n_dropped, dest_row, row_src,
+                       send_bytes, send_mode, (int)d.T, d.K, d.E, d.El, d.e0, d.cap, pad,
+                       d.R_max, d.tpr, d.N, (int64_t)d.h * d.s, lds_span, grid - 1, ffn ? 1 : 0,
+                       grid - 2, ffn ? *ffn : FfnPrepArgs{});
+    if (pad && xp && d.R_max > 0)   // zero the pad rows of xp
+      hipLaunchKernelGGL(disp_fill, dim3((unsigned)((d.R_max + 3) / 4)), dim3(256), 0, st,
+                         offsets, kept, row_src, static_cast<uint4*>(xp), d.R_max, d.El, d.e0,
+                         d.cap, pad, row_chunks);
+  } else {
+    if (n_chunks > 0)
+      hipLaunchKernelGGL(disp_hist, dim3(n_chunks), dim3(CH), 0, st, ids, chunk_counts,
+                         (int)d.T, d.K, d.E);
+    hipLaunchKernelGGL(disp_scan, dim3(1), dim3(1024), 0, st, chunk_counts, chunk_base, counts,
+                       kept, offsets, n_dropped, send_bytes, n_chunks, d.E, d.El, d.e0, d.cap,
+                       pad, d.N);
+    if (n_chunks > 0)
+      hipLaunchKernelGGL(disp_layout, dim3(n_chunks), dim3(CH), lds, st, ids, chunk_base,
+                         offsets, dest_row, row_src, send_bytes, (int)d.T, d.K, d.E, d.El, d.e0,
+                         d.cap, d.tpr, d.N, (int64_t)d.h * d.s, lds_span);
+    if (d.R_max > 0)
+      hipLaunchKernelGGL(disp_fill, dim3((unsigned)((d.R_max + 3) / 4)), dim3(256), 0, st,
+                         offsets, kept, row_src, static_cast<uint4*>(xp), d.R_max, d.El, d.e0,
+                         d.cap, pad, row_chunks);
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
+    if (ffn && launch_ffn_prep(*ffn, offsets, st) != MOE_OK) return MOE_ERR_LAUNCH;
+  }
   if (x && xp && d.T > 0)
     hipLaunchKernelGGL(disp_copy,
                        dim3((unsigned)((d.T + 3) / 4),

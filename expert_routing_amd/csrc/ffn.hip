@@ -15,135 +15,16 @@
 // (tall tiles); an XCD's last, partial round of tiles is split along K (fp32 partials,
 // summed in slice order by the last slice to arrive). Without xp the gate/up GEMM reads
 // its A rows straight from x through the row -> token map.
-#include "moe_internal.h"
+#include "ffn_sched.h"
 
 namespace moe {
 namespace {
 
-constexpr int G_MAX = 513;       // local experts (<= 512) + shared expert
-constexpr int G_PAD = 520;
-constexpr int kMaxSplit = 4;     // k-slices of a tile in an XCD's last, partial round
-constexpr int kCuPerXcdMax = 32; // MI355X: 256 CUs in 8 XCDs
-constexpr int kArriveSlots = kNumXcd * kCuPerXcdMax;   // split tiles per GEMM
-
-struct FfnGroup {
-  const void* A1;  // [rows][h], or with gidx the token rows x [T][h]
-  const int32_t* gidx;  // gathered A rows: row r is token gidx[r] / gK (< 0: zero row)
-  const void* B1;  // [2*inter][h]
-  void* C1;        // [rows][inter]  (hbuf)
-  const void* B2;  // [h][inter]
-  void* C2;        // [rows][h]
-  int rows;
-  int inter;
-  int mt[2];    // m-tiles of the gate/up [0] and down [1] GEMMs (their tile heights differ)
-  int tall[2];  // 1: the last m-tile also takes the (short) remainder: BM + tall_extra rows,
-                // split into tall_split narrower tiles per n-tile
-  int arows;  // rows addressable through A1 (rows, or T when gathering)
-  int gK;     // pairs per token (row index -> token) when gathering
-};
-
-struct FfnSched {
-  int n_groups;
-  int total1;
-  int total2;
-  int tall_split[2];
-  int cu_per_xcd;   // CUs of one XCD (one round of blocks there)
-  int split_max;    // 1: no split-K; else the most k-slices a tile may take
-  int pad2_;
-  int start1[G_PAD];
-  int start2[G_PAD];
-  FfnGroup g[G_MAX];
-};
-
-// One block of 1024 threads.
-__global__ __launch_bounds__(1024) void ffn_prep(FfnSched* __restrict__ sc,
-                                                 const int32_t* __restrict__ offsets,
-                                                 const char* xp, const char* w13, const char* w2,
-                                                 const char* x, const char* w13_sh,
-                                                 const char* w2_sh, char* hbuf, char* yp,
-                                                 char* y_sh, int El, int has_shared,
-                                                 int64_t sh_rows, int64_t sh_t0, int h, int inter,
-                                                 int sh_inter, int64_t R_max, int s, int BM1,
-                                                 int BM2, int tall_extra1, int tall_extra2,
-                                                 int tall_split1, int tall_split2, int BN1,
-                                                 int BN2, int cu_per_xcd, int split_max,
-                                                 int* __restrict__ arrive,
-                                                 const int32_t* __restrict__ row_src, int K,
-                                                 int64_t T) {
-  __shared__ int s1[1024], s2[1024];
-  const int g = threadIdx.x;
-  const int G = El + has_shared;
-  int t1 = 0, t2 = 0;
-  if (g < G) {
-    FfnGroup fg;
-    int rows, I;
-    if (g < El) {
-      const int r0 = offsets[g];
-      rows = offsets[g + 1] - r0;
-      I = inter;
-      fg.A1 = row_src ? x : xp + (size_t)r0 * h * s;
-      fg.gidx = row_src ? row_src + r0 : nullptr;
-      fg.B1 = w13 + (size_t)g * 2 * inter * h * s;
-      fg.C1 = hbuf + (size_t)r0 * inter * s;
-      fg.B2 = w2 + (size_t)g * h * inter * s;
-      fg.C2 = yp + (size_t)r0 * h * s;
-    } else {
-      rows = (int)sh_rows;
-      I = sh_inter;
-      fg.A1 = x + (size_t)sh_t0 * h * s;
-      fg.gidx = nullptr;
-      fg.B1 = w13_sh;
-      fg.C1 = hbuf + (size_t)R_max * inter * s;
-      fg.B2 = w2_sh;
-      fg.C2 = y_sh;
-    }
-    // A remainder of at most tall_extra rows rides on the expert's last full tile (it
-    // reads the same weights) instead of costing a tile of its own. Per n-tile: mt tiles,
-    // or mt - 1 full ones and tall_split tall ones.
-    int per_n[2];
-    const int BMg[2] = {BM1, BM2}, TEg[2] = {tall_extra1, tall_extra2};
-    const int TSg[2] = {tall_split1, tall_split2};
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int q = rows / BMg[k], r = rows % BMg[k];
-      const int tall = q >= 1 && r > 0 && r <= TEg[k];
-      fg.mt[k] = tall ? q : (rows + BMg[k] - 1) / BMg[k];
-      fg.tall[k] = tall;
-      per_n[k] = tall ? fg.mt[k] - 1 + TSg[k] : fg.mt[k];
-    }
-    fg.rows = rows;
-    fg.inter = I;
-    fg.arows = fg.gidx ? (int)T : rows;
-    fg.gK = K;
-    sc->g[g] = fg;
-    t1 = per_n[0] * ((I + BN1 - 1) / BN1);
-    t2 = per_n[1] * ((h + BN2 - 1) / BN2);
-  }
-  s1[g] = t1;
-  s2[g] = t2;
-  __syncthreads();
-  for (int st = 1; st < 1024; st <<= 1) {
-    const int a1 = g >= st ? s1[g - st] : 0;
-    const int a2 = g >= st ? s2[g - st] : 0;
-    __syncthreads();
-    s1[g] += a1;
-    s2[g] += a2;
-    __syncthreads();
-  }
-  if (g <= G) {
-    sc->start1[g] = g == 0 ? 0 : s1[g - 1];
-    sc->start2[g] = g == 0 ? 0 : s2[g - 1];
-  }
-  for (int i = g; i < 2 * kArriveSlots; i += 1024) arrive[i] = 0;
-  if (g == 0) {
-    sc->n_groups = G;
-    sc->tall_split[0] = tall_split1;
-    sc->tall_split[1] = tall_split2;
-    sc->cu_per_xcd = cu_per_xcd;
-    sc->split_max = split_max;
-    sc->total1 = s1[G - 1];
-    sc->total2 = s2[G - 1];
-  }
+// One block of 1024 threads: the tile table from the offsets in device memory.
+__global__ __launch_bounds__(1024) void ffn_prep(FfnPrepArgs a,
+                                                 const int32_t* __restrict__ offsets) {
+  __shared__ int wsum[16];
+  ffn_build_sched<1024>(a, offsets, wsum);
 }
 
 // Tile lookup shared by the GEMM kernels. The tile list is dealt to the XCDs in
@@ -423,14 +304,13 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
                                                uint4* __restrict__ smem, int slice,
                                                int nslice, float* __restrict__ part,
                                                size_t pstride, int* __restrict__ arrive) {
-  constexpr int NW = WM * WN, NT = 64 * NW;
+  constexpr int NW = WM * WN;
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(TM >= 1 && TN >= 1, "tile");
   static_assert(!GATED || TN % 2 == 0, "gated needs gate/up pairs");
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "DMA rows split evenly over waves");
-  constexpr int BNO = GATED ? BN / 2 : BN;          // output columns per tile
   constexpr int AI = BM / (8 * NW), BI = BN / (8 * NW);  // DMA instructions per wave per stage
   constexpr int LPS = AI + BI;
   constexpr int A_ST = BM * 8, B_ST = BN * 8;       // uint4 per stage
@@ -442,9 +322,7 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
   const int rows = fg.rows, I = fg.inter;
   const bf16_t* A = static_cast<const bf16_t*>(GATED ? fg.A1 : fg.C1);
   const bf16_t* B = static_cast<const bf16_t*>(GATED ? fg.B1 : fg.B2);
-  bf16_t* C = static_cast<bf16_t*>(GATED ? fg.C1 : fg.C2);
   const int Kd = GATED ? h : I;         // reduction length = lda = ldb
-  const int Nout = GATED ? I : h;       // output columns = ldc
   const uint32_t b_rows = GATED ? 2 * I : h;
   const uint32_t a_bytes = (uint32_t)(GATHER ? fg.arows : rows) * Kd * 2;
   const __amdgpu_buffer_rsrc_t ra_rs = make_rsrc(A, a_bytes);
@@ -879,45 +757,86 @@ size_t ffn_splitk_bytes(const Dims& d) {
   return (size_t)kNumXcd * kCuPerXcdMax * tile * 4;
 }
 
-int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_t* offsets,
-               const void* w13, const void* w2, const void* x, const void* w13_sh,
-               const void* w2_sh, void* yp, void* y_sh, char* ws, const WsLayout& L,
-               hipStream_t st, hipEvent_t const* ev, const int32_t* gather_rows) {
-  FfnSched* sc = reinterpret_cast<FfnSched*>(ws + L.sched);
-  float* part = reinterpret_cast<float*>(ws + L.splitk);
-  int* arrive = reinterpret_cast<int*>(ws + L.arrive);
-  const int has_sh = (p->n_shared && d.sh_rows > 0) ? 1 : 0;
-  const int64_t sh_t0 = (int64_t)d.rank * d.tpr;
-  Tiles k1 = Tiles::Large, k2 = Tiles::Large;
-  Tiling t1{F_BM, 0, 1}, t2{F_BM, 0, 1};
-  int BN1 = F_BN / 2, BN2 = F_BN, split_max = 1;
+int ffn_prep_args(const moe_problem* p, const Dims& d, const void* xp, const void* w13,
+                  const void* w2, const void* x, const void* w13_sh, const void* w2_sh, void* yp,
+                  void* y_sh, char* ws, const WsLayout& L, const int32_t* gather_rows,
+                  FfnPrepArgs* a) {
   int dev = 0, n_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return MOE_ERR_LAUNCH;
   const int cpx = n_cu / kNumXcd < 1 ? 1 : (n_cu / kNumXcd > kCuPerXcdMax ? kCuPerXcdMax
                                                                          : n_cu / kNumXcd);
+  Tiling t1{F_BM, 0, 1}, t2{F_BM, 0, 1};
+  int BN1 = F_BN / 2, BN2 = F_BN, split_max = 1;
+  const int has_sh = (p->n_shared && d.sh_rows > 0) ? 1 : 0;
   if (d.bf16) {
-    k1 = tile_kind(d, true);
-    k2 = tile_kind(d, false);
-    t1 = tiling(k1);
-    t2 = tiling(k2);
+    t1 = tiling(tile_kind(d, true));
+    t2 = tiling(tile_kind(d, false));
     int min_k = d.h < p->inter ? d.h : p->inter;
     if (has_sh && p->shared_inter < min_k) min_k = p->shared_inter;
     split_max = min_k / 64 < kMaxSplit ? min_k / 64 : kMaxSplit;
     BN1 = 128;   // output columns of the gated tile (256 B rows: 128 gate + 128 up)
     BN2 = 256;
   }
-  hipLaunchKernelGGL(ffn_prep, dim3(1), dim3(1024), 0, st, sc, offsets,
-                     static_cast<const char*>(xp), static_cast<const char*>(w13),
-                     static_cast<const char*>(w2), static_cast<const char*>(x),
-                     static_cast<const char*>(w13_sh), static_cast<const char*>(w2_sh),
-                     ws + L.hbuf, static_cast<char*>(yp), static_cast<char*>(y_sh), d.El, has_sh,
-                     d.sh_rows, sh_t0, d.h, p->inter, p->shared_inter, d.R_max, d.s, t1.BM,
-                     t2.BM, t1.tall_extra, t2.tall_extra, t1.tall_split, t2.tall_split, BN1, BN2,
-                     cpx, split_max, arrive, gather_rows, d.K, d.T);
-  if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
+  a->sc = reinterpret_cast<FfnSched*>(ws + L.sched);
+  a->xp = static_cast<const char*>(xp);
+  a->w13 = static_cast<const char*>(w13);
+  a->w2 = static_cast<const char*>(w2);
+  a->x = static_cast<const char*>(x);
+  a->w13_sh = static_cast<const char*>(w13_sh);
+  a->w2_sh = static_cast<const char*>(w2_sh);
+  a->hbuf = ws + L.hbuf;
+  a->yp = static_cast<char*>(yp);
+  a->y_sh = static_cast<char*>(y_sh);
+  a->arrive = reinterpret_cast<int*>(ws + L.arrive);
+  a->row_src = gather_rows;
+  a->sh_rows = d.sh_rows;
+  a->sh_t0 = (int64_t)d.rank * d.tpr;
+  a->R_max = d.R_max;
+  a->T = d.T;
+  a->El = d.El;
+  a->has_shared = has_sh;
+  a->h = d.h;
+  a->inter = p->inter;
+  a->sh_inter = p->shared_inter;
+  a->s = d.s;
+  a->K = d.K;
+  a->BM1 = t1.BM; a->BM2 = t2.BM;
+  a->tall_extra1 = t1.tall_extra; a->tall_extra2 = t2.tall_extra;
+  a->tall_split1 = t1.tall_split; a->tall_split2 = t2.tall_split;
+  a->BN1 = BN1; a->BN2 = BN2;
+  a->cu_per_xcd = cpx;
+  a->split_max = split_max;
+  return MOE_OK;
+}
+
+int launch_ffn_prep(const FfnPrepArgs& a, const int32_t* offsets, hipStream_t st) {
+  hipLaunchKernelGGL(ffn_prep, dim3(1), dim3(1024), 0, st, a, offsets);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_t* offsets,
+               const void* w13, const void* w2, const void* x, const void* w13_sh,
+               const void* w2_sh, void* yp, void* y_sh, char* ws, const WsLayout& L,
+               hipStream_t st, hipEvent_t const* ev, const int32_t* gather_rows,
+               const FfnPrepArgs* prepped) {
+  FfnPrepArgs a;
+  int rc = MOE_OK;
+  if (prepped) {
+    a = *prepped;     // the table was built by dispatch
+  } else {
+    if ((rc = ffn_prep_args(p, d, xp, w13, w2, x, w13_sh, w2_sh, yp, y_sh, ws, L, gather_rows,
+                            &a)) != MOE_OK)
+      return rc;
+    if ((rc = launch_ffn_prep(a, offsets, st)) != MOE_OK) return rc;
+  }
   if (ev && hipEventRecord(ev[0], st) != hipSuccess) return MOE_ERR_LAUNCH;
+  const FfnSched* sc = a.sc;
+  float* part = reinterpret_cast<float*>(ws + L.splitk);
+  const int has_sh = a.has_shared;
+  const int cpx = a.cu_per_xcd;
+  const int BN1 = a.BN1, BN2 = a.BN2;
   // Upper bound on m-tiles: sum_e ceil(rows_e / BM) <= R_max / BM + E_l (an expert with a
   // tall last tile has mt - 1 + tall_split <= ceil(rows_e / BM) tiles per n-tile).
   auto m_ub = [&](int BM) { return d.R_max / BM + d.El; };
@@ -925,13 +844,13 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
   const int64_t nt1 = (p->inter + BN1 - 1) / BN1;
   const int64_t nt1s = has_sh ? (p->shared_inter + BN1 - 1) / BN1 : 0;
   const int64_t nt2 = (d.h + BN2 - 1) / BN2;
-  const int64_t ub1 = m_ub(t1.BM) * nt1 + m_sh(t1.BM) * nt1s;
-  const int64_t ub2 = (m_ub(t2.BM) + m_sh(t2.BM)) * nt2;
+  const int64_t ub1 = m_ub(a.BM1) * nt1 + m_sh(a.BM1) * nt1s;
+  const int64_t ub2 = (m_ub(a.BM2) + m_sh(a.BM2)) * nt2;
   bool ok = true;
   if (d.bf16) {
-    ok = launch_bf16(k1, true, sc, d.h, ub1, cpx, part, arrive, st);
+    ok = launch_bf16(tile_kind(d, true), true, sc, d.h, ub1, cpx, part, a.arrive, st);
     if (ok && ev) ok = hipEventRecord(ev[1], st) == hipSuccess;
-    if (ok) ok = launch_bf16(k2, false, sc, d.h, ub2, cpx, part, arrive, st);
+    if (ok) ok = launch_bf16(tile_kind(d, false), false, sc, d.h, ub2, cpx, part, a.arrive, st);
   } else {
     const int64_t g1 = (ub1 + kNumXcd - 1) / kNumXcd * kNumXcd;
     const int64_t g2 = (ub2 + kNumXcd - 1) / kNumXcd * kNumXcd;

@@ -1,0 +1,179 @@
+// The expert FFN's tile table: which (group, m-tile, n-tile) each GEMM block takes. Built on
+// the device from the local experts' row offsets, either by its own one-block kernel before
+// the GEMMs or by the dispatch kernel that produces the offsets (one launch fewer). Shared by
+// ffn.hip and dispatch.hip; not part of the ABI.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int G_MAX = 513;       // local experts (<= 512) + shared expert
+constexpr int G_PAD = 520;
+constexpr int kMaxSplit = 4;     // k-slices of a tile in an XCD's last, partial round
+constexpr int kCuPerXcdMax = 32; // MI355X: 256 CUs in 8 XCDs
+constexpr int kArriveSlots = kNumXcd * kCuPerXcdMax;   // split tiles per GEMM
+
+struct FfnGroup {
+  const void* A1;  // [rows][h], or with gidx the token rows x [T][h]
+  const int32_t* gidx;  // gathered A rows: row r is token gidx[r] / gK (< 0: zero row)
+  const void* B1;  // [2*inter][h]
+  void* C1;        // [rows][inter]  (hbuf)
+  const void* B2;  // [h][inter]
+  void* C2;        // [rows][h]
+  int rows;
+  int inter;
+  int mt[2];    // m-tiles of the gate/up [0] and down [1] GEMMs (their tile heights differ)
+  int tall[2];  // 1: the last m-tile also takes the (short) remainder: BM + tall_extra rows,
+                // split into tall_split narrower tiles per n-tile
+  int arows;  // rows addressable through A1 (rows, or T when gathering)
+  int gK;     // pairs per token (row index -> token) when gathering
+};
+
+struct FfnSched {
+  int n_groups;
+  int total1;
+  int total2;
+  int tall_split[2];
+  int cu_per_xcd;   // CUs of one XCD (one round of blocks there)
+  int split_max;    // 1: no split-K; else the most k-slices a tile may take
+  int pad2_;
+  int start1[G_PAD];
+  int start2[G_PAD];
+  FfnGroup g[G_MAX];
+};
+
+// Everything the table is built from besides the offsets (filled on the host).
+struct FfnPrepArgs {
+  FfnSched* sc;
+  const char* xp;
+  const char* w13;
+  const char* w2;
+  const char* x;
+  const char* w13_sh;
+  const char* w2_sh;
+  char* hbuf;
+  char* yp;
+  char* y_sh;
+  int* arrive;              // split-K arrival counters, zeroed here
+  const int32_t* row_src;   // gathered gate/up A rows, or nullptr
+  int64_t sh_rows, sh_t0, R_max, T;
+  int El, has_shared, h, inter, sh_inter, s, K;
+  int BM1, BM2, tall_extra1, tall_extra2, tall_split1, tall_split2, BN1, BN2;
+  int cu_per_xcd, split_max;
+};
+
+// Inclusive scan of one int per thread over a block of NT threads: wave scans by shuffles,
+// then each thread adds the totals of the waves before its own (read from wsum, NT/64 ints
+// of LDS). Every thread of the block must call it; *total receives the block's sum.
+template <int NT>
+__device__ inline int block_inclusive_scan(int v, int* wsum, int* total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off);
+    if (lane >= off) v += u;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int s = wsum[w];
+    before += w < wave ? s : 0;
+    tot += s;
+  }
+  __syncthreads();   // wsum is free for the next scan
+  *total = tot;
+  return v + before;
+}
+
+// Builds a.sc from offsets[0..El] (any address space) with the calling block's NT threads;
+// every thread of the block must call it. Thread i takes groups [i*PER, (i+1)*PER): per
+// group the m-tiles of each GEMM (a short remainder of at most tall_extra rows rides on the
+// last full tile) and its tiles; the groups' starting tile indices are an exclusive scan.
+// wsum: NT/64 ints of LDS.
+template <int NT>
+__device__ inline void ffn_build_sched(const FfnPrepArgs& a, const int32_t* offsets, int* wsum) {
+  constexpr int PER = (G_MAX + 1 + NT - 1) / NT;   // covers index G (the end of the table)
+  const int tid = threadIdx.x;
+  const int G = a.El + a.has_shared;
+  int c1[PER], c2[PER];
+  int s1 = 0, s2 = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int g = tid * PER + i;
+    c1[i] = 0;
+    c2[i] = 0;
+    if (g < G) {
+      FfnGroup fg;
+      int rows, I;
+      if (g < a.El) {
+        const int r0 = offsets[g];
+        rows = offsets[g + 1] - r0;
+        I = a.inter;
+        fg.A1 = a.row_src ? a.x : a.xp + (size_t)r0 * a.h * a.s;
+        fg.gidx = a.row_src ? a.row_src + r0 : nullptr;
+        fg.B1 = a.w13 + (size_t)g * 2 * a.inter * a.h * a.s;
+        fg.C1 = a.hbuf + (size_t)r0 * a.inter * a.s;
+        fg.B2 = a.w2 + (size_t)g * a.h * a.inter * a.s;
+        fg.C2 = a.yp + (size_t)r0 * a.h * a.s;
+      } else {
+        rows = (int)a.sh_rows;
+        I = a.sh_inter;
+        fg.A1 = a.x + (size_t)a.sh_t0 * a.h * a.s;
+        fg.gidx = nullptr;
+        fg.B1 = a.w13_sh;
+        fg.C1 = a.hbuf + (size_t)a.R_max * a.inter * a.s;
+        fg.B2 = a.w2_sh;
+        fg.C2 = a.y_sh;
+      }
+      int per_n[2];
+      const int BMg[2] = {a.BM1, a.BM2}, TEg[2] = {a.tall_extra1, a.tall_extra2};
+      const int TSg[2] = {a.tall_split1, a.tall_split2};
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int q = rows / BMg[k], r = rows % BMg[k];
+        const int tall = q >= 1 && r > 0 && r <= TEg[k];
+        fg.mt[k] = tall ? q : (rows + BMg[k] - 1) / BMg[k];
+        fg.tall[k] = tall;
+        per_n[k] = tall ? fg.mt[k] - 1 + TSg[k] : fg.mt[k];
+      }
+      fg.rows = rows;
+      fg.inter = I;
+      fg.arows = fg.gidx ? (int)a.T : rows;
+      fg.gK = a.K;
+      a.sc->g[g] = fg;
+      c1[i] = per_n[0] * ((I + a.BN1 - 1) / a.BN1);
+      c2[i] = per_n[1] * ((a.h + a.BN2 - 1) / a.BN2);
+    }
+    s1 += c1[i];
+    s2 += c2[i];
+  }
+  int tot1 = 0, tot2 = 0;
+  int e1 = block_inclusive_scan<NT>(s1, wsum, &tot1) - s1;
+  int e2 = block_inclusive_scan<NT>(s2, wsum, &tot2) - s2;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int g = tid * PER + i;
+    if (g <= G) {          // start[G] = the total: the binary search's upper end
+      a.sc->start1[g] = e1;
+      a.sc->start2[g] = e2;
+    }
+    e1 += c1[i];
+    e2 += c2[i];
+  }
+  for (int i = tid; i < 2 * kArriveSlots; i += NT) a.arrive[i] = 0;
+  if (tid == 0) {
+    a.sc->n_groups = G;
+    a.sc->tall_split[0] = a.tall_split1;
+    a.sc->tall_split[1] = a.tall_split2;
+    a.sc->cu_per_xcd = a.cu_per_xcd;
+    a.sc->split_max = a.split_max;
+    a.sc->total1 = tot1;
+    a.sc->total2 = tot2;
+  }
+}
+
+}  // namespace moe

@@ -58,24 +58,43 @@ struct WsLayout {
   size_t total;
 };
 
+struct FfnPrepArgs;   // ffn_sched.h: what the expert FFN's tile table is built from
+
 int make_dims(const moe_problem* p, Dims* d);
 int route_split(const Dims& d);   // defined with the router kernels
 WsLayout ws_layout(const moe_problem* p, const Dims& d);
 
 // Stage launchers (arguments already validated; return MOE_OK or MOE_ERR_LAUNCH).
+// chunk_counts (or nullptr): the router also leaves dispatch's per-expert pair counts of
+// every route_count_tokens(d) tokens there ([rows][E]).
 int launch_route(const moe_problem* p, const Dims& d, const void* x, const float* w_router,
-                 const float* bias, int32_t* ids, float* w, float* logits, hipStream_t st);
+                 const float* bias, int32_t* ids, float* w, float* logits,
+                 int32_t* chunk_counts, hipStream_t st);
+int route_count_tokens(const Dims& d);
 int launch_select(const moe_problem* p, const Dims& d, const float* logits, const float* bias,
                   int32_t* ids, float* w, hipStream_t st);
+// `ffn`: also build the expert FFN's tile table from the offsets (nullptr: do not).
+// `counted_rows` > 0: the router already left the pair counts of every `counted_rows`
+// tokens in the workspace's chunk counts (launch_route with chunk_counts).
 int launch_dispatch(const moe_problem* p, const Dims& d, const void* x, const int32_t* ids,
                     int32_t* counts, int32_t* offsets, int32_t* dest_row, int32_t* row_src,
                     int64_t* send_bytes, int32_t* n_dropped, void* xp, char* ws,
-                    const WsLayout& L, hipStream_t st);
+                    const WsLayout& L, hipStream_t st, const FfnPrepArgs* ffn = nullptr,
+                    int counted_rows = 0);
+// Host: the tile table's parameters (tile shapes, operand pointers) for this problem.
+int ffn_prep_args(const moe_problem* p, const Dims& d, const void* xp, const void* w13,
+                  const void* w2, const void* x, const void* w13_sh, const void* w2_sh, void* yp,
+                  void* y_sh, char* ws, const WsLayout& L, const int32_t* gather_rows,
+                  FfnPrepArgs* a);
+// The one-block kernel that builds the table from offsets in device memory.
+int launch_ffn_prep(const FfnPrepArgs& a, const int32_t* offsets, hipStream_t st);
+// The two grouped GEMMs; `prepped`: the table was already built (by dispatch) from these
+// arguments, else the prep kernel runs first.
 int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_t* offsets,
                const void* w13, const void* w2, const void* x, const void* w13_sh,
                const void* w2_sh, void* yp, void* y_sh, char* ws, const WsLayout& L,
                hipStream_t st, hipEvent_t const* ev = nullptr,
-               const int32_t* gather_rows = nullptr);
+               const int32_t* gather_rows = nullptr, const FfnPrepArgs* prepped = nullptr);
 int launch_layout_stats(const moe_problem* p, const Dims& d, const int32_t* ids,
                         int64_t* tokens_to, int64_t* recv_pairs, int64_t* fanout_hist,
                         int64_t* busiest, char* ws, const WsLayout& L, hipStream_t st);

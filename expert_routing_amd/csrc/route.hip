@@ -38,11 +38,16 @@ __device__ __forceinline__ void split3(float w, bf16_t& hi, bf16_t& mid, bf16_t&
 }
 
 // One block: 64 tokens x BE experts (BE in {16, 32, 64}); 4 waves; MFMA 16x16x32.
+// zero / n_zero: ints the first block clears for the selection that follows (its chunk
+// histogram), or nullptr.
 template <int BE>
 __global__ __launch_bounds__(256) void router_gemm_bf16(const bf16_t* __restrict__ x,
                                                         const float* __restrict__ w,
                                                         float* __restrict__ logits,
-                                                        int T, int h, int E, int kslice) {
+                                                        int T, int h, int E, int kslice,
+                                                        int32_t* __restrict__ zero, int n_zero) {
+  if (zero && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    for (int i = threadIdx.x; i < n_zero; i += 256) zero[i] = 0;
   __shared__ uint4 xs[RT_BM * 8];           // [64 rows][8 chunks]
   __shared__ uint4 wsm[3][BE * 8];          // hi / mid / lo planes, [BE rows][8 chunks]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -141,7 +146,10 @@ __global__ __launch_bounds__(256) void router_gemm_bf16(const bf16_t* __restrict
 __global__ __launch_bounds__(256) void router_gemm_f32(const float* __restrict__ x,
                                                        const float* __restrict__ w,
                                                        float* __restrict__ logits,
-                                                       int T, int h, int E, int kslice) {
+                                                       int T, int h, int E, int kslice,
+                                                       int32_t* __restrict__ zero, int n_zero) {
+  if (zero && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    for (int i = threadIdx.x; i < n_zero; i += 256) zero[i] = 0;
   constexpr int BK = 16;
   __shared__ float xs[BK][64 + 4];
   __shared__ float wsm[BK][64 + 4];
@@ -192,11 +200,13 @@ __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
 // experts through a mask. When the group limit is on, every thread of the block must call
 // this (it synchronises the block); `active` says whether the segment has a token.
 // ks / gs / ga: this token's LDS rows for keys [E], group scores and flags [n_groups].
+// hist (LDS or global, may be nullptr): each winner adds 1 at its expert id (integer
+// atomics: the counts do not depend on their order).
 template <int SEG, int KPL>
 __device__ __forceinline__ void select_token(
     const float (&Lin)[KPL], bool active, const float* __restrict__ bias, int E, int K,
     int score, int renorm, int n_groups, int topk_groups, float* ks, float* gs, int* ga,
-    int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, int* hist) {
   const int lane = threadIdx.x & 63;
   const int sl = lane & (SEG - 1), base = lane & ~(SEG - 1);
   float L[KPL], key[KPL], raw[KPL];
@@ -320,6 +330,7 @@ __device__ __forceinline__ void select_token(
   if (sl < K) {
     ids_out[pos] = win_e;
     w_out[pos] = wv;
+    if (hist) atomicAdd(&hist[win_e], 1);
   }
 }
 
@@ -428,8 +439,9 @@ template <bool PAIRED>
 __global__ __launch_bounds__(64 * RS_NW) void router_small_e(
     const bf16_t* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
     int32_t* __restrict__ ids, float* __restrict__ wout, int T, int h, int E, int K,
-    int score, int renorm, int n_groups, int topk_groups) {
+    int score, int renorm, int n_groups, int topk_groups, int32_t* __restrict__ group_counts) {
   __shared__ float red[RS_NW][16][17];
+  __shared__ int hist_s[16];
   __shared__ float lg[16][17];
   __shared__ float sel_k[4 * RS_NW][16];
   __shared__ float sel_g[4 * RS_NW][16];
@@ -471,6 +483,7 @@ __global__ __launch_bounds__(64 * RS_NW) void router_small_e(
       for (int q = 1; q < RS_NW; ++q) s += red[q][tk][e];
       lg[tk][e] = s;
     }
+    if (tid < 16) hist_s[tid] = 0;
     __syncthreads();
     // selection: wave w takes tokens 4w .. 4w + 3 of the group (waves 4.. have none but
     // still pass the group limit's barriers), 16 lanes per token
@@ -479,8 +492,11 @@ __global__ __launch_bounds__(64 * RS_NW) void router_small_e(
     const float L[1] = {active ? lg[slot][n] : 0.f};
     const size_t t = (size_t)(t0 + (active ? slot : 0));
     select_token<16, 1>(L, active, bias, E, K, score, renorm, n_groups, topk_groups,
-                        sel_k[slot], sel_g[slot], sel_a[slot], ids + t * K, wout + t * K);
+                        sel_k[slot], sel_g[slot], sel_a[slot], ids + t * K, wout + t * K,
+                        group_counts ? hist_s : nullptr);
     __syncthreads();
+    // the group's per-expert pair counts: dispatch's histogram, 16 tokens per row
+    if (group_counts && tid < E) group_counts[(size_t)grp * E + tid] = hist_s[tid];
   }
 }
 
@@ -498,7 +514,10 @@ template <int TB>
 __global__ __launch_bounds__(256) void router_gemv(const bf16_t* __restrict__ x,
                                                    const float* __restrict__ w,
                                                    float* __restrict__ logits, int T, int h,
-                                                   int E, int kslice) {
+                                                   int E, int kslice,
+                                                   int32_t* __restrict__ zero, int n_zero) {
+  if (zero && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < n_zero; i += 256) zero[i] = 0;
   extern __shared__ uint4 xs_raw[];                   // [TB][kslice] bf16
   bf16_t* xs = reinterpret_cast<bf16_t*>(xs_raw);
   const int tid = threadIdx.x, kl = tid & 15;
@@ -560,51 +579,53 @@ __global__ __launch_bounds__(256) void router_gemv(const bf16_t* __restrict__ x,
   }
 }
 
-constexpr int SEL_KPL = 8;     // keys per lane: E <= 512
 constexpr int SEL_TOK = 4;     // tokens (waves) per block
 
-// One wave per token. Lane l holds experts l, l+64, ... Partial logits of nsplit slabs
-// are added in slab order, then select_token scores and selects.
+// One wave per token. Lane l holds experts l, l+64, ... (KPL keys per lane, 64 * KPL >= E).
+// Partial logits of nsplit slabs are added in slab order, then select_token scores and
+// selects. chunk_counts (or nullptr): [T / 256 chunks][E] pair counts for dispatch, zeroed
+// by the router GEMM.
+template <int KPL>
 __global__ __launch_bounds__(256) void select_topk(const float* __restrict__ logits,
                                                    const float* __restrict__ bias,
                                                    int32_t* __restrict__ ids,
                                                    float* __restrict__ wout, int T, int E,
                                                    int K, int score, int renorm, int n_groups,
-                                                   int topk_groups, int nsplit) {
-  __shared__ float keys_s[SEL_TOK][512];
-  __shared__ float gscore_s[SEL_TOK][512];
-  __shared__ int gallow_s[SEL_TOK][512];
+                                                   int topk_groups, int nsplit,
+                                                   int32_t* __restrict__ chunk_counts) {
+  __shared__ float keys_s[SEL_TOK][64 * KPL];
+  __shared__ float gscore_s[SEL_TOK][64 * KPL];
+  __shared__ int gallow_s[SEL_TOK][64 * KPL];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * SEL_TOK + wave;
   const bool active = t < T;
   // partial logits of the nsplit slabs added in slab order; every load of a chunk of 8
   // slabs is issued before the additions (lanes past E read a valid address)
-  const int kpl = (E + 63) >> 6;
   const int64_t tr = active ? t : 0;
-  float L[SEL_KPL];
+  float L[KPL];
 #pragma unroll
-  for (int j = 0; j < SEL_KPL; ++j) L[j] = 0.f;
+  for (int j = 0; j < KPL; ++j) L[j] = 0.f;
   for (int z0 = 0; z0 < nsplit; z0 += 8) {
-    float v[8][SEL_KPL];
+    float v[8][KPL];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
 #pragma unroll
-      for (int j = 0; j < SEL_KPL; ++j) {
+      for (int j = 0; j < KPL; ++j) {
         const int e = j * 64 + lane;
-        v[u][j] = (z0 + u < nsplit && j < kpl)
+        v[u][j] = z0 + u < nsplit
                       ? logits[(size_t)(z0 + u) * T * E + tr * E + (e < E ? e : E - 1)]
                       : 0.f;
       }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
 #pragma unroll
-      for (int j = 0; j < SEL_KPL; ++j)
+      for (int j = 0; j < KPL; ++j)
         if (z0 + u < nsplit) L[j] = (z0 + u == 0) ? v[u][j] : L[j] + v[u][j];
   }
-  const int64_t tt = active ? t : 0;
-  select_token<64, SEL_KPL>(L, active, bias, E, K, score, renorm, n_groups, topk_groups,
-                            keys_s[wave], gscore_s[wave], gallow_s[wave], ids + tt * K,
-                            wout + tt * K);
+  select_token<64, KPL>(L, active, bias, E, K, score, renorm, n_groups, topk_groups,
+                        keys_s[wave], gscore_s[wave], gallow_s[wave], ids + tr * K,
+                        wout + tr * K,
+                        chunk_counts ? chunk_counts + (tr / kDispatchChunk) * E : nullptr);
 }
 
 // Partial logits of the k-slices added in slice order into slab 0, one thread per
@@ -678,34 +699,49 @@ int route_split(const Dims& d) {
 }
 
 static int select_with(const moe_problem* p, const Dims& d, const float* logits, int nsplit,
-                       const float* bias, int32_t* ids, float* w, hipStream_t st) {
+                       const float* bias, int32_t* ids, float* w, int32_t* chunk_counts,
+                       hipStream_t st) {
   const unsigned grid = (unsigned)((d.T + SEL_TOK - 1) / SEL_TOK);
-  hipLaunchKernelGGL(select_topk, dim3(grid), dim3(256), 0, st, logits, bias, ids, w,
-                     (int)d.T, d.E, d.K, p->score, p->renorm, p->n_groups, p->topk_groups,
-                     nsplit);
+  const int kpl = (d.E + 63) / 64;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, logits, bias, ids, w, (int)d.T, d.E,
+                       d.K, p->score, p->renorm, p->n_groups, p->topk_groups, nsplit,
+                       chunk_counts);
+  };
+  if (kpl <= 1) go(select_topk<1>);
+  else if (kpl <= 2) go(select_topk<2>);
+  else if (kpl <= 4) go(select_topk<4>);
+  else go(select_topk<8>);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+int route_count_tokens(const Dims& d) {
+  return router_path(d) == RouterPath::Fused ? 16 : kDispatchChunk;
 }
 
 int launch_select(const moe_problem* p, const Dims& d, const float* logits, const float* bias,
                   int32_t* ids, float* w, hipStream_t st) {
-  return select_with(p, d, logits, 1, bias, ids, w, st);
+  return select_with(p, d, logits, 1, bias, ids, w, nullptr, st);
 }
 
 int launch_route(const moe_problem* p, const Dims& d, const void* x, const float* w_router,
-                 const float* bias, int32_t* ids, float* w, float* logits, hipStream_t st) {
+                 const float* bias, int32_t* ids, float* w, float* logits,
+                 int32_t* chunk_counts, hipStream_t st) {
   const bf16_t* xb = static_cast<const bf16_t*>(x);
   const RouterPath path = router_path(d);
+  // the selection's chunk histogram: the GEMM before it clears it
+  const int n_zero = (int)((d.T + kDispatchChunk - 1) / kDispatchChunk) * d.E;
   if (path == RouterPath::Fused) {
     const int64_t groups = (d.T + 15) / 16;
     const unsigned grid = (unsigned)(groups < 2048 ? groups : 2048);
     if (d.E <= 8)
       hipLaunchKernelGGL(router_small_e<true>, dim3(grid), dim3(64 * RS_NW), 0, st, xb,
                          w_router, bias, ids, w, (int)d.T, d.h, d.E, d.K, p->score, p->renorm,
-                         p->n_groups, p->topk_groups);
+                         p->n_groups, p->topk_groups, chunk_counts);
     else
       hipLaunchKernelGGL(router_small_e<false>, dim3(grid), dim3(64 * RS_NW), 0, st, xb,
                          w_router, bias, ids, w, (int)d.T, d.h, d.E, d.K, p->score, p->renorm,
-                         p->n_groups, p->topk_groups);
+                         p->n_groups, p->topk_groups, chunk_counts);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
   }
   if (path == RouterPath::Gemv) {
@@ -716,12 +752,12 @@ int launch_route(const moe_problem* p, const Dims& d, const void* x, const float
     const size_t lds = (size_t)tb * ks * 2;
     if (tb == 32)
       hipLaunchKernelGGL(router_gemv<32>, grid, dim3(256), lds, st, xb, w_router, logits,
-                         (int)d.T, d.h, d.E, ks);
+                         (int)d.T, d.h, d.E, ks, chunk_counts, n_zero);
     else
       hipLaunchKernelGGL(router_gemv<64>, grid, dim3(256), lds, st, xb, w_router, logits,
-                         (int)d.T, d.h, d.E, ks);
+                         (int)d.T, d.h, d.E, ks, chunk_counts, n_zero);
     if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
-    return select_with(p, d, logits, z, bias, ids, w, st);
+    return select_with(p, d, logits, z, bias, ids, w, chunk_counts, st);
   }
   const unsigned gt = (unsigned)((d.T + RT_BM - 1) / RT_BM);
   const int S = d.route_split;
@@ -733,14 +769,14 @@ int launch_route(const moe_problem* p, const Dims& d, const void* x, const float
     const dim3 grid(gt, (unsigned)((d.E + be - 1) / be), gz);
     if (be == 32)
       hipLaunchKernelGGL(router_gemm_bf16<32>, grid, dim3(256), 0, st, xb, w_router, logits,
-                         (int)d.T, d.h, d.E, kslice);
+                         (int)d.T, d.h, d.E, kslice, chunk_counts, n_zero);
     else
       hipLaunchKernelGGL(router_gemm_bf16<64>, grid, dim3(256), 0, st, xb, w_router, logits,
-                         (int)d.T, d.h, d.E, kslice);
+                         (int)d.T, d.h, d.E, kslice, chunk_counts, n_zero);
   } else {
     const dim3 grid(gt, (unsigned)((d.E + 63) / 64), gz);
     hipLaunchKernelGGL(router_gemm_f32, grid, dim3(256), 0, st, static_cast<const float*>(x),
-                       w_router, logits, (int)d.T, d.h, d.E, kslice);
+                       w_router, logits, (int)d.T, d.h, d.E, kslice, chunk_counts, n_zero);
   }
   if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
   if (gz >= 8 && d.T <= 1024) {
@@ -750,9 +786,9 @@ int launch_route(const moe_problem* p, const Dims& d, const void* x, const float
     const unsigned blocks = (unsigned)((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048);
     hipLaunchKernelGGL(logits_reduce, dim3(blocks), dim3(256), 0, st, logits, n, (int)gz);
     if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
-    return select_with(p, d, logits, 1, bias, ids, w, st);
+    return select_with(p, d, logits, 1, bias, ids, w, chunk_counts, st);
   }
-  return select_with(p, d, logits, (int)gz, bias, ids, w, st);
+  return select_with(p, d, logits, (int)gz, bias, ids, w, chunk_counts, st);
 }
 
 }  // namespace moe

@@ -252,8 +252,8 @@ int moe_forward(const moe_problem* p, const moe_tensors* t, void* ws, size_t ws_
 enum moe_trace_point {
   MOE_TRACE_BEGIN = 0,        /* before the router GEMM                        */
   MOE_TRACE_ROUTE = 1,        /* after router GEMM + top-K selection           */
-  MOE_TRACE_DISPATCH = 2,     /* after histogram, scan, layout, fill, row copy */
-  MOE_TRACE_FFN_PREP = 3,     /* after the FFN tile-table kernel               */
+  MOE_TRACE_DISPATCH = 2,     /* after histogram, placement (and row copy)     */
+  MOE_TRACE_FFN_PREP = 3,     /* after the FFN tile table (built by dispatch)  */
   MOE_TRACE_FFN_GATE_UP = 4,  /* after the gate/up grouped GEMM (silu * mul)   */
   MOE_TRACE_FFN_DOWN = 5,     /* after the down-projection grouped GEMM        */
   MOE_TRACE_COMBINE = 6,      /* after combine                                 */
