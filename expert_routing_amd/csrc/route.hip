@@ -193,15 +193,39 @@ __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
 }
 
 // ---- selection of one token by a segment of SEG lanes --------------------------------
+// Order-preserving code of a key (a larger float gives a larger code; +0 and -0 share one);
+// code 0 is below every real key (the code of -inf is 0x007fffff) and marks non-candidates.
+__device__ __forceinline__ uint32_t ord_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  u = (u == 0x80000000u) ? 0u : u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Sum / max over the SEG lanes of a segment (xor butterfly: every lane gets the result).
+template <int SEG>
+__device__ __forceinline__ float seg_sum(float v) {
+#pragma unroll
+  for (int off = SEG / 2; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+template <int SEG>
+__device__ __forceinline__ float seg_max(float v) {
+#pragma unroll
+  for (int off = SEG / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
 // Lane j of the segment holds experts j, j + SEG, ... (KPL keys per lane; KPL * SEG >= E).
-// Scoring, group limit, K rounds of a segment-wide (key desc, index asc) arg-max with
-// shuffles, weights, and the ids written in ascending order with weights aligned. A key of
-// -inf is an ordinary candidate (after every finite key, by index); the group limit removes
-// experts through a mask. When the group limit is on, every thread of the block must call
-// this (it synchronises the block); `active` says whether the segment has a token.
-// ks / gs / ga: this token's LDS rows for keys [E], group scores and flags [n_groups].
-// hist (LDS or global, may be nullptr): each winner adds 1 at its expert id (integer
-// atomics: the counts do not depend on their order).
+// Scoring, group limit, top-K, weights, and the ids written in ascending order with
+// weights aligned. Top-K is a radix select on the key codes: the K-th largest code is
+// built bit by bit from ballot counts, the codes above it are taken, and ties at it go to
+// the lowest expert ids, so a key of -inf is an ordinary candidate (after every finite key,
+// by index). The group limit scores each group by the sum of its two largest keys: with
+// groups that are aligned power-of-two runs of at most SEG lanes it runs on shuffles,
+// otherwise through LDS rows ks / gs / ga of this token (keys [E], group scores and flags
+// [n_groups]; then every thread of the block must call this, as it synchronises the
+// block). `active`: the segment has a token. hist (LDS or global, may be nullptr): each
+// winner adds 1 at its expert id (integer atomics: the counts do not depend on order).
 template <int SEG, int KPL>
 __device__ __forceinline__ void select_token(
     const float (&Lin)[KPL], bool active, const float* __restrict__ bias, int E, int K,
@@ -209,6 +233,8 @@ __device__ __forceinline__ void select_token(
     int32_t* __restrict__ ids_out, float* __restrict__ w_out, int* hist) {
   const int lane = threadIdx.x & 63;
   const int sl = lane & (SEG - 1), base = lane & ~(SEG - 1);
+  const uint64_t segmask = SEG == 64 ? ~0ull : (((1ull << SEG) - 1ull) << base);
+  const uint64_t below = (1ull << lane) - 1ull;     // lanes under this one
   float L[KPL], key[KPL], raw[KPL];
   uint32_t allow = 0;   // bit j: expert j*SEG + sl is a candidate
 #pragma unroll
@@ -231,106 +257,133 @@ __device__ __forceinline__ void select_token(
   }
   if (n_groups > 1 && topk_groups < n_groups) {
     const int gsz = E / n_groups;
+    const bool shuffled = (gsz & (gsz - 1)) == 0 && gsz <= SEG && n_groups <= SEG;
+    if (shuffled) {   // uniform: E and n_groups are kernel arguments
+      // top-2 of each aligned run of gsz lanes (per j), then the group's score
+      float gsc[KPL];
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-      const int e = j * SEG + sl;
-      if (e < E) ks[e] = key[j];
-    }
-    __syncthreads();
-    for (int g = sl; g < n_groups; g += SEG) {
-      float b1 = -INFINITY, b2 = -INFINITY;
-      for (int i = 0; i < gsz; ++i) {
-        const float v = ks[g * gsz + i];
-        if (v > b1) { b2 = b1; b1 = v; } else if (v > b2) { b2 = v; }
+      for (int j = 0; j < KPL; ++j) {
+        float v1 = key[j], v2 = -INFINITY;
+        for (int off = 1; off < gsz; off <<= 1) {
+          const float o1 = __shfl_xor(v1, off), o2 = __shfl_xor(v2, off);
+          const float hi = fmaxf(v1, o1), lo = fminf(v1, o1);
+          v2 = fmaxf(lo, fmaxf(v2, o2));
+          v1 = hi;
+        }
+        gsc[j] = gsz > 1 ? v1 + v2 : v1;
       }
-      gs[g] = gsz > 1 ? b1 + b2 : b1;
-    }
-    __syncthreads();
-    for (int g = sl; g < n_groups; g += SEG) {
-      const float sg = gs[g];
-      int rank = 0;
-      for (int q = 0; q < n_groups; ++q) rank += better(gs[q], q, sg, g) ? 1 : 0;
-      ga[g] = rank < topk_groups;
-    }
-    __syncthreads();
+      // segment lane q < n_groups takes group q's score, ranks it among the groups
+      const int q = sl;
+      const int qj = (q * gsz) / SEG, qlane = base + (q * gsz) % SEG;
+      float mine = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-      const int e = j * SEG + sl;
-      if (e < E && !ga[e / gsz]) allow &= ~(1u << j);
+      for (int j = 0; j < KPL; ++j) {
+        const float v = __shfl(gsc[j], qlane);
+        if (j == qj) mine = v;
+      }
+      int rank = 0;
+      for (int g = 0; g < n_groups; ++g) {
+        const float sg = __shfl(mine, base + g);
+        rank += better(sg, g, mine, q) ? 1 : 0;
+      }
+      const int gallow = (q < n_groups && rank < topk_groups) ? 1 : 0;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        const int e = j * SEG + sl;
+        const int ok = __shfl(gallow, base + (e < E ? e / gsz : 0));
+        if (e < E && !ok) allow &= ~(1u << j);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        const int e = j * SEG + sl;
+        if (e < E) ks[e] = key[j];
+      }
+      __syncthreads();
+      for (int g = sl; g < n_groups; g += SEG) {
+        float b1 = -INFINITY, b2 = -INFINITY;
+        for (int i = 0; i < gsz; ++i) {
+          const float v = ks[g * gsz + i];
+          if (v > b1) { b2 = b1; b1 = v; } else if (v > b2) { b2 = v; }
+        }
+        gs[g] = gsz > 1 ? b1 + b2 : b1;
+      }
+      __syncthreads();
+      for (int g = sl; g < n_groups; g += SEG) {
+        const float sg = gs[g];
+        int rank = 0;
+        for (int q = 0; q < n_groups; ++q) rank += better(gs[q], q, sg, g) ? 1 : 0;
+        ga[g] = rank < topk_groups;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        const int e = j * SEG + sl;
+        if (e < E && !ga[e / gsz]) allow &= ~(1u << j);
+      }
     }
   }
   if (!active) return;
 
-  // K rounds of a segment-wide arg-max over the remaining candidates; the sentinel (index
-  // INT_MAX) loses to every candidate, -inf keys included.
-  int win_e = -1;        // segment lane k < K keeps the k-th winner
-  float win_L = 0.f, win_r = 0.f;
-  for (int k = 0; k < K; ++k) {
-    float bk = -INFINITY; int bi = 0x7fffffff; float bl = 0.f, br = 0.f;
+  // radix select: thr = the largest code with at least K candidate codes >= thr
+  uint32_t code[KPL];
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-      const int e = j * SEG + sl;
-      if ((allow >> j & 1u) && better(key[j], e, bk, bi)) {
-        bk = key[j]; bi = e; bl = L[j]; br = raw[j];
-      }
-    }
+  for (int j = 0; j < KPL; ++j) code[j] = (allow >> j & 1u) ? ord_key(key[j]) : 0u;
+  uint32_t thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    int cnt = 0;
 #pragma unroll
-    for (int off = SEG / 2; off > 0; off >>= 1) {
-      const float ok = __shfl_xor(bk, off);
-      const int oi = __shfl_xor(bi, off);
-      const float ol = __shfl_xor(bl, off);
-      const float orr = __shfl_xor(br, off);
-      if (better(ok, oi, bk, bi)) { bk = ok; bi = oi; bl = ol; br = orr; }
-    }
-    if (bi < E && (bi & (SEG - 1)) == sl) allow &= ~(1u << (bi / SEG));
-    if (sl == k) { win_e = bi; win_L = bl; win_r = br; }
+    for (int j = 0; j < KPL; ++j) cnt += __popcll(__ballot(code[j] >= cand) & segmask);
+    if (cnt >= K) thr = cand;
   }
-  // Weights of the K winners (segment lanes 0..K-1).
-  float wv = 0.f;
+  int gt = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) gt += __popcll(__ballot(code[j] > thr) & segmask);
+  const int need = K - gt;   // ties at thr taken, lowest expert ids first
+  uint32_t sel = 0;
+  int eq_before = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const uint64_t eqm = __ballot(code[j] == thr) & segmask;
+    const bool take =
+        code[j] > thr || (code[j] == thr && eq_before + __popcll(eqm & below) < need);
+    if (take) sel |= 1u << j;
+    eq_before += __popcll(eqm);
+  }
+  // weights over the selected set
+  float m = -INFINITY, z = 0.f;
   if (score == MOE_SCORE_SOFTMAX) {
-    if (renorm) {
-      const float m = __shfl(win_L, base);   // first winner has the largest logit
-      const float ex = sl < K ? expf(win_L - m) : 0.f;
-      float z = ex;
 #pragma unroll
-      for (int off = SEG / 2; off > 0; off >>= 1) z += __shfl_xor(z, off);
-      wv = ex / z;
-    } else {
-      float m = -INFINITY;
+    for (int j = 0; j < KPL; ++j)
+      if (renorm ? (sel >> j & 1u) : j * SEG + sl < E) m = fmaxf(m, L[j]);
+    m = seg_max<SEG>(m);
 #pragma unroll
-      for (int j = 0; j < KPL; ++j) m = fmaxf(m, L[j]);
+    for (int j = 0; j < KPL; ++j)
+      if (renorm ? (sel >> j & 1u) : j * SEG + sl < E) z += expf(L[j] - m);
+    z = seg_sum<SEG>(z);
+  } else if (renorm) {
 #pragma unroll
-      for (int off = SEG / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-      float z = 0.f;
-#pragma unroll
-      for (int j = 0; j < KPL; ++j) {
-        const int e = j * SEG + sl;
-        if (e < E) z += expf(L[j] - m);
-      }
-#pragma unroll
-      for (int off = SEG / 2; off > 0; off >>= 1) z += __shfl_xor(z, off);
-      wv = expf(win_L - m) / z;
-    }
-  } else {
-    if (renorm) {
-      float z = sl < K ? win_r : 0.f;
-#pragma unroll
-      for (int off = SEG / 2; off > 0; off >>= 1) z += __shfl_xor(z, off);
-      wv = win_r / z;
-    } else {
-      wv = win_r;
-    }
+    for (int j = 0; j < KPL; ++j)
+      if (sel >> j & 1u) z += raw[j];
+    z = seg_sum<SEG>(z);
   }
-  // Ascending-id order: position = number of winners with a smaller id.
-  int pos = 0;
-  for (int q = 0; q < K; ++q) {
-    const int oe = __shfl(win_e, base + q);
-    pos += (oe < win_e) ? 1 : 0;
-  }
-  if (sl < K) {
-    ids_out[pos] = win_e;
-    w_out[pos] = wv;
-    if (hist) atomicAdd(&hist[win_e], 1);
+  // positions in ascending expert-id order: selected experts of lower j, then lower lanes
+  int sel_before = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const uint64_t sm = __ballot(sel >> j & 1u) & segmask;
+    if (sel >> j & 1u) {
+      const int pos = sel_before + __popcll(sm & below);
+      const int e = j * SEG + sl;
+      float wv;
+      if (score == MOE_SCORE_SOFTMAX) wv = expf(L[j] - m) / z;
+      else wv = renorm ? raw[j] / z : raw[j];
+      ids_out[pos] = e;
+      w_out[pos] = wv;
+      if (hist) atomicAdd(&hist[e], 1);
+    }
+    sel_before += __popcll(sm);
   }
 }
 

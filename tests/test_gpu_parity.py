@@ -192,9 +192,12 @@ def test_select_from_given_logits_is_exact_on_ties():
     1.0 or one common tiny value in both precisions) plus biases in steps of 1/4."""
     import expert_routing_amd as moe
     g = torch.Generator().manual_seed(0)
+    # groups of 32, 4 and 32 lanes select on shuffles; groups of 24 and 3 (not a power of
+    # two) through LDS
     for (E, K, G, M, score) in [(64, 6, 1, 1, "softmax"), (256, 8, 8, 4, "sigmoid"),
                                 (16, 4, 4, 2, "sigmoid"), (8, 2, 1, 1, "softmax"),
-                                (512, 16, 16, 5, "softmax"), (256, 8, 8, 4, "softmax")]:
+                                (512, 16, 16, 5, "softmax"), (256, 8, 8, 4, "softmax"),
+                                (96, 6, 4, 2, "sigmoid"), (12, 3, 4, 2, "softmax")]:
         T = 200
         if score == "softmax":
             L = torch.randint(-3, 4, (T, E), generator=g).float()
@@ -245,7 +248,8 @@ def test_select_minus_inf_keys_are_candidates():
 @pytest.mark.parametrize("E,K,G,M,score", [(8, 2, 1, 1, "softmax"), (8, 8, 1, 1, "softmax"),
                                            (16, 4, 4, 2, "sigmoid"), (12, 3, 3, 2, "softmax"),
                                            (6, 3, 3, 2, "sigmoid"), (64, 6, 1, 1, "softmax"),
-                                           (256, 8, 8, 4, "sigmoid")])
+                                           (256, 8, 8, 4, "sigmoid"), (12, 3, 4, 2, "softmax"),
+                                           (96, 6, 4, 2, "sigmoid")])
 @pytest.mark.parametrize("T", [40, 300])
 def test_route_exact_on_forced_ties(E, K, G, M, score, T):
     """moe_route from x with exact logits (x in {-1, 0, 1}, a sparse W_r in {-1/4, 0, 1/4},
