@@ -68,6 +68,13 @@ class Tensors(ctypes.Structure):
         "y_sh", "y")]
 
 
+class ReplicaMap(ctypes.Structure):
+    """Mirror of `moe_replica_map` (device pointers)."""
+    _fields_ = [("P", ctypes.c_int32), ("rep_start", ctypes.c_void_p),
+                ("rep_list", ctypes.c_void_p), ("phys_expert", ctypes.c_void_p),
+                ("phys_replica", ctypes.c_void_p)]
+
+
 _P = ctypes.POINTER(Problem)
 _V = ctypes.c_void_p
 _SZ = ctypes.c_size_t
@@ -95,13 +102,24 @@ _forward = _sig("moe_forward", [_P, ctypes.POINTER(Tensors), _V, _SZ, _V])
 _forward_traced = _sig("moe_forward_traced",
                        [_P, ctypes.POINTER(Tensors), _V, _SZ, _V, ctypes.POINTER(_V)])
 _forward_noalloc = _sig("moe_forward_noalloc", [_P, ctypes.POINTER(Tensors), _V])
+_RM = ctypes.POINTER(ReplicaMap)
+_replica_plan = _sig("moe_replica_plan", [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          _V, _V, _V, _V, _V, _V])
+_replicated_sizes = _sig("moe_replicated_sizes", [_P, ctypes.c_int32,
+                                                  ctypes.POINTER(ctypes.c_int64),
+                                                  ctypes.POINTER(ctypes.c_size_t)])
+_dispatch_replicated = _sig("moe_dispatch_replicated",
+                            [_P, _RM, _V, _V, _V, _V, _V, _V, _V, _V, _V, _SZ, _V])
+_forward_replicated = _sig("moe_forward_replicated", [_P, _RM, ctypes.POINTER(Tensors), _V, _SZ,
+                                                      _V])
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 TRACE_POINTS = ["begin", "route", "dispatch", "ffn_prep", "ffn_gate_up", "ffn_down", "combine"]
 
 EXPORTED = ["moe_check_problem", "moe_capacity", "moe_max_rows", "moe_workspace_bytes",
             "moe_status_string", "moe_route", "moe_select", "moe_dispatch", "moe_expert_ffn",
             "moe_combine", "moe_layout_stats", "moe_forward", "moe_forward_traced",
-            "moe_forward_noalloc"]
+            "moe_forward_noalloc", "moe_replica_plan", "moe_replicated_sizes",
+            "moe_dispatch_replicated", "moe_forward_replicated"]
 
 
 class MoeError(RuntimeError):
@@ -216,6 +234,71 @@ def moe_forward_traced(p, t: dict, ws, events, stream=None):
     wp, wn = _ws(ws)
     _ok(_forward_traced(ctypes.byref(p), ctypes.byref(ts), wp, wn, _stream(stream), arr),
         "moe_forward_traced")
+
+
+def replica_plan(E, R, n_ep, load):
+    """moe_replica_plan on host arrays: returns counts, rep_start, rep_list, phys_expert,
+    phys_replica as int32 numpy arrays."""
+    import numpy as np
+    P = E + R
+    ld = np.ascontiguousarray(np.asarray(load, dtype=np.int64))
+    out = {"counts": np.zeros(E, np.int32), "rep_start": np.zeros(E + 1, np.int32),
+           "rep_list": np.zeros(P, np.int32), "phys_expert": np.zeros(P, np.int32),
+           "phys_replica": np.zeros(P, np.int32)}
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    _ok(_replica_plan(int(E), int(R), int(n_ep), ptr(ld), ptr(out["counts"]),
+                      ptr(out["rep_start"]), ptr(out["rep_list"]), ptr(out["phys_expert"]),
+                      ptr(out["phys_replica"])), "moe_replica_plan")
+    return out
+
+
+def replicated_sizes(p: Problem, P: int):
+    rows, nb = ctypes.c_int64(), ctypes.c_size_t()
+    _ok(_replicated_sizes(ctypes.byref(p), int(P), ctypes.byref(rows), ctypes.byref(nb)),
+        "moe_replicated_sizes")
+    return rows.value, nb.value
+
+
+class DeviceReplicaMap:
+    """A replica map copied to the device (keeps the tensors alive)."""
+
+    def __init__(self, plan: dict, device="cuda"):
+        self.t = {k: torch.as_tensor(plan[k]).to(device=device, dtype=torch.int32)
+                  for k in ("rep_start", "rep_list", "phys_expert", "phys_replica")}
+        self.P = int(len(plan["rep_list"]))
+        self.c = ReplicaMap(self.P, *(self.t[k].data_ptr() for k in
+                                      ("rep_start", "rep_list", "phys_expert", "phys_replica")))
+
+
+def moe_dispatch_replicated(p, rmap: DeviceReplicaMap, topk_ids, counts, phys_counts, offsets,
+                            dest_row, row_src, send_bytes, n_dropped, ws, stream=None):
+    wp, wn = _ws(ws)
+    _ok(_dispatch_replicated(ctypes.byref(p), ctypes.byref(rmap.c), _ptr(topk_ids), _ptr(counts),
+                             _ptr(phys_counts), _ptr(offsets), _ptr(dest_row), _ptr(row_src),
+                             _ptr(send_bytes), _ptr(n_dropped), wp, wn, _stream(stream)),
+        "moe_dispatch_replicated")
+
+
+def moe_forward_replicated(p, rmap: DeviceReplicaMap, t: dict, ws, stream=None):
+    ts = Tensors(**{k: _ptr(t.get(k)) for k, _ in Tensors._fields_})
+    wp, wn = _ws(ws)
+    _ok(_forward_replicated(ctypes.byref(p), ctypes.byref(rmap.c), ctypes.byref(ts), wp, wn,
+                            _stream(stream)), "moe_forward_replicated")
+
+
+def alloc_buffers_replicated(p: Problem, P: int, device="cuda", send=True) -> dict:
+    """alloc_buffers for a layer over P physical experts."""
+    rows, nb = replicated_sizes(p, P)
+    b = alloc_buffers(p, device, send)
+    Pl = P // p.n_ep
+    R = max(rows, 1)
+    b["offsets"] = torch.empty((Pl + 1,), dtype=torch.int32, device=device)
+    b["phys_counts"] = torch.empty((P,), dtype=torch.int32, device=device)
+    b["row_src"] = torch.empty((R,), dtype=torch.int32, device=device)
+    b["xp"] = torch.empty((R, p.h), dtype=p.torch_dtype, device=device)
+    b["yp"] = torch.empty((R, p.h), dtype=p.torch_dtype, device=device)
+    b["ws"] = torch.empty((max(nb, 256),), dtype=torch.uint8, device=device)
+    return b
 
 
 class HipEvents:

@@ -96,6 +96,31 @@ int make_dims(const moe_problem* p, Dims* d) {
   return MOE_OK;
 }
 
+int make_dims_replicated(const moe_problem* p, int P, Dims* d) {
+  int st = make_dims(p, d);
+  if (st != MOE_OK) return st;
+  if (P < p->E || P % p->n_ep != 0) return MOE_ERR_INVALID;
+  if (p->pad_to_capacity) return MOE_ERR_UNSUPPORTED;
+  const int Pl = P / p->n_ep;
+  if (Pl > 512 || P > 8192) return MOE_ERR_UNSUPPORTED;
+  // the placement derives the scan in every block: the one-pass bound on count rows
+  const int64_t rows256 = (p->T + kDispatchChunk - 1) / kDispatchChunk;
+  const int rt = route_count_tokens(*d);
+  const int64_t rows_rt = (p->T + rt - 1) / rt;
+  if ((rows256 > rows_rt ? rows256 : rows_rt) * p->E > 32768) return MOE_ERR_UNSUPPORTED;
+  int64_t cap = -1;
+  if (!cap_exact(p->capacity_factor, p->T, p->K, P, &cap)) return MOE_ERR_UNSUPPORTED;
+  d->El = Pl;
+  d->e0 = p->ep_rank * Pl;
+  d->cap = cap;
+  const int64_t per_tok = p->K < Pl ? p->K : Pl;
+  int64_t rmax = p->T * per_tok;
+  if (cap >= 0 && (int64_t)Pl * cap < rmax) rmax = (int64_t)Pl * cap;
+  if (rmax >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  d->R_max = rmax;
+  return MOE_OK;
+}
+
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 WsLayout ws_layout(const moe_problem* p, const Dims& d) {
@@ -299,11 +324,14 @@ int moe_layout_stats(const moe_problem* p, const int32_t* topk_ids, int64_t* tok
 }
 
 static int forward_impl(const moe_problem* p, const moe_tensors* t, void* ws, size_t ws_bytes,
-                        void* stream, void* const* events) {
+                        void* stream, void* const* events,
+                        const moe_replica_map* map = nullptr) {
   if (!t) return MOE_ERR_INVALID;
   Dims d;
-  int st = make_dims(p, &d);
+  int st = map ? make_dims_replicated(p, map->P, &d) : make_dims(p, &d);
   if (st != MOE_OK) return st;
+  if (map && (!map->rep_start || !map->rep_list || !map->phys_expert || !map->phys_replica))
+    return MOE_ERR_INVALID;
   if (p->inter <= 0 || (d.T > 0 && !t->x)) return MOE_ERR_INVALID;
   // No xp: the row copy is skipped and the gate/up GEMM reads x through row_src.
   const bool gather = t->xp == nullptr;
@@ -339,9 +367,15 @@ static int forward_impl(const moe_problem* p, const moe_tensors* t, void* ws, si
   if ((st = ffn_prep_args(p, d, t->xp, t->w13, t->w2, t->x, t->w13_sh, t->w2_sh, t->yp,
                           t->y_sh, w, L, gather ? t->row_src : nullptr, &fa)) != MOE_OK)
     return st;
+  ReplicaArgs rm{};
+  if (map) {
+    rm = ReplicaArgs{map->rep_start, map->rep_list, map->phys_expert, map->phys_replica,
+                     map->P, nullptr};
+    fa.phys_expert = map->phys_expert;   // each physical expert runs its logical weights
+  }
   if ((st = launch_dispatch(p, d, gather ? nullptr : t->x, t->topk_ids, t->counts, t->offsets,
                             t->dest_row, t->row_src, t->send_bytes, t->n_dropped, t->xp, w, L,
-                            s, &fa, route_count_tokens(d))) != MOE_OK)
+                            s, &fa, route_count_tokens(d), map ? &rm : nullptr)) != MOE_OK)
     return st;
   if (!mark(MOE_TRACE_DISPATCH)) return MOE_ERR_LAUNCH;
   if ((st = launch_ffn(p, d, t->xp, t->offsets, t->w13, t->w2, t->x, t->w13_sh, t->w2_sh, t->yp,
@@ -364,6 +398,95 @@ int moe_forward_traced(const moe_problem* p, const moe_tensors* t, void* ws, siz
                        void* stream, void* const* events) {
   if (!events) return MOE_ERR_INVALID;
   return forward_impl(p, t, ws, ws_bytes, stream, events);
+}
+
+int moe_replicated_sizes(const moe_problem* p, int32_t P, int64_t* max_rows, size_t* ws_bytes) {
+  Dims d;
+  int st = make_dims_replicated(p, P, &d);
+  if (st != MOE_OK) return st;
+  if (!max_rows || !ws_bytes) return MOE_ERR_INVALID;
+  *max_rows = d.R_max;
+  *ws_bytes = ws_layout(p, d).total;
+  return MOE_OK;
+}
+
+int moe_dispatch_replicated(const moe_problem* p, const moe_replica_map* map,
+                            const int32_t* topk_ids, int32_t* counts, int32_t* phys_counts,
+                            int32_t* offsets, int32_t* dest_row, int32_t* row_src,
+                            int64_t* send_bytes, int32_t* n_dropped, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (!map) return MOE_ERR_INVALID;
+  Dims d;
+  int st = make_dims_replicated(p, map->P, &d);
+  if (st != MOE_OK) return st;
+  if (!map->rep_start || !map->rep_list || !map->phys_expert || !map->phys_replica)
+    return MOE_ERR_INVALID;
+  if ((st = v_dispatch(p, d, nullptr, topk_ids, counts, offsets, dest_row, row_src, send_bytes,
+                       n_dropped, nullptr, ws, ws_bytes)) != MOE_OK)
+    return st;
+  const WsLayout L = ws_layout(p, d);
+  const ReplicaArgs rm{map->rep_start, map->rep_list, map->phys_expert, map->phys_replica,
+                       map->P, phys_counts};
+  return launch_dispatch(p, d, nullptr, topk_ids, counts, offsets, dest_row, row_src,
+                         send_bytes, n_dropped, nullptr, (char*)ws, L, (hipStream_t)stream,
+                         nullptr, 0, &rm);
+}
+
+int moe_forward_replicated(const moe_problem* p, const moe_replica_map* map,
+                           const moe_tensors* t, void* ws, size_t ws_bytes, void* stream) {
+  if (!map) return MOE_ERR_INVALID;
+  return forward_impl(p, t, ws, ws_bytes, stream, nullptr, map);
+}
+
+int moe_replica_plan(int32_t E, int32_t R, int32_t n_ep, const int64_t* load, int32_t* counts,
+                     int32_t* rep_start, int32_t* rep_list, int32_t* phys_expert,
+                     int32_t* phys_replica) {
+  if (E < 1 || E > 512 || R < 0 || n_ep < 1 || (E + R) % n_ep != 0 || E + R > 8192)
+    return MOE_ERR_INVALID;
+  if (!load || !counts || !rep_start || !rep_list || !phys_expert || !phys_replica)
+    return MOE_ERR_INVALID;
+  for (int e = 0; e < E; ++e)
+    if (load[e] < 0 || load[e] > INT32_MAX) return MOE_ERR_INVALID;
+  const int P = E + R, per = P / n_ep;
+  // replica counts: each redundant slot to the largest load per replica, ties to lower id
+  for (int e = 0; e < E; ++e) counts[e] = 1;
+  for (int slot = 0; slot < R; ++slot) {
+    int best = 0;
+    for (int e = 1; e < E; ++e)
+      if (load[e] * counts[best] > load[best] * counts[e]) best = e;
+    ++counts[best];
+  }
+  rep_start[0] = 0;
+  for (int e = 0; e < E; ++e) rep_start[e + 1] = rep_start[e] + counts[e];
+  // packing: replicas by their pair share (descending; ties lower id, then lower replica)
+  // onto the least loaded rank with a free slot (ties to the lower rank)
+  struct Rep { int64_t w; int e, q; };
+  Rep* reps = new Rep[P];
+  int n = 0;
+  for (int e = 0; e < E; ++e)
+    for (int q = 0; q < counts[e]; ++q)
+      reps[n++] = Rep{load[e] / counts[e] + (q < load[e] % counts[e] ? 1 : 0), e, q};
+  std::sort(reps, reps + n, [](const Rep& a, const Rep& b) {
+    if (a.w != b.w) return a.w > b.w;
+    if (a.e != b.e) return a.e < b.e;
+    return a.q < b.q;
+  });
+  int64_t* rank_load = new int64_t[n_ep]();
+  int* fill = new int[n_ep]();
+  for (int i = 0; i < n; ++i) {
+    int best = -1;
+    for (int j = 0; j < n_ep; ++j)
+      if (fill[j] < per && (best < 0 || rank_load[j] < rank_load[best])) best = j;
+    const int pid = best * per + fill[best]++;
+    rank_load[best] += reps[i].w;
+    phys_expert[pid] = reps[i].e;
+    phys_replica[pid] = reps[i].q;
+    rep_list[rep_start[reps[i].e] + reps[i].q] = pid;
+  }
+  delete[] reps;
+  delete[] rank_load;
+  delete[] fill;
+  return MOE_OK;
 }
 
 }  // extern "C"

@@ -196,6 +196,13 @@ enum SendMode { kSendNone = 0, kSendAtomic = 1, kSendFromCounts = 2 };
 // into a send_bytes zeroed by disp_count; kSendFromCounts (every row inside one source
 // rank) lets block 0 derive it from the counts: a row's kept pairs on expert e are those
 // ranked below cap, i.e. clamp(cap - earlier pairs on e, 0, pairs).
+//
+// With a replica map (rm.rep_start != nullptr) the buffers are laid out over physical
+// experts: a pair ranked rho among its logical expert e's pairs goes to replica rho mod r_e
+// (physical id rep_list[rep_start[e] + rho mod r_e]) where it ranks rho / r_e; a physical
+// expert's pair count follows from e's total (floor(n_e / r_e) plus one for the first
+// n_e mod r_e replicas), and the capacity applies per physical expert. El / e0 are then the
+// local physical experts.
 __global__ __launch_bounds__(CH) void disp_place(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ chunk_counts, int n_rows,
     int gtok, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -203,10 +210,11 @@ __global__ __launch_bounds__(CH) void disp_place(
     int32_t* __restrict__ dest_row, int32_t* __restrict__ row_src,
     int64_t* __restrict__ send_bytes, int send_mode, int T, int K, int E, int El, int e0,
     int64_t cap, int pad, int64_t R_max, int64_t tpr, int N, int64_t row_bytes, int lds_span,
-    int send_block, int do_ffn, int ffn_block, FfnPrepArgs ffn) {
+    int send_block, int do_ffn, int ffn_block, FfnPrepArgs ffn, ReplicaArgs rm) {
   __shared__ unsigned long long masks[CH / 64][512];
   __shared__ int base_s[512];
-  __shared__ int kept_s[512];
+  __shared__ int tot_s[512];
+  __shared__ int kept_s[512];   // local (physical) experts
   __shared__ int off_s[513];
   __shared__ int wsum[CH / 64];
   __shared__ int drop_s[CH / 64];
@@ -215,16 +223,17 @@ __global__ __launch_bounds__(CH) void disp_place(
   const int c = blockIdx.x;
   const int g0 = c * (CH / gtok);   // first count row of this block's tokens
   const bool lds_send = send_mode == kSendAtomic && lds_span > 0;
-  // Row walks per expert are split over P consecutive lanes (P a power of two, P * E <= 256
-  // when E < 256), each taking a contiguous range of rows; lane sums meet by shuffles.
-  int P = 1;
-  while (P < 64 && P * 2 * E <= CH) P *= 2;
-  // (a) per expert: total over all rows, and the sum over rows before this chunk
-  int drop = 0;
-  for (int eb = 0; eb < E; eb += CH / P) {
-    const int e = eb + tid / P, p = tid % P;
+  // Row walks per expert are split over LPE consecutive lanes (a power of two, LPE * E <=
+  // 256 when E < 256), each taking a contiguous range of rows; lane sums meet by shuffles.
+  int LPE = 1;
+  while (LPE < 64 && LPE * 2 * E <= CH) LPE *= 2;
+  const int P = rm.rep_start ? rm.P : E;   // physical experts
+  // (a) per logical expert: total over all rows, and the sum over rows before this chunk
+  for (int eb = 0; eb < E; eb += CH / LPE) {
+    const int e = eb + tid / LPE, p = tid % LPE;
     const bool ok = e < E;
-    const int r0 = (int)((int64_t)p * n_rows / P), r1 = (int)((int64_t)(p + 1) * n_rows / P);
+    const int r0 = (int)((int64_t)p * n_rows / LPE);
+    const int r1 = (int)((int64_t)(p + 1) * n_rows / LPE);
     int tot = 0, bs = 0;
     if (ok) {
       int r = r0;
@@ -244,19 +253,37 @@ __global__ __launch_bounds__(CH) void disp_place(
         bs += r < g0 ? v : 0;
       }
     }
-    for (int off = P / 2; off > 0; off >>= 1) {
+    for (int off = LPE / 2; off > 0; off >>= 1) {
       tot += __shfl_xor(tot, off);
       bs += __shfl_xor(bs, off);
     }
     if (ok && p == 0) {
       base_s[e] = bs;
-      const int kept = (cap < 0 || tot < cap) ? tot : (int)cap;
-      kept_s[e] = kept;
-      drop += tot - kept;
+      tot_s[e] = tot;
       if (c == 0) {
         counts[e] = tot;
-        kept_out[e] = kept;
+        kept_out[e] = (cap < 0 || tot < cap) ? tot : (int)cap;
       }
+    }
+  }
+  __syncthreads();
+  // (a') pairs per physical expert (= per logical one without a map), kept ones, dropped
+  auto phys_pairs = [&](int p) {
+    if (!rm.rep_start) return tot_s[p];
+    const int e = rm.phys_expert[p], q = rm.phys_replica[p];
+    const int r = rm.rep_start[e + 1] - rm.rep_start[e];
+    return tot_s[e] / r + (q < tot_s[e] % r ? 1 : 0);
+  };
+  for (int el = tid; el < El; el += CH) {
+    const int n = phys_pairs(e0 + el);
+    kept_s[el] = (cap < 0 || n < cap) ? n : (int)cap;
+  }
+  int drop = 0;
+  if (c == 0) {
+    for (int p = tid; p < P; p += CH) {
+      const int n = phys_pairs(p);
+      drop += n - ((cap < 0 || n < cap) ? n : (int)cap);
+      if (rm.phys_counts) rm.phys_counts[p] = n;
     }
   }
 #pragma unroll
@@ -265,8 +292,8 @@ __global__ __launch_bounds__(CH) void disp_place(
   __syncthreads();
   // (b) exclusive scan of the local experts' rows (El <= 2 * CH: two per thread)
   const int el0 = 2 * tid;
-  const int v0 = el0 < El ? (pad ? (int)cap : kept_s[e0 + el0]) : 0;
-  const int v1 = el0 + 1 < El ? (pad ? (int)cap : kept_s[e0 + el0 + 1]) : 0;
+  const int v0 = el0 < El ? (pad ? (int)cap : kept_s[el0]) : 0;
+  const int v1 = el0 + 1 < El ? (pad ? (int)cap : kept_s[el0 + 1]) : 0;
   int rows_total = 0;
   const int excl = block_inclusive_scan<CH>(v0 + v1, wsum, &rows_total) - v0 - v1;
   if (el0 < El) off_s[el0] = excl;
@@ -307,14 +334,20 @@ __global__ __launch_bounds__(CH) void disp_place(
     if (e >= 0) {
       int rank = base_s[e] + __popcll(masks[wave][e] & below);
       for (int w = 0; w < wave; ++w) rank += __popcll(masks[w][e]);
+      int pe = e;   // physical expert of the pair and its rank there
+      if (rm.rep_start) {
+        const int r = rm.rep_start[e + 1] - rm.rep_start[e];
+        pe = rm.rep_list[rm.rep_start[e] + rank % r];
+        rank = rank / r;
+      }
       const bool kept = cap < 0 || rank < cap;
       if (kept) {
-        if (e >= e0 && e < e0 + El) {
-          dr = off_s[e - e0] + rank;
+        if (pe >= e0 && pe < e0 + El) {
+          dr = off_s[pe - e0] + rank;
           row_src[dr] = (int32_t)(t * K + k);
         }
         if (send_mode == kSendAtomic) {
-          const int dst = e / El;
+          const int dst = pe / El;
           if (lds_span > 0)
             atomicAdd(&ncount[(src_rank - src_first) * N + dst], 1);
           else
@@ -331,7 +364,7 @@ __global__ __launch_bounds__(CH) void disp_place(
   if (pad) {
     for (int64_t r = tfirst + tid; r < R_max; r += stride) {
       const int64_t el = r / cap;
-      if (r - el * cap >= kept_s[e0 + el]) row_src[r] = -1;
+      if (r - el * cap >= kept_s[el]) row_src[r] = -1;
     }
   } else {
     for (int64_t r = off_s[El] + tfirst + tid; r < R_max; r += stride) row_src[r] = -1;
@@ -349,16 +382,17 @@ __global__ __launch_bounds__(CH) void disp_place(
   if (send_mode == kSendFromCounts && c == send_block) {
     // n_ij from the counts: each expert's rows in token order, split over its P lanes; a
     // lane starts from the pairs on e before its range (an exclusive scan of the lane sums)
-    for (int eb = 0; eb < E; eb += CH / P) {
-      const int e = eb + tid / P, p = tid % P;
+    for (int eb = 0; eb < E; eb += CH / LPE) {
+      const int e = eb + tid / LPE, p = tid % LPE;
       const bool ok = e < E;
-      const int r0 = (int)((int64_t)p * n_rows / P), r1 = (int)((int64_t)(p + 1) * n_rows / P);
+      const int r0 = (int)((int64_t)p * n_rows / LPE);
+      const int r1 = (int)((int64_t)(p + 1) * n_rows / LPE);
       int sum = 0;
       if (ok)
         for (int r = r0; r < r1; ++r) sum += chunk_counts[(size_t)r * E + e];
       int incl = sum;
-      for (int off = 1; off < P; off <<= 1) {
-        const int v = __shfl_up(incl, off, P);
+      for (int off = 1; off < LPE; off <<= 1) {
+        const int v = __shfl_up(incl, off, LPE);
         if (p >= off) incl += v;
       }
       if (ok) {
@@ -534,7 +568,8 @@ int launch_dispatch(const moe_problem* p, const Dims& d, const void* x, const in
                     int32_t* counts, int32_t* offsets, int32_t* dest_row, int32_t* row_src,
                     int64_t* send_bytes, int32_t* n_dropped, void* xp, char* ws,
                     const WsLayout& L, hipStream_t st, const FfnPrepArgs* ffn,
-                    int counted_rows) {
+                    int counted_rows, const ReplicaArgs* rm) {
+  const ReplicaArgs rmap = rm ? *rm : ReplicaArgs{};
   const int n_chunks = (int)((d.T + CH - 1) / CH);
   int32_t* chunk_counts = reinterpret_cast<int32_t*>(ws + L.chunk_counts);
   int32_t* chunk_base = reinterpret_cast<int32_t*>(ws + L.chunk_base);
@@ -555,7 +590,9 @@ int launch_dispatch(const moe_problem* p, const Dims& d, const void* x, const in
   if (n_rows * d.E <= kPlaceMaxScan && n_chunks * (int64_t)d.E <= kPlaceMaxScan) {
     // the send matrix from the counts needs every row inside one source rank
     auto rows_in_one_rank = [&](int gt) { return d.tpr > 0 && (d.N == 1 || d.tpr % gt == 0); };
-    const bool from_counts = send_bytes && rows_in_one_rank(gtok) && d.N * d.N <= 4096;
+    // (with replicas a row's pairs spread over replicas on several ranks: atomics instead)
+    const bool from_counts = send_bytes && !rmap.rep_start && rows_in_one_rank(gtok) &&
+                             d.N * d.N <= 4096;
     if (counted_rows == 0 || (send_bytes && !from_counts)) {
       gtok = CH;
       n_rows = n_chunks;
@@ -563,7 +600,8 @@ int launch_dispatch(const moe_problem* p, const Dims& d, const void* x, const in
                          0, st, ids, chunk_counts, (int)d.T, d.K, d.E, n_chunks, send_bytes,
                          d.N * d.N);
     }
-    const bool counts_mode = send_bytes && rows_in_one_rank(gtok) && d.N * d.N <= 4096;
+    const bool counts_mode = send_bytes && !rmap.rep_start && rows_in_one_rank(gtok) &&
+                             d.N * d.N <= 4096;
     const int send_mode = !send_bytes ? kSendNone : (counts_mode ? kSendFromCounts : kSendAtomic);
     const size_t plds = send_mode == kSendFromCounts ? (size_t)d.N * d.N * sizeof(int)
                         : (send_mode == kSendAtomic ? lds : 0);
@@ -574,12 +612,13 @@ int launch_dispatch(const moe_problem* p, const Dims& d, const void* x, const in
                        (int)n_rows, gtok, counts, offsets, kept, n_dropped, dest_row, row_src,
                        send_bytes, send_mode, (int)d.T, d.K, d.E, d.El, d.e0, d.cap, pad,
                        d.R_max, d.tpr, d.N, (int64_t)d.h * d.s, lds_span, grid - 1, ffn ? 1 : 0,
-                       grid - 2, ffn ? *ffn : FfnPrepArgs{});
+                       grid - 2, ffn ? *ffn : FfnPrepArgs{}, rmap);
     if (pad && xp && d.R_max > 0)   // zero the pad rows of xp
       hipLaunchKernelGGL(disp_fill, dim3((unsigned)((d.R_max + 3) / 4)), dim3(256), 0, st,
                          offsets, kept, row_src, static_cast<uint4*>(xp), d.R_max, d.El, d.e0,
                          d.cap, pad, row_chunks);
   } else {
+    if (rmap.rep_start) return MOE_ERR_UNSUPPORTED;   // the map needs the one-pass placement
     if (n_chunks > 0)
       hipLaunchKernelGGL(disp_hist, dim3(n_chunks), dim3(CH), 0, st, ids, chunk_counts,
                          (int)d.T, d.K, d.E);

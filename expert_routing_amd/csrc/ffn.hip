@@ -791,6 +791,8 @@ int ffn_prep_args(const moe_problem* p, const Dims& d, const void* xp, const voi
   a->y_sh = static_cast<char*>(y_sh);
   a->arrive = reinterpret_cast<int*>(ws + L.arrive);
   a->row_src = gather_rows;
+  a->phys_expert = nullptr;
+  a->p0 = d.e0;
   a->sh_rows = d.sh_rows;
   a->sh_t0 = (int64_t)d.rank * d.tpr;
   a->R_max = d.R_max;

@@ -57,6 +57,10 @@ struct FfnPrepArgs {
   char* y_sh;
   int* arrive;              // split-K arrival counters, zeroed here
   const int32_t* row_src;   // gathered gate/up A rows, or nullptr
+  const int32_t* phys_expert;  // replica map: group g runs with the weights of logical
+                               // expert phys_expert[p0 + g] (w13 / w2 hold every logical
+                               // expert); nullptr: group g uses weight block g
+  int p0;
   int64_t sh_rows, sh_t0, R_max, T;
   int El, has_shared, h, inter, sh_inter, s, K;
   int BM1, BM2, tall_extra1, tall_extra2, tall_split1, tall_split2, BN1, BN2;
@@ -115,9 +119,10 @@ __device__ inline void ffn_build_sched(const FfnPrepArgs& a, const int32_t* offs
         I = a.inter;
         fg.A1 = a.row_src ? a.x : a.xp + (size_t)r0 * a.h * a.s;
         fg.gidx = a.row_src ? a.row_src + r0 : nullptr;
-        fg.B1 = a.w13 + (size_t)g * 2 * a.inter * a.h * a.s;
+        const int wg = a.phys_expert ? a.phys_expert[a.p0 + g] : g;   // weight block
+        fg.B1 = a.w13 + (size_t)wg * 2 * a.inter * a.h * a.s;
         fg.C1 = a.hbuf + (size_t)r0 * a.inter * a.s;
-        fg.B2 = a.w2 + (size_t)g * a.h * a.inter * a.s;
+        fg.B2 = a.w2 + (size_t)wg * a.h * a.inter * a.s;
         fg.C2 = a.yp + (size_t)r0 * a.h * a.s;
       } else {
         rows = (int)a.sh_rows;

@@ -60,7 +60,21 @@ struct WsLayout {
 
 struct FfnPrepArgs;   // ffn_sched.h: what the expert FFN's tile table is built from
 
+// The replica map as the placement reads it (rep_start == nullptr: physical = logical).
+struct ReplicaArgs {
+  const int32_t* rep_start;    // [E + 1]
+  const int32_t* rep_list;     // [P]
+  const int32_t* phys_expert;  // [P]
+  const int32_t* phys_replica; // [P]
+  int P;                       // physical experts
+  int32_t* phys_counts;        // [P] out: pairs per physical expert before capacity, or nullptr
+};
+
+
 int make_dims(const moe_problem* p, Dims* d);
+// Dims over P physical experts (a replica map): El / e0 count this rank's physical experts,
+// cap is per physical expert, R_max the rows of its buffer.
+int make_dims_replicated(const moe_problem* p, int P, Dims* d);
 int route_split(const Dims& d);   // defined with the router kernels
 WsLayout ws_layout(const moe_problem* p, const Dims& d);
 
@@ -76,11 +90,12 @@ int launch_select(const moe_problem* p, const Dims& d, const float* logits, cons
 // `ffn`: also build the expert FFN's tile table from the offsets (nullptr: do not).
 // `counted_rows` > 0: the router already left the pair counts of every `counted_rows`
 // tokens in the workspace's chunk counts (launch_route with chunk_counts).
+// `rm`: a replica map (Dims then counts physical experts: make_dims_replicated).
 int launch_dispatch(const moe_problem* p, const Dims& d, const void* x, const int32_t* ids,
                     int32_t* counts, int32_t* offsets, int32_t* dest_row, int32_t* row_src,
                     int64_t* send_bytes, int32_t* n_dropped, void* xp, char* ws,
                     const WsLayout& L, hipStream_t st, const FfnPrepArgs* ffn = nullptr,
-                    int counted_rows = 0);
+                    int counted_rows = 0, const ReplicaArgs* rm = nullptr);
 // Host: the tile table's parameters (tile shapes, operand pointers) for this problem.
 int ffn_prep_args(const moe_problem* p, const Dims& d, const void* xp, const void* w13,
                   const void* w2, const void* x, const void* w13_sh, const void* w2_sh, void* yp,

@@ -262,6 +262,62 @@ enum moe_trace_point {
 int moe_forward_traced(const moe_problem* p, const moe_tensors* t, void* ws, size_t ws_bytes,
                        void* stream, void* const* events);
 
+/* ---- redundant experts ---------------------------------------------------------------
+ * A logical -> physical replica map: P = E + R physical experts (replicas), P a multiple of
+ * n_ep, rank j holding physical ids [j*P/n_ep, (j+1)*P/n_ep) ("总览" glossary: logical
+ * expert, physical expert / replica, redundant expert: 256 logical + 32 redundant = 288
+ * physical; "Expert-Parallelism", 设计空间与取舍, route 3: replicate hot experts). The pairs
+ * of logical expert e are dealt to its r_e replicas round robin in token order: the pair
+ * ranked rho among e's pairs goes to replica rho mod r_e, where it ranks rho / r_e. With a
+ * capacity factor the capacity is per physical expert, ceil(cf * T * K / P). No padding.
+ *   P             physical experts
+ *   rep_start     [E+1] device: replicas of e are rep_list[rep_start[e] .. rep_start[e+1])
+ *   rep_list      [P] device: physical id of replica q of e, in replica order
+ *   phys_expert   [P] device: the logical expert a physical id holds
+ *   phys_replica  [P] device: its replica index q                                       */
+typedef struct moe_replica_map {
+  int32_t P;
+  const int32_t* rep_start;
+  const int32_t* rep_list;
+  const int32_t* phys_expert;
+  const int32_t* phys_replica;
+} moe_replica_map;
+
+/* Host only (all pointers host memory): the map for per-expert loads load[E] (for example
+ * a routing's pair counts) with R redundant replicas over n_ep ranks. Replica counts: one
+ * each, then every redundant slot to the expert with the largest load per replica (ties to
+ * the lower id). Packing: replicas by the pairs they will receive (descending; ties: lower
+ * expert id, then lower replica index) onto the rank with the least load so far among ranks
+ * with a free slot (ties to the lower rank); a rank's slots fill in placement order. Writes
+ * counts[E] (r_e), rep_start[E+1], rep_list[P], phys_expert[P], phys_replica[P].
+ * MOE_ERR_INVALID for E outside 1..512, R < 0, (E+R) % n_ep != 0, E + R > 8192, loads
+ * outside 0..2^31-1 or NULL pointers.                                                  */
+int moe_replica_plan(int32_t E, int32_t R, int32_t n_ep, const int64_t* load, int32_t* counts,
+                     int32_t* rep_start, int32_t* rep_list, int32_t* phys_expert,
+                     int32_t* phys_replica);
+
+/* Rows of this rank's buffer and workspace bytes for the problem over P physical experts.
+ * MOE_ERR_INVALID when P < E or P % n_ep != 0; MOE_ERR_UNSUPPORTED with padding, more than
+ * 512 physical experts per rank, or more than 32768 (pair-count rows x E).            */
+int moe_replicated_sizes(const moe_problem* p, int32_t P, int64_t* max_rows, size_t* ws_bytes);
+
+/* moe_dispatch (layout only: no x / xp) over the map. counts [E]: pairs per logical expert;
+ * phys_counts [P] (or NULL): pairs per physical expert before capacity; offsets [P/n_ep+1]:
+ * first row of each local physical expert; rows ordered by (physical expert, token);
+ * dest_row / row_src / send_bytes / n_dropped as moe_dispatch with the destination rank of a
+ * pair the one holding its replica; workspace of moe_replicated_sizes.               */
+int moe_dispatch_replicated(const moe_problem* p, const moe_replica_map* map,
+                            const int32_t* topk_ids, int32_t* counts, int32_t* phys_counts,
+                            int32_t* offsets, int32_t* dest_row, int32_t* row_src,
+                            int64_t* send_bytes, int32_t* n_dropped, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* moe_forward over the map: w13 [E][2*inter][h] and w2 [E][h][inter] hold every LOGICAL
+ * expert and each local physical expert runs with its logical expert's weights (no copy);
+ * offsets has P/n_ep + 1 entries; row buffers and workspace from moe_replicated_sizes.  */
+int moe_forward_replicated(const moe_problem* p, const moe_replica_map* map,
+                           const moe_tensors* t, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- allocation-free forward ------------------------------------------------------
  * For callers that cannot allocate device memory or pass a workspace (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): moe_forward with its

@@ -23,3 +23,4 @@ from .combine import combine  # noqa: F401
 from .forward import forward  # noqa: F401
 from . import volumes  # noqa: F401
 from . import layout  # noqa: F401
+from . import replicas  # noqa: F401
