@@ -24,3 +24,4 @@ from .forward import forward  # noqa: F401
 from . import volumes  # noqa: F401
 from . import layout  # noqa: F401
 from . import replicas  # noqa: F401
+from . import fp8  # noqa: F401
