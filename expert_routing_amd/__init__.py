@@ -24,8 +24,9 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 SCORE = {"softmax": 0, "sigmoid": 1}
-DTYPE = {"f32": 0, "bf16": 1}
-_TORCH_DTYPE = {0: torch.float32, 1: torch.bfloat16}
+DTYPE = {"f32": 0, "bf16": 1, "mxfp8": 2}
+# activations of each act_dtype (MX-FP8 problems keep bf16 activations)
+_TORCH_DTYPE = {0: torch.float32, 1: torch.bfloat16, 2: torch.bfloat16}
 
 
 class Problem(ctypes.Structure):
@@ -65,7 +66,7 @@ class Tensors(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "x", "w_router", "bias", "w13", "w2", "w13_sh", "w2_sh", "topk_ids", "topk_w",
         "counts", "offsets", "dest_row", "row_src", "send_bytes", "n_dropped", "xp", "yp",
-        "y_sh", "y")]
+        "y_sh", "y", "w13_scale", "w2_scale", "w13_sh_scale", "w2_sh_scale")]
 
 
 class ReplicaMap(ctypes.Structure):
@@ -102,6 +103,8 @@ _forward = _sig("moe_forward", [_P, ctypes.POINTER(Tensors), _V, _SZ, _V])
 _forward_traced = _sig("moe_forward_traced",
                        [_P, ctypes.POINTER(Tensors), _V, _SZ, _V, ctypes.POINTER(_V)])
 _forward_noalloc = _sig("moe_forward_noalloc", [_P, ctypes.POINTER(Tensors), _V])
+_quantize_mx = _sig("moe_quantize_mx", [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _V, _V,
+                                        _V, _V])
 _RM = ctypes.POINTER(ReplicaMap)
 _replica_plan = _sig("moe_replica_plan", [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           _V, _V, _V, _V, _V, _V])
@@ -119,7 +122,7 @@ EXPORTED = ["moe_check_problem", "moe_capacity", "moe_max_rows", "moe_workspace_
             "moe_status_string", "moe_route", "moe_select", "moe_dispatch", "moe_expert_ffn",
             "moe_combine", "moe_layout_stats", "moe_forward", "moe_forward_traced",
             "moe_forward_noalloc", "moe_replica_plan", "moe_replicated_sizes",
-            "moe_dispatch_replicated", "moe_forward_replicated"]
+            "moe_dispatch_replicated", "moe_forward_replicated", "moe_quantize_mx"]
 
 
 class MoeError(RuntimeError):
@@ -212,6 +215,29 @@ def moe_layout_stats(p, topk_ids, tokens_to, recv_pairs, fanout_hist, busiest, w
     _ok(_layout_stats(ctypes.byref(p), _ptr(topk_ids), _ptr(tokens_to), _ptr(recv_pairs),
                       _ptr(fanout_hist), _ptr(busiest), wp, wn, _stream(stream)),
         "moe_layout_stats")
+
+
+def moe_quantize_mx(src, codes, scales, stream=None):
+    """MX-FP8 codes [rows][cols] and scale bytes [rows][cols/32] (uint8 tensors) of a 2-D
+    fp32 or bf16 tensor."""
+    rows, cols = src.shape
+    sd = {torch.float32: DTYPE["f32"], torch.bfloat16: DTYPE["bf16"]}.get(src.dtype)
+    if sd is None or not src.is_contiguous():
+        raise MoeError(-1, "moe_quantize_mx: src must be a contiguous fp32 or bf16 tensor")
+    for t, shape in ((codes, (rows, cols)), (scales, (rows, cols // 32))):
+        if t.dtype != torch.uint8 or tuple(t.shape) != shape or not t.is_contiguous():
+            raise MoeError(-1, f"moe_quantize_mx: expected contiguous uint8 {shape}")
+    _ok(_quantize_mx(rows, cols, sd, _ptr(src), _ptr(codes), _ptr(scales), _stream(stream)),
+        "moe_quantize_mx")
+
+
+def quantize_mx(src, stream=None):
+    """(codes, scales) of src, allocated here."""
+    rows, cols = src.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=src.device)
+    scales = torch.empty((rows, max(cols // 32, 0)), dtype=torch.uint8, device=src.device)
+    moe_quantize_mx(src, codes, scales, stream)
+    return codes, scales
 
 
 def moe_forward(p, t: dict, ws, stream=None):

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmoe.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["abi.hip", "route.hip", "dispatch.hip", "ffn.hip", "combine.hip"]
+SOURCES = ["abi.hip", "route.hip", "dispatch.hip", "ffn.hip", "combine.hip", "quant.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
          # packed fp32 VALU ops stay off (see the design notes)

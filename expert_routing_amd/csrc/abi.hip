@@ -48,7 +48,9 @@ int make_dims(const moe_problem* p, Dims* d) {
   if (p->n_groups < 1 || p->E % p->n_groups != 0) return MOE_ERR_INVALID;
   if (p->topk_groups < 1 || p->topk_groups > p->n_groups) return MOE_ERR_INVALID;
   if ((int64_t)p->topk_groups * (p->E / p->n_groups) < p->K) return MOE_ERR_INVALID;
-  if (p->act_dtype != MOE_DTYPE_F32 && p->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID;
+  if (p->act_dtype != MOE_DTYPE_F32 && p->act_dtype != MOE_DTYPE_BF16 &&
+      p->act_dtype != MOE_DTYPE_MXFP8)
+    return MOE_ERR_INVALID;
   if (p->n_shared != 0 && p->n_shared != 1) return MOE_ERR_INVALID;
   if (p->inter < 0 || p->shared_inter < 0) return MOE_ERR_INVALID;
   if (p->n_shared == 1 && (p->shared_inter <= 0 || p->T % p->n_ep != 0)) return MOE_ERR_INVALID;
@@ -56,7 +58,10 @@ int make_dims(const moe_problem* p, Dims* d) {
   int64_t cap = -1;
   if (!cap_exact(p->capacity_factor, p->T, p->K, p->E, &cap)) return MOE_ERR_UNSUPPORTED;
   if (p->pad_to_capacity && cap < 0) return MOE_ERR_INVALID;
-  const bool bf16 = p->act_dtype == MOE_DTYPE_BF16;
+  const bool mx = p->act_dtype == MOE_DTYPE_MXFP8;
+  const bool bf16 = p->act_dtype == MOE_DTYPE_BF16 || mx;
+  if (mx && (p->h % 128 != 0 || p->inter % 128 != 0 || p->shared_inter % 128 != 0))
+    return MOE_ERR_UNSUPPORTED;   // 128-value k-steps: four scale blocks per row and step
   if (bf16) {
     if (p->h % 64 != 0 || p->inter % 64 != 0 || p->shared_inter % 64 != 0)
       return MOE_ERR_UNSUPPORTED;
@@ -92,6 +97,7 @@ int make_dims(const moe_problem* p, Dims* d) {
   d->sh_rows = p->n_shared ? d->tpr : 0;
   d->s = bf16 ? 2 : 4;
   d->bf16 = bf16;
+  d->mx = mx;
   d->route_split = route_split(*d);
   return MOE_OK;
 }
@@ -136,7 +142,15 @@ WsLayout ws_layout(const moe_problem* p, const Dims& d) {
   L.kept = off;         off = align256(off + (size_t)d.E * 4);
   L.sched = off;        off = align256(off + ffn_sched_bytes(d));
   const int imax = p->inter > p->shared_inter ? p->inter : p->shared_inter;
-  L.hbuf = off;         off = align256(off + (size_t)(d.R_max + d.sh_rows) * imax * d.s);
+  if (d.mx) {
+    L.hbuf = off;       off = align256(off + (size_t)(d.R_max + d.sh_rows) * imax);
+    L.hbuf_s = off;     off = align256(off + (size_t)(d.R_max + d.sh_rows) * (imax / 32));
+    L.xq = off;         off = align256(off + (size_t)d.T * d.h);
+    L.xs = off;         off = align256(off + (size_t)d.T * (d.h / 32));
+  } else {
+    L.hbuf = off;       off = align256(off + (size_t)(d.R_max + d.sh_rows) * imax * d.s);
+    L.hbuf_s = L.xq = L.xs = 0;
+  }
   L.splitk = off;       off = align256(off + ffn_splitk_bytes(d));
   L.arrive = off;       off = align256(off + ffn_arrive_bytes(d));
   L.stats_recv = align256((size_t)(d.E + d.El + 2) * 4);
@@ -292,6 +306,7 @@ int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* offsets,
   Dims d;
   int st = make_dims(p, &d);
   if (st != MOE_OK) return st;
+  if (d.mx) return MOE_ERR_UNSUPPORTED;   // the weight scales travel in moe_tensors
   if ((st = v_ffn(p, d, xp, offsets, w13, w2, x, w13_sh, w2_sh, yp, y_sh, ws, ws_bytes)) != MOE_OK)
     return st;
   WsLayout L = ws_layout(p, d);
@@ -348,6 +363,13 @@ static int forward_impl(const moe_problem* p, const moe_tensors* t, void* ws, si
                   t->y_sh, ws, ws_bytes, gather)) != MOE_OK ||
       (st = v_combine(p, d, t->yp, t->dest_row, t->topk_w, t->y_sh, t->y)) != MOE_OK)
     return st;
+  if (d.mx) {
+    if (!t->w13_scale || !t->w2_scale) return MOE_ERR_INVALID;
+    if (p->n_shared && d.sh_rows > 0 && (!t->w13_sh_scale || !t->w2_sh_scale))
+      return MOE_ERR_INVALID;
+  } else if (t->w13_scale || t->w2_scale || t->w13_sh_scale || t->w2_sh_scale) {
+    return MOE_ERR_INVALID;
+  }
   const hipStream_t s = (hipStream_t)stream;
   hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(events);
   auto mark = [&](int i) {
@@ -363,10 +385,22 @@ static int forward_impl(const moe_problem* p, const moe_tensors* t, void* ws, si
     return st;
   if (!mark(MOE_TRACE_ROUTE)) return MOE_ERR_LAUNCH;
   // dispatch also builds the expert FFN's tile table from the offsets it produces
+  // MX-FP8: the gate/up GEMM always reads the token rows of x's E4M3 copy through row_src
+  const bool gather_a = gather || d.mx;
   FfnPrepArgs fa;
   if ((st = ffn_prep_args(p, d, t->xp, t->w13, t->w2, t->x, t->w13_sh, t->w2_sh, t->yp,
-                          t->y_sh, w, L, gather ? t->row_src : nullptr, &fa)) != MOE_OK)
+                          t->y_sh, w, L, gather_a ? t->row_src : nullptr, &fa)) != MOE_OK)
     return st;
+  if (d.mx) {
+    fa.w13_s = reinterpret_cast<const char*>(t->w13_scale);
+    fa.w2_s = reinterpret_cast<const char*>(t->w2_scale);
+    fa.w13_sh_s = reinterpret_cast<const char*>(t->w13_sh_scale);
+    fa.w2_sh_s = reinterpret_cast<const char*>(t->w2_sh_scale);
+    // x quantised once per token (before dispatch: the rows a rank would send)
+    if (d.T > 0 && (st = launch_mx_quant(t->x, true, d.T, d.h, (uint8_t*)(w + L.xq),
+                                         (uint8_t*)(w + L.xs), s)) != MOE_OK)
+      return st;
+  }
   ReplicaArgs rm{};
   if (map) {
     rm = ReplicaArgs{map->rep_start, map->rep_list, map->phys_expert, map->phys_replica,
@@ -380,7 +414,7 @@ static int forward_impl(const moe_problem* p, const moe_tensors* t, void* ws, si
   if (!mark(MOE_TRACE_DISPATCH)) return MOE_ERR_LAUNCH;
   if ((st = launch_ffn(p, d, t->xp, t->offsets, t->w13, t->w2, t->x, t->w13_sh, t->w2_sh, t->yp,
                        t->y_sh, w, L, s, ev ? ev + MOE_TRACE_FFN_PREP : nullptr,
-                       gather ? t->row_src : nullptr, &fa)) != MOE_OK)
+                       gather_a ? t->row_src : nullptr, &fa)) != MOE_OK)
     return st;
   if (d.T > 0 && (st = launch_combine(p, d, t->yp, t->dest_row, t->topk_w, t->y_sh, t->y, s)) !=
                      MOE_OK)
@@ -398,6 +432,16 @@ int moe_forward_traced(const moe_problem* p, const moe_tensors* t, void* ws, siz
                        void* stream, void* const* events) {
   if (!events) return MOE_ERR_INVALID;
   return forward_impl(p, t, ws, ws_bytes, stream, events);
+}
+
+int moe_quantize_mx(int64_t rows, int32_t cols, int32_t src_dtype, const void* src,
+                    uint8_t* codes, uint8_t* scales, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 32 != 0) return MOE_ERR_INVALID;
+  if (src_dtype != MOE_DTYPE_F32 && src_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID;
+  if (rows > 0 && (!src || !codes || !scales)) return MOE_ERR_INVALID;
+  if (rows * (int64_t)cols / 32 >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+  return launch_mx_quant(src, src_dtype == MOE_DTYPE_BF16, rows, cols, codes, scales,
+                         (hipStream_t)stream);
 }
 
 int moe_replicated_sizes(const moe_problem* p, int32_t P, int64_t* max_rows, size_t* ws_bytes) {

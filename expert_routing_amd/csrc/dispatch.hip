@@ -564,6 +564,12 @@ __global__ __launch_bounds__(256) void max_u64(const unsigned long long* __restr
 // experts); larger problems run histogram, one-block scan and layout as three kernels.
 constexpr int64_t kPlaceMaxScan = 32768;
 
+// Bytes one pair puts on the wire: its activation row, or with MX-FP8 expert weights the
+// row's E4M3 codes and scale bytes (x is quantised before dispatch).
+static int64_t send_row_bytes(const Dims& d) {
+  return d.mx ? (int64_t)d.h + d.h / 32 : (int64_t)d.h * d.s;
+}
+
 int launch_dispatch(const moe_problem* p, const Dims& d, const void* x, const int32_t* ids,
                     int32_t* counts, int32_t* offsets, int32_t* dest_row, int32_t* row_src,
                     int64_t* send_bytes, int32_t* n_dropped, void* xp, char* ws,
@@ -611,7 +617,7 @@ int launch_dispatch(const moe_problem* p, const Dims& d, const void* x, const in
     hipLaunchKernelGGL(disp_place, dim3((unsigned)grid), dim3(CH), plds, st, ids, chunk_counts,
                        (int)n_rows, gtok, counts, offsets, kept, n_dropped, dest_row, row_src,
                        send_bytes, send_mode, (int)d.T, d.K, d.E, d.El, d.e0, d.cap, pad,
-                       d.R_max, d.tpr, d.N, (int64_t)d.h * d.s, lds_span, grid - 1, ffn ? 1 : 0,
+                       d.R_max, d.tpr, d.N, send_row_bytes(d), lds_span, grid - 1, ffn ? 1 : 0,
                        grid - 2, ffn ? *ffn : FfnPrepArgs{}, rmap);
     if (pad && xp && d.R_max > 0)   // zero the pad rows of xp
       hipLaunchKernelGGL(disp_fill, dim3((unsigned)((d.R_max + 3) / 4)), dim3(256), 0, st,
@@ -628,7 +634,7 @@ int launch_dispatch(const moe_problem* p, const Dims& d, const void* x, const in
     if (n_chunks > 0)
       hipLaunchKernelGGL(disp_layout, dim3(n_chunks), dim3(CH), lds, st, ids, chunk_base,
                          offsets, dest_row, row_src, send_bytes, (int)d.T, d.K, d.E, d.El, d.e0,
-                         d.cap, d.tpr, d.N, (int64_t)d.h * d.s, lds_span);
+                         d.cap, d.tpr, d.N, send_row_bytes(d), lds_span);
     if (d.R_max > 0)
       hipLaunchKernelGGL(disp_fill, dim3((unsigned)((d.R_max + 3) / 4)), dim3(256), 0, st,
                          offsets, kept, row_src, static_cast<uint4*>(xp), d.R_max, d.El, d.e0,

@@ -16,6 +16,7 @@
 // summed in slice order by the last slice to arrive). Without xp the gate/up GEMM reads
 // its A rows straight from x through the row -> token map.
 #include "ffn_sched.h"
+#include "mxfp8.h"
 
 namespace moe {
 namespace {
@@ -611,6 +612,379 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_down_bf16(const FfnSched* __
 }
 
 // fp32 grouped GEMM: 64 x 64 tiles (gated: 32 gate + 32 up columns), 4x4 per thread.
+// ---- MX-FP8 grouped GEMM --------------------------------------------------------------
+// Same tiles, DMA layout and pipeline as the bf16 body. A k-step is still 128 bytes of each
+// operand row, now 128 E4M3 values, and takes two scaled MFMAs 32x32x64 per fragment pair.
+// In a lane of that MFMA's operand, bytes 0-15 hold k 16h..16h+15 of the first 32-value
+// scale block and bytes 16-31 k 32+16h..32+16h+15 of the second (h = lane / 32): exactly the
+// two 16-byte chunks the bf16 body reads in its phases 2c and 2c+1, so the swizzled LDS rows
+// carry over unchanged and MFMA c takes chunks 4c+h and 4c+2+h. Each stage also holds the
+// scale dword (the 4 blocks of the k-step) of every A and B row, fetched by 4-byte DMA;
+// the lanes of half h shift it right by 8h, and op_sel picks byte 0 for MFMA 0 and byte 2
+// for MFMA 1, which is block 2c+h: the hardware takes a row's first block scale from lane
+// r and its second from lane r+32.
+typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
+
+template <int BM, int BN, int NW>
+struct Fp8Shape {
+  static constexpr int BMS = (BM + 63) / 64 * 64;   // A scale dwords per stage
+  static constexpr int ZA = BMS / 64, ZB = BN / 64; // 64-row scale DMA instructions
+  static constexpr int SPW = (ZA + ZB + NW - 1) / NW;   // ... per wave (some repeat one)
+  static constexpr int S_ST = BMS + BN;              // scale dwords per stage
+};
+
+template <int BM>
+constexpr int fp8_stages() { return BM >= 256 ? 2 : 3; }
+
+// Epilogue of the gated MX-FP8 tile: H = silu(gate) * up in fp32, then per token row and
+// 32 output columns (one lane pair holds them: lane r and r+32, 16 values each) the block
+// exponent from the largest magnitude, E4M3 codes staged in LDS and stored as 16-byte row
+// chunks, and the scale byte stored by the first lane of the pair.
+template <int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void store_tile_mx(const floatx16 (&acc)[BM / WM / 32][BN / WN / 32],
+                                              const FfnGroup& fg, int m0, int n0,
+                                              uint4* __restrict__ smem) {
+  constexpr int NT = 64 * WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int BNO = BN / 2;
+  constexpr int PITCH = BNO + 16;
+  const int rows = fg.rows, Nout = fg.inter, KSo = fg.inter / 32;
+  uint8_t* C = static_cast<uint8_t*>(fg.C1);
+  uint8_t* Cs = fg.C1s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  char* stage = reinterpret_cast<char*>(smem);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int row = wm * WTM + i * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < TN / 2; ++j) {
+      float v[16];
+      uint32_t am = 0;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        v[q] = silu_fast(acc[i][j][q]) * acc[i][j + TN / 2][q];
+        am = max(am, mag_bits(v[q]));
+      }
+      am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+      const int x = mx_exponent(am);
+      const int cblk = wn * (WTN / 2) + j * 32;          // the block's first column
+      const int cbase = cblk + 4 * (lane >> 5);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<uint32_t*>(stage + row * PITCH + cbase + 8 * q4) =
+            mx_pack4(v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3], x);
+      const int gr = m0 + row, gb = (n0 + cblk) / 32;
+      if (lane < 32 && gr < rows && gb < KSo) Cs[(size_t)gr * KSo + gb] = (uint8_t)(x + 127);
+    }
+  }
+  __syncthreads();
+  constexpr int RCH = BNO / 16;
+  for (int id = tid; id < BM * RCH; id += NT) {
+    const int r = id / RCH, cc = id % RCH;
+    const int gr = m0 + r, gc = n0 + cc * 16;
+    if (gr < rows && gc < Nout)
+      *reinterpret_cast<uint4*>(C + (size_t)gr * Nout + gc) =
+          *reinterpret_cast<const uint4*>(stage + r * PITCH + cc * 16);
+  }
+}
+
+template <int BM, int BN, int WM, int WN, bool GATED, bool GATHER, int NS>
+__device__ __forceinline__ void gemm_mx_body(const FfnGroup& fg, int m0, int n0, int h,
+                                             uint4* __restrict__ smem) {
+  constexpr int NW = WM * WN;
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  static_assert(TM >= 1 && TN >= 1, "tile");
+  static_assert(!GATED || TN % 2 == 0, "gated needs gate/up pairs");
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "DMA rows split evenly over waves");
+  using SH = Fp8Shape<BM, BN, NW>;
+  constexpr int AI = BM / (8 * NW), BI = BN / (8 * NW);
+  constexpr int SPW = SH::SPW;
+  constexpr int LPS = AI + BI + SPW;                // DMA instructions per wave per stage
+  constexpr int A_ST = BM * 8, B_ST = BN * 8;       // uint4 per stage
+  constexpr int NMF = TM * TN;                      // MFMAs per 64-k half step
+  static_assert(NS >= 2 && NS <= 4 && LPS * (NS - 2) < 64, "LDS stages");
+  uint4* As = smem;                                 // [NS][BM rows][8 chunks]
+  uint4* Bs = smem + NS * A_ST;                     // [NS][BN rows][8 chunks]
+  uint32_t* Ss = reinterpret_cast<uint32_t*>(smem + NS * (A_ST + B_ST));   // [NS][S_ST]
+
+  const int rows = fg.rows, I = fg.inter;
+  const uint8_t* A = static_cast<const uint8_t*>(GATED ? fg.A1 : fg.C1);
+  const uint8_t* Asc = GATED ? fg.A1s : fg.C1s;
+  const uint8_t* B = static_cast<const uint8_t*>(GATED ? fg.B1 : fg.B2);
+  const uint8_t* Bsc = GATED ? fg.B1s : fg.B2s;
+  const int Kd = GATED ? h : I;          // reduction length = row bytes
+  const int KS = Kd / 32;                // scale bytes per row
+  const uint32_t b_rows = GATED ? 2 * I : h;
+  const uint32_t a_rows = (uint32_t)(GATHER ? fg.arows : rows);
+  const uint32_t a_bytes = a_rows * (uint32_t)Kd;
+  const uint32_t as_bytes = a_rows * (uint32_t)KS;
+  const __amdgpu_buffer_rsrc_t ra_rs = make_rsrc(A, a_bytes);
+  const __amdgpu_buffer_rsrc_t rb_rs = make_rsrc(B, b_rows * (uint32_t)Kd);
+  const __amdgpu_buffer_rsrc_t rsa_rs = make_rsrc(Asc, as_bytes);
+  const __amdgpu_buffer_rsrc_t rsb_rs = make_rsrc(Bsc, b_rows * (uint32_t)KS);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  // operand DMA as in the bf16 body, one byte per element
+  const int dr = lane >> 3;
+  const int dc = (lane & 7) ^ dr ^ (wave & 1);
+  const uint32_t a_lane = (uint32_t)(m0 + 8 * wave + dr) * Kd + dc * 16;
+  const uint32_t b_lane = (uint32_t)(n0 + 8 * wave + dr) * Kd + dc * 16;
+  const uint32_t b_lane_up = GATED ? b_lane + (uint32_t)I * Kd : b_lane;
+  const uint32_t x_stride = (uint32_t)(8 * NW) * Kd;
+  constexpr int BH = GATED ? BI / 2 : BI;
+  const __attribute__((address_space(1))) int32_t* gidx =
+      (const __attribute__((address_space(1))) int32_t*)fg.gidx;
+  uint32_t a_off[GATHER ? AI : 1];
+  if constexpr (GATHER) {
+    int src[AI];
+#pragma unroll
+    for (int x = 0; x < AI; ++x) {
+      const int r = m0 + 8 * (NW * x + wave) + dr;
+      src[x] = gidx[r < rows ? r : rows - 1];
+    }
+#pragma unroll
+    for (int x = 0; x < AI; ++x) {
+      const int r = m0 + 8 * (NW * x + wave) + dr;
+      a_off[x] = (r < rows && src[x] >= 0) ? (uint32_t)(src[x] / fg.gK) * Kd + dc * 16 : a_bytes;
+    }
+  }
+  // scale DMA: instruction z covers 64 rows (A rows first, then B rows); lane L fetches the
+  // k-step's scale dword of row 64z + L (past an operand's end: zero)
+  int s_z[SPW];
+  uint32_t s_off[SPW];
+#pragma unroll
+  for (int y = 0; y < SPW; ++y) {
+    // wave-uniform: the descriptor and the LDS destination (M0) stay scalar
+    const int z = __builtin_amdgcn_readfirstlane(min(NW * y + wave, SH::ZA + SH::ZB - 1));
+    s_z[y] = z;
+    if (z < SH::ZA) {
+      const int r = 64 * z + lane, gr = m0 + r;
+      bool ok = r < BM && gr < rows;
+      int srow = gr;
+      if constexpr (GATHER) {
+        const int sv = gidx[ok ? gr : 0];
+        ok = ok && sv >= 0;
+        srow = sv / fg.gK;
+      }
+      s_off[y] = ok ? (uint32_t)srow * KS : as_bytes;
+    } else {
+      const int r = 64 * (z - SH::ZA) + lane;
+      const int gr = GATED ? (r < BN / 2 ? n0 + r : I + n0 + r - BN / 2) : n0 + r;
+      s_off[y] = (uint32_t)gr * KS;
+    }
+  }
+  const int nk = __builtin_amdgcn_readfirstlane(Kd / 128);   // k-steps, in an SGPR
+  auto issue_one = [&](int step, int stage, int x) __attribute__((always_inline)) {
+    const uint32_t soff = (uint32_t)step * 128;
+    if (x < AI) {
+      if constexpr (GATHER)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra_rs, LDS_PTR(As + stage * A_ST + 64 * (NW * x + wave)), 16, a_off[x], soff, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra_rs, LDS_PTR(As + stage * A_ST + 64 * (NW * x + wave)), 16, a_lane,
+            soff + x * x_stride, 0, 0);
+    } else if (x < AI + BI) {
+      const int y = x - AI;
+      const int yh = y % BH;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb_rs, LDS_PTR(Bs + stage * B_ST + 64 * (NW * y + wave)), 16,
+          y < BH ? b_lane : b_lane_up, soff + yh * x_stride, 0, 0);
+    } else {
+      const int y = x - AI - BI;
+      const int z = s_z[y];
+      const uint32_t ks = __builtin_amdgcn_readfirstlane(step * 4);
+      if (z < SH::ZA)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsa_rs, LDS_PTR(Ss + stage * SH::S_ST + 64 * z), 4, s_off[y], ks, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsb_rs, LDS_PTR(Ss + stage * SH::S_ST + SH::BMS + 64 * (z - SH::ZA)), 4, s_off[y],
+            ks, 0, 0);
+    }
+  };
+
+  floatx16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  int arow[TM], brow[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) arow[i] = wm * WTM + i * 32 + (lane & 31);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    int br;
+    if (GATED)
+      br = j < TN / 2 ? wn * (WTN / 2) + j * 32 : BN / 2 + wn * (WTN / 2) + (j - TN / 2) * 32;
+    else
+      br = wn * WTN + j * 32;
+    brow[j] = br + (lane & 31);
+  }
+  intx8 fa[2][TM], fb[2][TN];
+  uint32_t sa[TM], sb[TN];
+  auto frag = [&](const uint4* base, int r, int c) __attribute__((always_inline)) {
+    const int sw = row_swz(r);
+    const intx4 lo = __builtin_bit_cast(intx4, base[r * 8 + (c ^ sw)]);
+    const intx4 hi = __builtin_bit_cast(intx4, base[r * 8 + ((c + 2) ^ sw)]);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  // fragments of MFMA `half` (0 or 1) of the k-step in `stage`
+  auto read_frags = [&](int set, int stage, int half) __attribute__((always_inline)) {
+    const int c = 4 * half + (lane >> 5);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[set][j] = frag(Bs + stage * B_ST, brow[j], c);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[set][i] = frag(As + stage * A_ST, arow[i], c);
+  };
+  auto read_scales = [&](int stage) __attribute__((always_inline)) {
+    const uint32_t* ss = Ss + stage * SH::S_ST;
+    const int sh = 8 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sa[i] = ss[arow[i]] >> sh;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sb[j] = ss[SH::BMS + brow[j]] >> sh;
+  };
+
+  // One k-step: two halves of NMF scaled MFMAs; the second half's fragments are read
+  // after the first MFMA; the next k-step's DMA rides along one instruction per MFMA.
+  auto kstep = [&](int stage, bool dma, int next_step, int dma_stage)
+                   __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int t = 0; t < NMF; ++t) {
+        const int i = t / TN, j = t % TN;
+        if (c == 0)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fb[0][j], fa[0][i], acc[i][j], 0, 0, 0, (int)sb[j], 0, (int)sa[i]);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fb[1][j], fa[1][i], acc[i][j], 0, 0, 2, (int)sb[j], 2, (int)sa[i]);
+        const int slot = c * NMF + t;
+        if (dma && slot >= 1 && slot - 1 < LPS) issue_one(next_step, dma_stage, slot - 1);
+        if (t == 0 && c == 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          read_frags(1, stage, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (dma) {
+#pragma unroll
+      for (int x = 2 * NMF - 1; x < LPS; ++x) issue_one(next_step, dma_stage, x);
+    }
+  };
+
+  if (nk > 0) {
+#pragma unroll
+    for (int s0 = 0; s0 < NS - 1; ++s0)
+      if (s0 < nk)
+#pragma unroll
+        for (int x = 0; x < LPS; ++x) issue_one(s0, s0, x);
+    if (nk >= NS - 1) wait_vmcnt<LPS * (NS - 2)>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    read_frags(0, 0, 0);
+    read_scales(0);
+    int kt = 0;
+    for (; kt + NS - 1 < nk; ++kt) {
+      kstep(kt % NS, true, kt + NS - 1, (kt + NS - 1) % NS);
+      wait_vmcnt<LPS * (NS - 2)>();
+      lds_barrier();
+      read_frags(0, (kt + 1) % NS, 0);
+      read_scales((kt + 1) % NS);
+    }
+    for (; kt + 1 < nk; ++kt) {
+      kstep(kt % NS, false, 0, 0);
+      const int after = nk - kt - 2;
+      if (NS > 3 && after >= 2) wait_vmcnt<LPS * (NS > 3 ? 2 : 0)>();
+      else if (NS > 2 && after >= 1) wait_vmcnt<LPS * (NS > 2 ? 1 : 0)>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      read_frags(0, (kt + 1) % NS, 0);
+      read_scales((kt + 1) % NS);
+    }
+    kstep((nk - 1) % NS, false, 0, 0);
+  }
+  __syncthreads();
+  if constexpr (GATED)
+    store_tile_mx<BM, BN, WM, WN>(acc, fg, m0, n0, smem);
+  else
+    store_tile<BM, BN, WM, WN, false>(acc, fg, m0, n0, h, smem);
+}
+
+template <int BM, int BN, int WM, int WN, bool GATED, int NS>
+constexpr size_t mx_lds_bytes() {
+  using SH = Fp8Shape<BM, BN, WM * WN>;
+  constexpr size_t ops = NS * ((size_t)(BM + BN) * 8 * 16 + (size_t)SH::S_ST * 4);
+  constexpr size_t stg = GATED ? (size_t)BM * (BN / 2 + 16) : (size_t)BM * (BN * 2 + 16);
+  return ops > stg ? ops : stg;
+}
+
+template <int BM, int BN, int WM, int WN, bool GATED, bool TALL>
+constexpr size_t mx_tile_lds_bytes() {
+  constexpr int NS = fp8_stages<BM>();
+  return TALL ? cmax<mx_lds_bytes<BM, BN, WM, WN, GATED, NS>(),
+                     mx_lds_bytes<BM + 32 * WM, BN / tall_split<WM, WN>(), WM, WN, GATED, NS>()>()
+              : mx_lds_bytes<BM, BN, WM, WN, GATED, NS>();
+}
+
+template <int BM, int BN, int WM, int WN, bool GATED, bool TALL>
+__device__ __forceinline__ void gemm_mx_tile(const FfnSched* __restrict__ sc, int h,
+                                             uint4* __restrict__ smem) {
+  constexpr int BMT = BM + 32 * WM, TS = tall_split<WM, WN>(), BNT = BN / TS;
+  constexpr int BNO = GATED ? BN / 2 : BN;
+  constexpr int NS = fp8_stages<BM>();
+  TileRef t;
+  if (!find_tile(sc, GATED, t)) return;   // no split-K here: every tile takes all of K
+  t.g = __builtin_amdgcn_readfirstlane(t.g);
+  t.m_tile = __builtin_amdgcn_readfirstlane(t.m_tile);
+  t.n_tile = __builtin_amdgcn_readfirstlane(t.n_tile);
+  t.tall = __builtin_amdgcn_readfirstlane(t.tall);
+  const FfnGroup& fg = sc->g[t.g];
+  const int m0 = t.m_tile * BM, n0 = t.n_tile * BNO;
+  const int n0t = n0 + (t.tall - 1) * (BNO / TS);
+  if (GATED && fg.gidx) {
+    if (TALL && t.tall)
+      gemm_mx_body<TALL ? BMT : BM, TALL ? BNT : BN, WM, WN, GATED, GATED, NS>(fg, m0, n0t, h,
+                                                                               smem);
+    else
+      gemm_mx_body<BM, BN, WM, WN, GATED, GATED, NS>(fg, m0, n0, h, smem);
+  } else {
+    if (TALL && t.tall)
+      gemm_mx_body<TALL ? BMT : BM, TALL ? BNT : BN, WM, WN, GATED, false, NS>(fg, m0, n0t, h,
+                                                                               smem);
+    else
+      gemm_mx_body<BM, BN, WM, WN, GATED, false, NS>(fg, m0, n0, h, smem);
+  }
+}
+
+template <int BM, int BN, int WM, int WN, bool TALL>
+__global__ __launch_bounds__(64 * WM * WN) void ffn_gate_up_mxfp8(const FfnSched* __restrict__ sc,
+                                                                  int h) {
+  __shared__ uint4 smem[mx_tile_lds_bytes<BM, BN, WM, WN, true, TALL>() / 16];
+  gemm_mx_tile<BM, BN, WM, WN, true, TALL>(sc, h, smem);
+}
+template <int BM, int BN, int WM, int WN, bool TALL>
+__global__ __launch_bounds__(64 * WM * WN) void ffn_down_mxfp8(const FfnSched* __restrict__ sc,
+                                                               int h) {
+  __shared__ uint4 smem[mx_tile_lds_bytes<BM, BN, WM, WN, false, TALL>() / 16];
+  gemm_mx_tile<BM, BN, WM, WN, false, TALL>(sc, h, smem);
+}
+
 constexpr int F_BM = 64, F_BN = 64, F_BK = 16;
 template <bool GATED>
 __global__ __launch_bounds__(256) void ffn_gemm_f32(const FfnSched* __restrict__ sc, int h) {
@@ -740,6 +1114,31 @@ bool launch_bf16(Tiles k, bool gated, const FfnSched* sc, int h, int64_t ub, int
   }
 }
 
+template <int BM, int BN, int WM, int WN, bool TALL>
+bool launch_mx_gemm(bool gated, const FfnSched* sc, int h, int64_t ub, hipStream_t st) {
+  constexpr int NT = 64 * WM * WN;
+  if (ub <= 0) return true;
+  const int64_t g = (ub + kNumXcd - 1) / kNumXcd * kNumXcd;
+  if (gated)
+    hipLaunchKernelGGL((ffn_gate_up_mxfp8<BM, BN, WM, WN, TALL>), dim3((unsigned)g), dim3(NT), 0,
+                       st, sc, h);
+  else
+    hipLaunchKernelGGL((ffn_down_mxfp8<BM, BN, WM, WN, TALL>), dim3((unsigned)g), dim3(NT), 0, st,
+                       sc, h);
+  return hipGetLastError() == hipSuccess;
+}
+
+// MX-FP8 tiles: the 128- and 32-row shapes (a 256-row tile's two fragment sets of 32-byte
+// operands do not fit the register file beside its accumulators).
+Tiles mx_tiles(Tiles k) { return k == Tiles::Large ? Tiles::Medium : k; }
+
+bool launch_mx(Tiles k, bool gated, const FfnSched* sc, int h, int64_t ub, hipStream_t st) {
+  switch (mx_tiles(k)) {
+    case Tiles::Medium: return launch_mx_gemm<128, 256, 2, 2, true>(gated, sc, h, ub, st);
+    default: return launch_mx_gemm<32, 256, 1, 4, true>(gated, sc, h, ub, st);
+  }
+}
+
 }  // namespace
 
 size_t ffn_sched_bytes(const Dims&) { return sizeof(FfnSched); }
@@ -771,11 +1170,12 @@ int ffn_prep_args(const moe_problem* p, const Dims& d, const void* xp, const voi
   int BN1 = F_BN / 2, BN2 = F_BN, split_max = 1;
   const int has_sh = (p->n_shared && d.sh_rows > 0) ? 1 : 0;
   if (d.bf16) {
-    t1 = tiling(tile_kind(d, true));
-    t2 = tiling(tile_kind(d, false));
+    t1 = tiling(d.mx ? mx_tiles(tile_kind(d, true)) : tile_kind(d, true));
+    t2 = tiling(d.mx ? mx_tiles(tile_kind(d, false)) : tile_kind(d, false));
     int min_k = d.h < p->inter ? d.h : p->inter;
     if (has_sh && p->shared_inter < min_k) min_k = p->shared_inter;
     split_max = min_k / 64 < kMaxSplit ? min_k / 64 : kMaxSplit;
+    if (d.mx) split_max = 1;   // the MX-FP8 GEMMs take whole tiles
     BN1 = 128;   // output columns of the gated tile (256 B rows: 128 gate + 128 up)
     BN2 = 256;
   }
@@ -792,6 +1192,15 @@ int ffn_prep_args(const moe_problem* p, const Dims& d, const void* xp, const voi
   a->arrive = reinterpret_cast<int*>(ws + L.arrive);
   a->row_src = gather_rows;
   a->phys_expert = nullptr;
+  // MX-FP8: the GEMM operands are E4M3 (x's copy and the gated product in the workspace);
+  // the weight scales are filled in by the caller
+  a->x_s = a->w13_s = a->w2_s = a->w13_sh_s = a->w2_sh_s = nullptr;
+  a->hbuf_s = nullptr;
+  if (d.mx) {
+    a->x = ws + L.xq;
+    a->x_s = ws + L.xs;
+    a->hbuf_s = ws + L.hbuf_s;
+  }
   a->p0 = d.e0;
   a->sh_rows = d.sh_rows;
   a->sh_t0 = (int64_t)d.rank * d.tpr;
@@ -802,7 +1211,8 @@ int ffn_prep_args(const moe_problem* p, const Dims& d, const void* xp, const voi
   a->h = d.h;
   a->inter = p->inter;
   a->sh_inter = p->shared_inter;
-  a->s = d.s;
+  a->s = d.mx ? 1 : d.s;
+  a->sy = d.s;
   a->K = d.K;
   a->BM1 = t1.BM; a->BM2 = t2.BM;
   a->tall_extra1 = t1.tall_extra; a->tall_extra2 = t2.tall_extra;
@@ -849,7 +1259,11 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
   const int64_t ub1 = m_ub(a.BM1) * nt1 + m_sh(a.BM1) * nt1s;
   const int64_t ub2 = (m_ub(a.BM2) + m_sh(a.BM2)) * nt2;
   bool ok = true;
-  if (d.bf16) {
+  if (d.mx) {
+    ok = launch_mx(tile_kind(d, true), true, sc, d.h, ub1, st);
+    if (ok && ev) ok = hipEventRecord(ev[1], st) == hipSuccess;
+    if (ok) ok = launch_mx(tile_kind(d, false), false, sc, d.h, ub2, st);
+  } else if (d.bf16) {
     ok = launch_bf16(tile_kind(d, true), true, sc, d.h, ub1, cpx, part, a.arrive, st);
     if (ok && ev) ok = hipEventRecord(ev[1], st) == hipSuccess;
     if (ok) ok = launch_bf16(tile_kind(d, false), false, sc, d.h, ub2, cpx, part, a.arrive, st);

@@ -28,6 +28,11 @@ struct FfnGroup {
                 // split into tall_split narrower tiles per n-tile
   int arows;  // rows addressable through A1 (rows, or T when gathering)
   int gK;     // pairs per token (row index -> token) when gathering
+  // MX-FP8 only: E8M0 scale bytes, one per 32 values along each row's reduction dimension
+  const uint8_t* A1s;  // of A1's rows: [arows][h/32]
+  const uint8_t* B1s;  // [2*inter][h/32]
+  uint8_t* C1s;        // of the gated product's rows: [rows][inter/32]
+  const uint8_t* B2s;  // [h][inter/32]
 };
 
 struct FfnSched {
@@ -61,8 +66,18 @@ struct FfnPrepArgs {
                                // expert phys_expert[p0 + g] (w13 / w2 hold every logical
                                // expert); nullptr: group g uses weight block g
   int p0;
+  // MX-FP8 (else nullptr): scale bytes of x (token rows, [T][h/32]), of the weights and of
+  // the gated product's rows (beside hbuf)
+  const char* x_s;
+  const char* w13_s;
+  const char* w2_s;
+  const char* w13_sh_s;
+  const char* w2_sh_s;
+  char* hbuf_s;
   int64_t sh_rows, sh_t0, R_max, T;
-  int El, has_shared, h, inter, sh_inter, s, K;
+  int El, has_shared, h, inter, sh_inter, K;
+  int s;    // bytes per element of x, the weights and hbuf (the GEMM operands)
+  int sy;   // bytes per element of yp / y_sh
   int BM1, BM2, tall_extra1, tall_extra2, tall_split1, tall_split2, BN1, BN2;
   int cu_per_xcd, split_max;
 };
@@ -112,6 +127,8 @@ __device__ inline void ffn_build_sched(const FfnPrepArgs& a, const int32_t* offs
     c2[i] = 0;
     if (g < G) {
       FfnGroup fg;
+      fg.A1s = fg.B1s = fg.B2s = nullptr;
+      fg.C1s = nullptr;
       int rows, I;
       if (g < a.El) {
         const int r0 = offsets[g];
@@ -123,7 +140,13 @@ __device__ inline void ffn_build_sched(const FfnPrepArgs& a, const int32_t* offs
         fg.B1 = a.w13 + (size_t)wg * 2 * a.inter * a.h * a.s;
         fg.C1 = a.hbuf + (size_t)r0 * a.inter * a.s;
         fg.B2 = a.w2 + (size_t)wg * a.h * a.inter * a.s;
-        fg.C2 = a.yp + (size_t)r0 * a.h * a.s;
+        fg.C2 = a.yp + (size_t)r0 * a.h * a.sy;
+        if (a.w13_s) {
+          fg.A1s = reinterpret_cast<const uint8_t*>(a.x_s);
+          fg.B1s = reinterpret_cast<const uint8_t*>(a.w13_s) + (size_t)wg * 2 * a.inter * (a.h / 32);
+          fg.C1s = reinterpret_cast<uint8_t*>(a.hbuf_s) + (size_t)r0 * (a.inter / 32);
+          fg.B2s = reinterpret_cast<const uint8_t*>(a.w2_s) + (size_t)wg * a.h * (a.inter / 32);
+        }
       } else {
         rows = (int)a.sh_rows;
         I = a.sh_inter;
@@ -133,6 +156,12 @@ __device__ inline void ffn_build_sched(const FfnPrepArgs& a, const int32_t* offs
         fg.C1 = a.hbuf + (size_t)a.R_max * a.inter * a.s;
         fg.B2 = a.w2_sh;
         fg.C2 = a.y_sh;
+        if (a.w13_s) {
+          fg.A1s = reinterpret_cast<const uint8_t*>(a.x_s) + (size_t)a.sh_t0 * (a.h / 32);
+          fg.B1s = reinterpret_cast<const uint8_t*>(a.w13_sh_s);
+          fg.C1s = reinterpret_cast<uint8_t*>(a.hbuf_s) + (size_t)a.R_max * (a.inter / 32);
+          fg.B2s = reinterpret_cast<const uint8_t*>(a.w2_sh_s);
+        }
       }
       int per_n[2];
       const int BMg[2] = {a.BM1, a.BM2}, TEg[2] = {a.tall_extra1, a.tall_extra2};

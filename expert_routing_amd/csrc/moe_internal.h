@@ -39,7 +39,8 @@ struct Dims {
   int64_t tpr;      // tokens per virtual rank (T / N), 0 when T % N != 0
   int64_t sh_rows;  // shared-expert rows (T/N or 0)
   int s;            // activation bytes
-  bool bf16;
+  bool bf16;        // bf16 activations (also with MX-FP8 expert weights)
+  bool mx;          // MX-FP8 expert weights and GEMM operands
   int route_split;  // K-slices of the router GEMM (partial logits summed in order)
 };
 
@@ -50,7 +51,9 @@ struct WsLayout {
   size_t chunk_base;    // [n_chunks][E] i32
   size_t kept;          // [E_l] i32
   size_t sched;         // ffn tile schedule
-  size_t hbuf;          // [R_max + sh_rows][I_max] act
+  size_t hbuf;          // [R_max + sh_rows][I_max] act (MX-FP8: E4M3 codes)
+  size_t hbuf_s;        // MX-FP8: the gated product's scale bytes [..][I_max/32]
+  size_t xq, xs;        // MX-FP8: x as E4M3 codes [T][h] and scale bytes [T][h/32]
   size_t splitk;        // split-K partial sums (fp32), bf16 problems only
   size_t arrive;        // split-K arrival counters
   size_t stats;         // layout statistics scratch: scan outputs [E + E_l + 2] i32, then
@@ -115,6 +118,11 @@ int launch_layout_stats(const moe_problem* p, const Dims& d, const int32_t* ids,
                         int64_t* busiest, char* ws, const WsLayout& L, hipStream_t st);
 int launch_combine(const moe_problem* p, const Dims& d, const void* yp, const int32_t* dest_row,
                    const float* w, const void* y_sh, void* y, hipStream_t st);
+
+// MX-FP8 quantisation of a rows x cols matrix (cols % 32 == 0): codes [rows][cols],
+// scale bytes [rows][cols / 32].
+int launch_mx_quant(const void* src, bool bf16, int64_t rows, int cols, uint8_t* codes,
+                    uint8_t* scales, hipStream_t st);
 
 size_t ffn_sched_bytes(const Dims& d);
 size_t ffn_splitk_bytes(const Dims& d);

@@ -46,7 +46,7 @@ enum moe_status {
 };
 
 enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
-enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
+enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1, MOE_DTYPE_MXFP8 = 2 };
 
 /*
  * The problem statement of one MoE layer call, in the pages' own quantities: T tokens
@@ -85,7 +85,15 @@ enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
  *               256 routed + 1 shared expert)
  *  shared_inter SwiGLU intermediate size of the shared expert
  *  act_dtype    MOE_DTYPE_F32 or MOE_DTYPE_BF16 (activations and expert weights;
- *               accumulation is fp32 either way)
+ *               accumulation is fp32 either way), or MOE_DTYPE_MXFP8: activations
+ *               (x, xp, yp, y_sh, y) bf16 and the expert weights MX-FP8 (E4M3 codes
+ *               with E8M0 scales, see moe_quantize_mx). The expert FFN then runs on the
+ *               FP8 matrix cores: x is quantised once per token before dispatch, the
+ *               GEMMs apply the block scales inside the MFMA, and the gated product is
+ *               quantised in the gate/up GEMM's epilogue ("Expert-Parallelism",
+ *               关键观察 observation 3: quantise / dequantise passes cost as much as the
+ *               GEMMs unless fused). Only moe_forward and its variants take it; the
+ *               stage call moe_expert_ffn returns MOE_ERR_UNSUPPORTED.
  */
 typedef struct moe_problem {
   int64_t T;
@@ -106,7 +114,8 @@ typedef struct moe_problem {
  * Invalid: T < 0, h <= 0, E not in 1..512, K not in 1..min(E,16), E % n_ep != 0,
  * ep_rank outside [0, n_ep), E % n_groups != 0, topk_groups outside 1..n_groups,
  * topk_groups*E/n_groups < K, padding without a capacity, n_shared not 0/1,
- * n_shared = 1 with T % n_ep != 0. Unsupported (bf16): h % 64 != 0, inter % 64 != 0,
+ * n_shared = 1 with T % n_ep != 0. Unsupported (MX-FP8): h, inter or shared_inter not a
+ * multiple of 128, and the bf16 limits below; (bf16): h % 64 != 0, inter % 64 != 0,
  * shared_inter % 64 != 0, or operands beyond the GEMMs' 32-bit byte offsets:
  * (rows + 1) * max(h, inter, shared_inter) * 2 >= 2^32 with rows = T (the capacity when
  * padding to a larger one), or 2 * max(inter, shared_inter) * h * 2 >= 2^32;
@@ -158,7 +167,8 @@ int moe_select(const moe_problem* p, const float* logits, const float* bias,
  *              was dropped or its expert is remote
  *   row_src    [R_max] int32 out: t*K+k of the row's pair, -1 for pad / unused rows
  *   send_bytes [n_ep][n_ep] int64 out or NULL; kept pairs only, diagonal included;
- *              needs T % n_ep == 0
+ *              needs T % n_ep == 0. With MOE_DTYPE_MXFP8 a pair counts h + h/32 bytes
+ *              (the row's E4M3 codes and scale bytes: x is quantised before dispatch)
  *   n_dropped  [1] int32 out: pairs dropped by capacity, over all E experts
  *   xp         [R_max][h] act out or NULL: xp[r] = x[row_src[r]/K]; pad rows zero;
  *              rows at or past offsets[E_l] (compact layout) are left undefined      */
@@ -239,6 +249,13 @@ typedef struct moe_tensors {
   void* yp;                 /* [R_max][h] act                              */
   void* y_sh;               /* [T/n_ep][h] act or NULL                     */
   void* y;                  /* [T][h] act out                              */
+  /* MX-FP8 only (NULL otherwise): E8M0 scale bytes of the weights, one per 32 values
+   * along h for w13 / w13_sh and along the intermediate dimension for w2 / w2_sh; the
+   * weights themselves are then E4M3 codes in the layouts above.                      */
+  const uint8_t* w13_scale;     /* [E_l][2*inter][h/32]                      */
+  const uint8_t* w2_scale;      /* [E_l][h][inter/32]                        */
+  const uint8_t* w13_sh_scale;  /* [2*shared_inter][h/32] or NULL            */
+  const uint8_t* w2_sh_scale;   /* [h][shared_inter/32] or NULL              */
 } moe_tensors;
 
 int moe_forward(const moe_problem* p, const moe_tensors* t, void* ws, size_t ws_bytes,
@@ -261,6 +278,19 @@ enum moe_trace_point {
 };
 int moe_forward_traced(const moe_problem* p, const moe_tensors* t, void* ws, size_t ws_bytes,
                        void* stream, void* const* events);
+
+/* ---- MX-FP8 quantisation ------------------------------------------------------------
+ * OCP E4M3 codes with one power-of-two scale per 32 consecutive values of a row (OCP
+ * Microscaling): a block's scale is 2^X, X = floor(log2(max |v|)) - 8 (the largest E4M3
+ * exponent), -127 for an all-zero block, clamped to [-127, 127], stored as the byte X + 127;
+ * each value becomes the E4M3 code of v / 2^X, rounded to nearest with ties to the even
+ * code and saturated at +-448 (no NaN codes are produced; the sign bit is v's). FP8 data
+ * paths of MoE layers spend much of their time in such quantise / dequantise passes next to
+ * the GEMMs ("Expert-Parallelism", 关键观察, observation 3).
+ *   src     [rows][cols] device, src_dtype MOE_DTYPE_F32 or MOE_DTYPE_BF16; cols % 32 == 0
+ *   codes   [rows][cols] uint8 out;  scales [rows][cols/32] uint8 out                   */
+int moe_quantize_mx(int64_t rows, int32_t cols, int32_t src_dtype, const void* src,
+                    uint8_t* codes, uint8_t* scales, void* stream);
 
 /* ---- redundant experts ---------------------------------------------------------------
  * A logical -> physical replica map: P = E + R physical experts (replicas), P a multiple of
