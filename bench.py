@@ -3,6 +3,7 @@
 on one MI355X, seeded synthetic inputs resident in HBM.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME|all] [--no-cpu-baseline]
+                    [--dtype bf16|mxfp8]
 
 Default workload: the Mixtral-shaped prefill layer (T=4096 tokens, h=4096, 8 experts, top-2
 softmax, SwiGLU inter=14336, bf16 with fp32 accumulation, fp32 router, no capacity limit).
@@ -19,6 +20,11 @@ L2s and the 256 MB Infinity Cache), outside the stage events; `flushed` reports 
 times and the per-stage rates against the HBM / MFMA rooflines. The CPU baseline times
 the fp64 oracle on the same workload; its routing result also gives the near-tie count and
 the first-choice skew.
+
+`--dtype mxfp8` runs the same workload with MX-FP8 expert weights (E4M3 codes and E8M0
+block scales, quantised once on the GPU before timing): x is quantised per token inside
+the step, both GEMMs run on the FP8 matrix cores, and their rates are taken against the
+dense fp8 MFMA peak.
 """
 from __future__ import annotations
 
@@ -36,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "routed tokens/sec per MoE layer (route+dispatch+FFN+combine); % MFMA/HBM peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (the MX-FP8 GEMMs)
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 RIDGE_BF16 = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per byte
@@ -46,7 +53,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 # kernel name prefix -> stage of the layer
 STAGE_OF = [("router_", "route"), ("select_", "route"), ("logits_", "route"),
-            ("disp_", "dispatch"), ("ffn_prep", "ffn_prep"), ("ffn_gate_up", "ffn_gate_up"),
+            ("disp_", "dispatch"), ("mx_quant", "dispatch"), ("ffn_prep", "ffn_prep"),
+            ("ffn_gate_up", "ffn_gate_up"),
             ("ffn_down", "ffn_down"), ("combine", "combine")]
 
 
@@ -178,10 +186,13 @@ def cpu_baseline(cfg, inp, ids_gpu, min_seconds=10.0):
                        f"{cfg.E_local} local experts on their rows, combine"}, check)
 
 
-def stage_work(cfg, R, active, gather):
+def stage_work(cfg, R, active, gather, mx=False):
     """Algorithmic bytes and flops of each stage of one layer call (what the method must
-    move: each operand read once, each result written once)."""
+    move: each operand read once, each result written once). With MX-FP8 weights an
+    operand element of the GEMMs is one byte plus a scale byte per 32."""
     s = cfg.act_bytes
+    if mx:
+        return stage_work_mx(cfg, R, active)
     T, h, E, K, I = cfg.T, cfg.h, cfg.E, cfg.K, cfg.inter
     sh = (T // cfg.n_ep) if cfg.n_shared else 0
     Is = cfg.shared_inter
@@ -204,42 +215,84 @@ def stage_work(cfg, R, active, gather):
     return w
 
 
-def rate(work, ms, bound=None):
+def stage_work_mx(cfg, R, active):
+    T, h, E, K, I = cfg.T, cfg.h, cfg.E, cfg.K, cfg.inter
+    sh = (T // cfg.n_ep) if cfg.n_shared else 0
+    Is = cfg.shared_inter
+    n_sh = 1 if cfg.n_shared else 0
+    q = 33 / 32    # E4M3 byte + its share of the block's scale byte
+    return {
+        "route": {"bytes": T * h * 2 + E * h * 4 + T * K * 8, "flops": 2.0 * T * h * E},
+        # per-token quantisation of x (bf16 in, codes and scales out) and the layout
+        "dispatch": {"bytes": T * h * 2 + T * h * q + 8 * T * K + 4 * R + 4 * E, "flops": 0.0},
+        "ffn_gate_up": {"bytes": (2 * I * h * active + 2 * Is * h * n_sh + R * h + sh * h
+                                  + R * I + sh * Is) * q,
+                        "flops": 4.0 * R * h * I + 4.0 * sh * h * Is},
+        "ffn_down": {"bytes": (I * h * active + Is * h * n_sh + R * I + sh * Is) * q
+                     + (R * h + sh * h) * 2,
+                     "flops": 2.0 * R * I * h + 2.0 * sh * Is * h},
+        "combine": {"bytes": R * h * 2 + T * h * 2 + 8 * T * K + sh * h * 2, "flops": 0.0},
+    }
+
+
+def rate(work, ms, bound=None, mfma_peak=PEAK_BF16_TFLOPS):
     """Achieved GB/s and TFLOP/s of a stage, and its roofline fraction: against HBM when its
-    arithmetic intensity is below the bf16 ridge, else against bf16 MFMA (the router: fp32
-    vector when its flops outweigh its bytes at the fp32 ridge)."""
+    arithmetic intensity is below the ridge of `mfma_peak`, else against that peak (the
+    GEMMs: the dtype's dense MFMA peak; the router: route_bound's)."""
     sec = ms * 1e-3
     gbs = work["bytes"] / sec / 1e9
     tfs = work["flops"] / sec / 1e12
     if bound is None:
         ai = work["flops"] / max(work["bytes"], 1)
-        bound = "mfma" if ai > RIDGE_BF16 else "hbm"
+        bound = "mfma" if ai > mfma_peak * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
     if bound == "hbm":
         frac = gbs / PEAK_HBM_GBS
-    elif bound == "f32":
-        frac = tfs / PEAK_F32_TFLOPS
     else:
-        frac = tfs / PEAK_BF16_TFLOPS
+        frac = tfs / mfma_peak
     return {"us": round(ms * 1e3, 2), "GBps": round(gbs, 1), "TFLOPs": round(tfs, 2),
             "bound": bound, "frac": round(frac, 4)}
 
 
+# The router's logits are fp32-exact: with bf16 activations the fp32 weight enters as three
+# bf16 planes, so one algorithmic multiply-add costs three bf16 MFMA ones; with fp32
+# activations it runs on the fp32 vector units.
+PEAK_ROUTER_MFMA_TFLOPS = PEAK_BF16_TFLOPS / 3
+
+
 def route_bound(cfg):
-    # the fp32 router against fp32 vector peak once its flops outweigh its bytes there
-    w = 2.0 * cfg.T * cfg.h * cfg.E / (cfg.T * cfg.h * cfg.act_bytes)
-    return "f32" if w > PEAK_F32_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
+    """(bound, peak TFLOP/s) of the router: its compute peak once its flops outweigh its
+    bytes there, else HBM."""
+    ai = 2.0 * cfg.T * cfg.h * cfg.E / (cfg.T * cfg.h * cfg.act_bytes + cfg.E * cfg.h * 4)
+    peak = PEAK_F32_TFLOPS if cfg.dtype == "f32" else PEAK_ROUTER_MFMA_TFLOPS
+    if ai > peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+        return ("f32" if cfg.dtype == "f32" else "mfma"), peak
+    return "hbm", peak
 
 
 def run_workload(name, args, moe, torch, np):
     from synth import CONFIGS, make_inputs
 
     cfg = CONFIGS[name]
+    mx = args.dtype == "mxfp8"
     inp = make_inputs(cfg, device="cuda")
     p = moe.problem_from_config(cfg)
+    if mx:
+        p.act_dtype = moe.DTYPE["mxfp8"]
     b = moe.alloc_buffers(p, "cuda")
     t = dict(b)
     t.update(x=inp["x"], w_router=inp["w_router"], bias=inp["bias"], w13=inp["w13"],
              w2=inp["w2"], w13_sh=inp["w13_sh"], w2_sh=inp["w2_sh"])
+    if mx:
+        # the weights as E4M3 codes and block scales, quantised once before timing
+        for k in ("w13", "w2", "w13_sh", "w2_sh"):
+            w = inp[k]
+            if w is None:
+                t[k + "_scale"] = None
+                continue
+            c, sc = moe.quantize_mx(w.reshape(-1, w.shape[-1]))
+            t[k] = c.reshape(w.shape)
+            t[k + "_scale"] = sc.reshape(w.shape[:-1] + (w.shape[-1] // 32,))
+        torch.cuda.synchronize()
     gather = not args.materialize_xp
     if gather:
         t["xp"] = None
@@ -313,22 +366,25 @@ def run_workload(name, args, moe, torch, np):
     R = int(offsets[-1])
     active = int((np.diff(offsets) > 0).sum())
     dropped = int(b["n_dropped"].item())
-    work = stage_work(cfg, R, active, gather)
+    work = stage_work(cfg, R, active, gather, mx)
     T, K = cfg.T, cfg.K
     gu = work["ffn_gate_up"]
-    gu_bound = "mfma" if gu["flops"] / gu["bytes"] > RIDGE_BF16 else "hbm"
-    traffic = load_traffic(name)
+    mfma_peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
+    gu_bound = "mfma" if gu["flops"] / gu["bytes"] > mfma_peak * 1e12 / (PEAK_HBM_GBS * 1e9) \
+        else "hbm"
+    traffic = load_traffic(name + ("_mxfp8" if mx else ""))
     gu_ms = net(steady)["ffn_gate_up"]
+    kname = ("ffn_gate_up_mxfp8 (grouped gate/up GEMM on scaled FP8 MFMA, fused silu*mul "
+             "and MX quantisation)" if mx else
+             "ffn_gate_up_bf16 (grouped gate/up GEMM, fused silu*mul)")
     if gu_bound == "mfma":
         achieved = gu["flops"] / (gu_ms * 1e-3) / 1e12
-        roof = {"kernel": "ffn_gate_up_bf16 (grouped gate/up GEMM, fused silu*mul)",
-                "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS}
+        roof = {"kernel": kname, "bound": "mfma", "achieved": achieved, "peak": mfma_peak,
+                "unit": "TFLOP/s", "frac": achieved / mfma_peak}
     else:
         achieved = gu["bytes"] / (gu_ms * 1e-3) / 1e9
-        roof = {"kernel": "ffn_gate_up_bf16 (grouped gate/up GEMM, fused silu*mul)",
-                "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS}
+        roof = {"kernel": kname, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS}
     roof.update({"traffic": (traffic["ffn_gate_up"]["fetch_bytes"]
                              + traffic["ffn_gate_up"]["write_bytes"]) if traffic else None,
                  "algorithmic_flops": gu["flops"], "algorithmic_bytes": gu["bytes"],
@@ -336,18 +392,19 @@ def run_workload(name, args, moe, torch, np):
 
     def stage_rates(st):
         r = {}
+        rb, rpeak = route_bound(cfg)
         for sname in ("route", "dispatch", "ffn_gate_up", "ffn_down", "combine"):
             r[sname] = rate(work[sname], st[sname],
-                            route_bound(cfg) if sname == "route" else
-                            ("hbm" if sname in ("dispatch", "combine") else None))
+                            rb if sname == "route" else
+                            ("hbm" if sname in ("dispatch", "combine") else None),
+                            mfma_peak=rpeak if sname == "route" else mfma_peak)
         r["ffn_prep"] = {"us": round(st["ffn_prep"] * 1e3, 2)}   # 0: built by dispatch
         # route + dispatch + prep + combine against their summed roofline times
         rdc_t = st["route"] + st["dispatch"] + st["ffn_prep"] + st["combine"]
         roof_t = 0.0
         for sname in ("route", "dispatch", "combine"):
             wk = work[sname]
-            peak_f = PEAK_F32_TFLOPS if route_bound(cfg) == "f32" and sname == "route" \
-                else PEAK_BF16_TFLOPS
+            peak_f = rpeak if sname == "route" else PEAK_BF16_TFLOPS
             roof_t += max(wk["bytes"] / (PEAK_HBM_GBS * 1e9), wk["flops"] / (peak_f * 1e12))
         r["route_dispatch_combine"] = {"us": round(rdc_t * 1e3, 2),
                                        "roofline_us": round(roof_t * 1e6, 2),
@@ -365,7 +422,7 @@ def run_workload(name, args, moe, torch, np):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "dtype": "mxfp8" if mx else ("bf16" if cfg.dtype == "bf16" else "f32"),
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": T, "h": cfg.h, "E": cfg.E, "K": K,
                    "inter": cfg.inter, "score": cfg.score, "n_groups": cfg.n_groups,
@@ -398,7 +455,7 @@ def run_workload(name, args, moe, torch, np):
         sb = b["send_bytes"].cpu().numpy()
         result["layout"]["send_bytes_row_sum_mean"] = float(sb.sum(1).mean())
         result["layout"]["send_zero_pair_fraction"] = float((sb == 0).mean())
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not mx:
         ids = b["topk_ids"].cpu().numpy()
         result["cpu_baseline"], result["routing_check"] = cpu_baseline(cfg, inp, ids)
     else:
@@ -421,6 +478,9 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one device copy of a known size (counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--dtype", choices=["bf16", "mxfp8"], default="bf16",
+                    help="expert weights and GEMM operands: bf16 (the workloads' dtype), or "
+                         "MX-FP8 (E4M3 with E8M0 block scales; activations stay bf16)")
     ap.add_argument("--materialize-xp", action="store_true",
                     help="pass xp, so dispatch copies rows into it (default: no xp; the "
                          "gate/up GEMM reads x through row_src)")

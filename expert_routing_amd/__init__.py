@@ -96,7 +96,7 @@ _status_string = _sig("moe_status_string", [ctypes.c_int], ctypes.c_char_p)
 _route = _sig("moe_route", [_P, _V, _V, _V, _V, _V, _V, _SZ, _V])
 _select = _sig("moe_select", [_P, _V, _V, _V, _V, _V])
 _dispatch = _sig("moe_dispatch", [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _SZ, _V])
-_expert_ffn = _sig("moe_expert_ffn", [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _SZ, _V])
+_expert_ffn = _sig("moe_expert_ffn", [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _SZ, _V])
 _combine = _sig("moe_combine", [_P, _V, _V, _V, _V, _V, _V])
 _layout_stats = _sig("moe_layout_stats", [_P, _V, _V, _V, _V, _V, _V, _SZ, _V])
 _forward = _sig("moe_forward", [_P, ctypes.POINTER(Tensors), _V, _SZ, _V])
@@ -197,11 +197,13 @@ def moe_dispatch(p, x, topk_ids, counts, offsets, dest_row, row_src, send_bytes,
                   wp, wn, _stream(stream)), "moe_dispatch")
 
 
-def moe_expert_ffn(p, xp, offsets, w13, w2, x, w13_sh, w2_sh, yp, y_sh, ws, stream=None):
+def moe_expert_ffn(p, xp, offsets, w13, w2, x, w13_sh, w2_sh, yp, y_sh, ws, stream=None,
+                   row_src=None):
+    """xp=None with row_src: the gate/up GEMM reads its rows from x through row_src."""
     wp, wn = _ws(ws)
-    _ok(_expert_ffn(ctypes.byref(p), _ptr(xp), _ptr(offsets), _ptr(w13), _ptr(w2), _ptr(x),
-                    _ptr(w13_sh), _ptr(w2_sh), _ptr(yp), _ptr(y_sh), wp, wn, _stream(stream)),
-        "moe_expert_ffn")
+    _ok(_expert_ffn(ctypes.byref(p), _ptr(xp), _ptr(row_src), _ptr(offsets), _ptr(w13),
+                    _ptr(w2), _ptr(x), _ptr(w13_sh), _ptr(w2_sh), _ptr(yp), _ptr(y_sh), wp, wn,
+                    _stream(stream)), "moe_expert_ffn")
 
 
 def moe_combine(p, yp, dest_row, topk_w, y_sh, y, stream=None):

@@ -299,19 +299,23 @@ int moe_dispatch(const moe_problem* p, const void* x, const int32_t* topk_ids,
                          n_dropped, xp, (char*)ws, L, (hipStream_t)stream);
 }
 
-int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* offsets,
-                   const void* w13, const void* w2, const void* x, const void* w13_sh,
-                   const void* w2_sh, void* yp, void* y_sh,
+int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* row_src,
+                   const int32_t* offsets, const void* w13, const void* w2, const void* x,
+                   const void* w13_sh, const void* w2_sh, void* yp, void* y_sh,
                    void* ws, size_t ws_bytes, void* stream) {
   Dims d;
   int st = make_dims(p, &d);
   if (st != MOE_OK) return st;
   if (d.mx) return MOE_ERR_UNSUPPORTED;   // the weight scales travel in moe_tensors
-  if ((st = v_ffn(p, d, xp, offsets, w13, w2, x, w13_sh, w2_sh, yp, y_sh, ws, ws_bytes)) != MOE_OK)
+  // no xp: the gate/up GEMM gathers its rows from x through row_src
+  const bool gather = xp == nullptr;
+  if (gather && d.R_max > 0 && (!row_src || !x)) return MOE_ERR_INVALID;
+  if ((st = v_ffn(p, d, xp, offsets, w13, w2, x, w13_sh, w2_sh, yp, y_sh, ws, ws_bytes,
+                  gather)) != MOE_OK)
     return st;
   WsLayout L = ws_layout(p, d);
   return launch_ffn(p, d, xp, offsets, w13, w2, x, w13_sh, w2_sh, yp, y_sh, (char*)ws, L,
-                    (hipStream_t)stream);
+                    (hipStream_t)stream, nullptr, gather ? row_src : nullptr);
 }
 
 int moe_combine(const moe_problem* p, const void* yp, const int32_t* dest_row,

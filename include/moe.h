@@ -182,17 +182,24 @@ int moe_dispatch(const moe_problem* p, const void* x, const int32_t* topk_ids,
  * "技術原理" step 3; "MoE 服務的專家並行性": grouped GEMM batching many experts):
  *   yp = (silu(xp W_g^T) * (xp W_u^T)) W_d^T, fp32 accumulation; the gated product is
  *   rounded to act once before the down projection.
- *   xp        [R_max][h] act (rows below offsets[E_l] are read)
+ *   xp        [R_max][h] act (rows below offsets[E_l] are read), or NULL: then the
+ *             gate/up GEMM reads row r straight from x[row_src[r] / K] (a row whose
+ *             row_src is negative reads zeros), the permutation folded into its operand
+ *             loads, and xp need not exist
+ *   row_src   [R_max] int32 (device) as written by moe_dispatch; needed when xp is NULL,
+ *             ignored otherwise
  *   offsets   [E_l+1] int32 (device) as written by moe_dispatch
  *   w13       [E_l][2*inter][h] act: per expert W_g rows then W_u rows
  *   w2        [E_l][h][inter] act: per expert W_d
- *   x, w13_sh, w2_sh   shared expert input [T][h], weights [2*shared_inter][h] and
- *             [h][shared_inter]; all NULL when n_shared = 0
+ *   x         [T][h] act: the shared expert's input, and the gate/up GEMM's rows when
+ *             xp is NULL; may be NULL otherwise
+ *   w13_sh, w2_sh   shared expert weights [2*shared_inter][h] and [h][shared_inter];
+ *             NULL when n_shared = 0
  *   yp        [R_max][h] act out: rows below offsets[E_l] written, others undefined
  *   y_sh      [T/n_ep][h] act out (NULL when n_shared = 0)                           */
-int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* offsets,
-                   const void* w13, const void* w2, const void* x, const void* w13_sh,
-                   const void* w2_sh, void* yp, void* y_sh,
+int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* row_src,
+                   const int32_t* offsets, const void* w13, const void* w2, const void* x,
+                   const void* w13_sh, const void* w2_sh, void* yp, void* y_sh,
                    void* ws, size_t ws_bytes, void* stream);
 
 /* ---- stage 4: combine ------------------------------------------------------------

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import expert_routing_amd as moe
 import oracle
 from oracle.dispatch import permute
 from synth import CONFIGS
@@ -167,6 +168,29 @@ def test_forward_gather_equals_materialised(name):
     assert torch.equal(f["yp"][:R], g["yp"][:R])
     if f["y_sh"] is not None:
         assert torch.equal(f["y_sh"], g["y_sh"])
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "bf16_ragged", "bf16_groups_shared",
+                                  "bf16_cap_pad", "bf16_large_tiles", "bf16_decode"])
+def test_stage_ffn_gather_equals_materialised(name):
+    """moe_expert_ffn without xp (rows read from x through row_src) writes the same yp and
+    y_sh bit for bit as with the materialised xp."""
+    cfg = SMALL[name]
+    print(f"[case] {name}", flush=True)
+    inp = gpu_inputs(cfg)
+    p, b = run_stages(cfg, inp)
+    yp2 = torch.full_like(b["yp"], float("nan"))
+    ysh2 = None if b["y_sh"] is None else torch.full_like(b["y_sh"], float("nan"))
+    moe.moe_expert_ffn(p, None, b["offsets"], inp["w13"], inp["w2"], inp["x"], inp["w13_sh"],
+                       inp["w2_sh"], yp2, ysh2, b["ws"], row_src=b["row_src"])
+    torch.cuda.synchronize()
+    rows = int(b["offsets"][-1].item())
+    assert torch.equal(yp2[:rows], b["yp"][:rows])
+    if ysh2 is not None:
+        assert torch.equal(ysh2, b["y_sh"])
+    with pytest.raises(moe.MoeError):   # no xp and no row_src
+        moe.moe_expert_ffn(p, None, b["offsets"], inp["w13"], inp["w2"], inp["x"],
+                           inp["w13_sh"], inp["w2_sh"], yp2, ysh2, b["ws"])
 
 
 def test_all_pairs_dropped_or_remote_give_zero_rows():
