@@ -120,7 +120,12 @@ def test_null_and_workspace_errors_before_launch():
     assert moe._dispatch(moe.ctypes.byref(p2), None, fake, fake, fake, fake, fake, fake, fake,
                          None, fake, 1 << 30, None) == -1
     # ffn without shared expert must not get shared pointers
-    assert moe._expert_ffn(b, fake, fake, fake, fake, fake, fake, fake, fake, None, fake,
+    assert moe._expert_ffn(b, fake, None, fake, fake, fake, fake, fake, fake, fake, None, fake,
+                           1 << 30, None) == -1
+    # ffn without xp needs row_src and x (the gathered gate/up rows)
+    assert moe._expert_ffn(b, None, None, fake, fake, fake, fake, None, None, fake, None, fake,
+                           1 << 30, None) == -1
+    assert moe._expert_ffn(b, None, fake, fake, fake, fake, None, None, None, fake, None, fake,
                            1 << 30, None) == -1
     assert moe._combine(b, fake, None, fake, None, fake, None) == -1
     assert moe._forward(b, None, fake, 1 << 30, None) == -1
