@@ -619,12 +619,31 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_down_bf16(const FfnSched* __
 // scale block and bytes 16-31 k 32+16h..32+16h+15 of the second (h = lane / 32): exactly the
 // two 16-byte chunks the bf16 body reads in its phases 2c and 2c+1, so the swizzled LDS rows
 // carry over unchanged and MFMA c takes chunks 4c+h and 4c+2+h. Each stage also holds the
-// scale dword (the 4 blocks of the k-step) of every A and B row, fetched by 4-byte DMA;
-// the lanes of half h shift it right by 8h, and op_sel picks byte 0 for MFMA 0 and byte 2
-// for MFMA 1, which is block 2c+h: the hardware takes a row's first block scale from lane
-// r and its second from lane r+32.
+// scale dword (the 4 blocks of the k-step) of every A and B row, fetched by 4-byte DMA.
+// The hardware takes a row's first block scale from lane r and its second from lane r+32,
+// so MFMA c needs block 2c+h in the lanes of half h: byte 0 (c = 0) or byte 2 (c = 1) of the
+// row's dword shifted right by 8h. Those bytes of a wave's (at most four) A fragments are
+// packed into one word per half, likewise for B, and op_sel picks the fragment's byte:
+// four scale registers instead of one per fragment, which keeps the 256-row tile's
+// register file from spilling.
 typedef int intx8 __attribute__((ext_vector_type(8)));
 typedef int intx4 __attribute__((ext_vector_type(4)));
+
+// Scaled MFMA 32x32x64 whose scale bytes op_sel picks out of packed words (oa, ob in 0..3:
+// constants after unrolling, so the switch folds to one instruction).
+__device__ __forceinline__ floatx16 mfma_mx(intx8 a, intx8 b, floatx16 c, int sa, int oa, int sb,
+                                            int ob) {
+#define MX_CASE(X, Y) \
+  case X * 4 + Y: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, X, sa, Y, sb);
+  switch (oa * 4 + ob) {
+    MX_CASE(0, 0) MX_CASE(0, 1) MX_CASE(0, 2) MX_CASE(0, 3)
+    MX_CASE(1, 0) MX_CASE(1, 1) MX_CASE(1, 2) MX_CASE(1, 3)
+    MX_CASE(2, 0) MX_CASE(2, 1) MX_CASE(2, 2) MX_CASE(2, 3)
+    MX_CASE(3, 0) MX_CASE(3, 1) MX_CASE(3, 2) MX_CASE(3, 3)
+    default: return c;
+  }
+#undef MX_CASE
+}
 
 template <int BM, int BN, int NW>
 struct Fp8Shape {
@@ -833,8 +852,13 @@ __device__ __forceinline__ void gemm_mx_body(const FfnGroup& fg, int m0, int n0,
       br = wn * WTN + j * 32;
     brow[j] = br + (lane & 31);
   }
-  intx8 fa[2][TM], fb[2][TN];
-  uint32_t sa[TM], sb[TN];
+  // B fragments of both halves are live together (the second half's are read after the
+  // first MFMA); an A fragment is re-read for the second half right after its last use in
+  // the first, so only one set of A fragments is live (the register file also holds the
+  // accumulators).
+  intx8 fa[TM], fb[2][TN];
+  uint32_t pa[2], pb[2];   // per half: byte i = the scale of fragment i's rows
+  static_assert(TM <= 4 && TN <= 4, "op_sel addresses four fragments");
   auto frag = [&](const uint4* base, int r, int c) __attribute__((always_inline)) {
     const int sw = row_swz(r);
     const intx4 lo = __builtin_bit_cast(intx4, base[r * 8 + (c ^ sw)]);
@@ -842,20 +866,35 @@ __device__ __forceinline__ void gemm_mx_body(const FfnGroup& fg, int m0, int n0,
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
   // fragments of MFMA `half` (0 or 1) of the k-step in `stage`
-  auto read_frags = [&](int set, int stage, int half) __attribute__((always_inline)) {
+  auto read_b = [&](int set, int stage, int half) __attribute__((always_inline)) {
     const int c = 4 * half + (lane >> 5);
 #pragma unroll
     for (int j = 0; j < TN; ++j) fb[set][j] = frag(Bs + stage * B_ST, brow[j], c);
+  };
+  auto read_a = [&](int i, int stage, int half) __attribute__((always_inline)) {
+    fa[i] = frag(As + stage * A_ST, arow[i], 4 * half + (lane >> 5));
+  };
+  auto read_frags = [&](int stage) __attribute__((always_inline)) {
+    read_b(0, stage, 0);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) fa[set][i] = frag(As + stage * A_ST, arow[i], c);
+    for (int i = 0; i < TM; ++i) read_a(i, stage, 0);
   };
   auto read_scales = [&](int stage) __attribute__((always_inline)) {
     const uint32_t* ss = Ss + stage * SH::S_ST;
     const int sh = 8 * (lane >> 5);
+    pa[0] = pa[1] = pb[0] = pb[1] = 0;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) sa[i] = ss[arow[i]] >> sh;
+    for (int i = 0; i < TM; ++i) {
+      const uint32_t d = ss[arow[i]] >> sh;
+      pa[0] |= (d & 0xffu) << (8 * i);
+      pa[1] |= ((d >> 16) & 0xffu) << (8 * i);
+    }
 #pragma unroll
-    for (int j = 0; j < TN; ++j) sb[j] = ss[SH::BMS + brow[j]] >> sh;
+    for (int j = 0; j < TN; ++j) {
+      const uint32_t d = ss[SH::BMS + brow[j]] >> sh;
+      pb[0] |= (d & 0xffu) << (8 * j);
+      pb[1] |= ((d >> 16) & 0xffu) << (8 * j);
+    }
   };
 
   // One k-step: two halves of NMF scaled MFMAs; the second half's fragments are read
@@ -867,17 +906,16 @@ __device__ __forceinline__ void gemm_mx_body(const FfnGroup& fg, int m0, int n0,
 #pragma unroll
       for (int t = 0; t < NMF; ++t) {
         const int i = t / TN, j = t % TN;
-        if (c == 0)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fb[0][j], fa[0][i], acc[i][j], 0, 0, 0, (int)sb[j], 0, (int)sa[i]);
-        else
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fb[1][j], fa[1][i], acc[i][j], 0, 0, 2, (int)sb[j], 2, (int)sa[i]);
+        acc[i][j] = mfma_mx(fb[c][j], fa[i], acc[i][j], (int)pb[c], j, (int)pa[c], i);
         const int slot = c * NMF + t;
         if (dma && slot >= 1 && slot - 1 < LPS) issue_one(next_step, dma_stage, slot - 1);
-        if (t == 0 && c == 0) {
+        if (c == 0 && t == 0) {
           __builtin_amdgcn_sched_barrier(0);
-          read_frags(1, stage, 1);
+          read_b(1, stage, 1);
+        }
+        if (c == 0 && j == TN - 1) {   // last use of fa[i] in this half
+          __builtin_amdgcn_sched_barrier(0);
+          read_a(i, stage, 1);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -897,14 +935,14 @@ __device__ __forceinline__ void gemm_mx_body(const FfnGroup& fg, int m0, int n0,
     if (nk >= NS - 1) wait_vmcnt<LPS * (NS - 2)>();
     else wait_vmcnt<0>();
     lds_barrier();
-    read_frags(0, 0, 0);
+    read_frags(0);
     read_scales(0);
     int kt = 0;
     for (; kt + NS - 1 < nk; ++kt) {
       kstep(kt % NS, true, kt + NS - 1, (kt + NS - 1) % NS);
       wait_vmcnt<LPS * (NS - 2)>();
       lds_barrier();
-      read_frags(0, (kt + 1) % NS, 0);
+      read_frags((kt + 1) % NS);
       read_scales((kt + 1) % NS);
     }
     for (; kt + 1 < nk; ++kt) {
@@ -914,7 +952,7 @@ __device__ __forceinline__ void gemm_mx_body(const FfnGroup& fg, int m0, int n0,
       else if (NS > 2 && after >= 1) wait_vmcnt<LPS * (NS > 2 ? 1 : 0)>();
       else wait_vmcnt<0>();
       lds_barrier();
-      read_frags(0, (kt + 1) % NS, 0);
+      read_frags((kt + 1) % NS);
       read_scales((kt + 1) % NS);
     }
     kstep((nk - 1) % NS, false, 0, 0);
@@ -1128,12 +1166,12 @@ bool launch_mx_gemm(bool gated, const FfnSched* sc, int h, int64_t ub, hipStream
   return hipGetLastError() == hipSuccess;
 }
 
-// MX-FP8 tiles: the 128- and 32-row shapes (a 256-row tile's two fragment sets of 32-byte
-// operands do not fit the register file beside its accumulators).
-Tiles mx_tiles(Tiles k) { return k == Tiles::Large ? Tiles::Medium : k; }
+// MX-FP8 tiles: the same shapes as bf16.
+Tiles mx_tiles(Tiles k) { return k; }
 
 bool launch_mx(Tiles k, bool gated, const FfnSched* sc, int h, int64_t ub, hipStream_t st) {
   switch (mx_tiles(k)) {
+    case Tiles::Large: return launch_mx_gemm<256, 256, 2, 2, false>(gated, sc, h, ub, st);
     case Tiles::Medium: return launch_mx_gemm<128, 256, 2, 2, true>(gated, sc, h, ub, st);
     default: return launch_mx_gemm<32, 256, 1, 4, true>(gated, sc, h, ub, st);
   }
