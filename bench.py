@@ -94,11 +94,12 @@ def stage_of(kernel_name):
     return None
 
 
-def summarize_traffic(fetch_csv, write_csv, workload, calls):
+def summarize_traffic(fetch_csv, write_csv, workload):
     """HBM bytes per layer call of every stage from two rocprofv3 --pmc runs of
     `bench.py --calibrate-copy --no-flush` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch),
     each scaled by what the same counter reads for the CALIB_BYTES device copy in that run.
-    `calls`: layer calls in each run (warm-up + timed). Writes profiles/traffic_<w>.json."""
+    Layer calls are counted as the combine kernel's launches (one per call). Writes
+    profiles/traffic_<workload>.json."""
     import csv
 
     def per_stage(path, counter):
@@ -112,17 +113,20 @@ def summarize_traffic(fetch_csv, write_csv, workload, calls):
         first = min(d for d, n, _ in rows if stage_of(n) is not None)
         copies = [v for d, n, v in rows if "copyBuffer" in n and d < first]
         tot, kern = {}, {}
+        calls = 0
         for _, n, v in rows:
             s = stage_of(n)
             if s is None:
                 continue
+            calls += s == "combine"
             tot[s] = tot.get(s, 0.0) + v
             kern.setdefault(n.split("(")[0], []).append(v)
-        return ({s: v / calls for s, v in tot.items()}, copies[-1],
-                {k: sum(v) / len(v) for k, v in kern.items()})
+        return ({s: v / max(calls, 1) for s, v in tot.items()}, copies[-1],
+                {k: sum(v) / len(v) for k, v in kern.items()}, calls)
 
-    f, fcopy, fk = per_stage(fetch_csv, "FETCH_SIZE")
-    w, wcopy, wk = per_stage(write_csv, "WRITE_SIZE")
+    f, fcopy, fk, calls = per_stage(fetch_csv, "FETCH_SIZE")
+    w, wcopy, wk, wcalls = per_stage(write_csv, "WRITE_SIZE")
+    assert calls == wcalls and calls > 0, (calls, wcalls)
     fs, ws_ = fcopy / CALIB_BYTES, wcopy / CALIB_BYTES
     out = {
         "workload": workload,
@@ -486,8 +490,8 @@ def main():
                          "gate/up GEMM reads x through row_src)")
     args = ap.parse_args()
     if args.summarize_traffic:
-        summarize_traffic(*args.summarize_traffic, workload=args.workload,
-                          calls=args.warmup + args.steps)
+        summarize_traffic(*args.summarize_traffic,
+                          workload=args.workload + ("_mxfp8" if args.dtype == "mxfp8" else ""))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
