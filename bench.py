@@ -87,9 +87,17 @@ def load_traffic(workload):
     return t.get("stages")
 
 
+def kernel_base_name(kernel_name):
+    """The kernel's own name: return type, namespaces and argument list stripped."""
+    n = kernel_name[5:] if kernel_name.startswith("void ") else kernel_name
+    n = n.replace("moe::(anonymous namespace)::", "").replace("moe::", "")
+    return n.split("(", 1)[0]
+
+
 def stage_of(kernel_name):
+    n = kernel_base_name(kernel_name)
     for prefix, stage in STAGE_OF:
-        if kernel_name.startswith(prefix):
+        if n.startswith(prefix):
             return stage
     return None
 
@@ -120,7 +128,7 @@ def summarize_traffic(fetch_csv, write_csv, workload):
                 continue
             calls += s == "combine"
             tot[s] = tot.get(s, 0.0) + v
-            kern.setdefault(n.split("(")[0], []).append(v)
+            kern.setdefault(kernel_base_name(n), []).append(v)
         return ({s: v / max(calls, 1) for s, v in tot.items()}, copies[-1],
                 {k: sum(v) / len(v) for k, v in kern.items()}, calls)
 
