@@ -84,6 +84,14 @@ __device__ __forceinline__ void locate(const FfnSched* sc, bool first, int L, Ti
     t.m_tile = local % mt;
     t.n_tile = local / mt;
     t.tall = 0;
+    if (sc->tall_split[gi] == 0 && t.m_tile == mt - 1) {
+      // short last m-tile: a remainder of 65..192 rows rounded up to 128 or 192 rows (a
+      // 64-row tile streams the same weight bytes per k-step as a full one and was measured
+      // no faster, so smaller remainders keep the full tile)
+      const int rem = sc->g[lo].rows - t.m_tile * sc->bm[gi];
+      const int q64 = (rem + 63) >> 6;
+      t.tall = q64 >= 2 && q64 <= 3 && rem < sc->bm[gi] ? q64 : 0;
+    }
   }
 }
 
@@ -110,7 +118,8 @@ __device__ __forceinline__ bool find_tile(const FfnSched* sc, bool first, TileRe
     t.tid_x = xcd * sc->cu_per_xcd + p % q.rem;
   }
   locate(sc, first, L, t);
-  if (t.tall && t.nslice > 1) {   // tall parts are not split: slice 0 takes all of K
+  // tall parts are not split (slice 0 takes all of K); short last tiles are
+  if (t.tall && t.nslice > 1 && sc->tall_split[first ? 0 : 1] != 0) {
     if (t.slice > 0) return false;
     t.nslice = 1;
     t.piece = -1;
@@ -134,6 +143,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// The row -> token map read as global memory (global_load rather than flat loads, which
+// would also count against the LDS wait counter).
+typedef const __attribute__((address_space(1))) int32_t global_i32;
+__device__ __forceinline__ global_i32* as_global(const int32_t* p) { return (global_i32*)p; }
 
 // Slot of a 16-byte chunk in a 128-byte LDS row: chunk c of row r sits at
 // c ^ row_swz(r). Any 8 aligned consecutive rows (one 128-byte bank sweep) and any 16
@@ -300,7 +314,12 @@ __device__ __forceinline__ void store_tile_parts(const float* __restrict__ part,
 // staging) one k-step ahead of the MFMAs. Every DMA request covers whole 128-byte row
 // segments (half-line requests roughly halve what L2 can deliver per CU). The MFMA takes
 // the weight fragment first, so a lane's accumulators hold 4 consecutive output columns.
-template <int BM, int BN, int WM, int WN, bool GATED, bool GATHER = false, int NS = 2>
+// VARIANT only tells apart instantiations that are otherwise identical but reached from
+// different tile kinds (an expert's short last tile in the 256-row kernels and the 128-row
+// kernels' full tile): the host compilation pass rejects a second use of the same
+// specialisation of this body from another kernel.
+template <int BM, int BN, int WM, int WN, bool GATED, bool GATHER = false, int NS = 2,
+          int VARIANT = 0>
 __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n0, int h,
                                                uint4* __restrict__ smem, int slice,
                                                int nslice, float* __restrict__ part,
@@ -352,8 +371,7 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
   uint32_t a_off[GATHER ? AI : 1];
   if constexpr (GATHER) {
     // all AI indices in flight at once (clamped, then masked), as global-memory loads
-    const __attribute__((address_space(1))) int32_t* gidx =
-        (const __attribute__((address_space(1))) int32_t*)fg.gidx;
+    const global_i32* gidx = as_global(fg.gidx);
     int src[AI];
 #pragma unroll
     for (int x = 0; x < AI; ++x) {
@@ -544,6 +562,21 @@ constexpr int tall_split() { return WM > 1 ? 2 : 1; }
 template <int BM>
 constexpr int kernel_stages() { return BM >= 256 ? 2 : (BM >= 128 ? 3 : 4); }
 
+// An expert's short last m-tile in a 256-row-tile GEMM: 64 * q rows (q = 2, 3) by BN, or
+// one k-slice of it (the partial sums use a prefix of the tile's slot). The 128-row body
+// gets a third stage (it streams more bytes per MFMA).
+template <int BN, int WM, int WN, bool GATED, bool GATHER>
+__device__ __forceinline__ void bf16_short(int q, const FfnGroup& fg, int m0, int n0, int h,
+                                           uint4* __restrict__ smem, int slice, int nslice,
+                                           float* part, size_t pstride, int* arrive) {
+  if (q == 2)
+    gemm_bf16_body<128, BN, WM, WN, GATED, GATHER, 3, 1>(fg, m0, n0, h, smem, slice, nslice,
+                                                         part, pstride, arrive);
+  else
+    gemm_bf16_body<192, BN, WM, WN, GATED, GATHER, 2>(fg, m0, n0, h, smem, slice, nslice, part,
+                                                      pstride, arrive);
+}
+
 template <int BM, int BN, int WM, int WN, bool GATED, bool TALL>
 __device__ __forceinline__ void gemm_bf16_tile(const FfnSched* __restrict__ sc, int h,
                                                float* __restrict__ part,
@@ -571,6 +604,17 @@ __device__ __forceinline__ void gemm_bf16_tile(const FfnSched* __restrict__ sc, 
   int* ar = arrive + (GATED ? 0 : kArriveSlots) + (t.tid_x >= 0 ? t.tid_x : 0);
   const size_t ps = (size_t)t.pstride * BM * BN;
   const int n0t = n0 + (t.tall - 1) * (BNO / TS);
+  if constexpr (!TALL) {
+    if (t.tall) {   // an expert's short last m-tile (128 or 192 rows)
+      if (GATED && fg.gidx)
+        bf16_short<BN, WM, WN, GATED, GATED>(t.tall, fg, m0, n0, h, smem, t.slice, t.nslice, pt,
+                                             ps, ar);
+      else
+        bf16_short<BN, WM, WN, GATED, false>(t.tall, fg, m0, n0, h, smem, t.slice, t.nslice, pt,
+                                             ps, ar);
+      return;
+    }
+  }
   if (GATED && fg.gidx) {   // gate/up reading x through the row -> token map
     if (TALL && t.tall)
       gemm_bf16_body<TALL ? BMT : BM, TALL ? BNT : BN, WM, WN, GATED, GATED, NS>(
@@ -593,7 +637,9 @@ constexpr size_t tile_lds_bytes() {
   constexpr int NS = kernel_stages<BM>();
   return TALL ? cmax<bf16_lds_bytes<BM, BN, GATED, NS>(),
                      bf16_lds_bytes<BM + 32 * WM, BN / tall_split<WM, WN>(), GATED, NS>()>()
-              : bf16_lds_bytes<BM, BN, GATED, NS>();
+              : cmax<bf16_lds_bytes<BM, BN, GATED, NS>(),
+                     cmax<bf16_lds_bytes<128, BN, GATED, 3>(),
+                          bf16_lds_bytes<192, BN, GATED, 2>()>()>();
 }
 
 template <int BM, int BN, int WM, int WN, bool TALL>
@@ -760,8 +806,7 @@ __device__ __forceinline__ void gemm_mx_body(const FfnGroup& fg, int m0, int n0,
   const uint32_t b_lane_up = GATED ? b_lane + (uint32_t)I * Kd : b_lane;
   const uint32_t x_stride = (uint32_t)(8 * NW) * Kd;
   constexpr int BH = GATED ? BI / 2 : BI;
-  const __attribute__((address_space(1))) int32_t* gidx =
-      (const __attribute__((address_space(1))) int32_t*)fg.gidx;
+  const global_i32* gidx = as_global(fg.gidx);
   uint32_t a_off[GATHER ? AI : 1];
   if constexpr (GATHER) {
     int src[AI];
@@ -977,7 +1022,15 @@ constexpr size_t mx_tile_lds_bytes() {
   constexpr int NS = fp8_stages<BM>();
   return TALL ? cmax<mx_lds_bytes<BM, BN, WM, WN, GATED, NS>(),
                      mx_lds_bytes<BM + 32 * WM, BN / tall_split<WM, WN>(), WM, WN, GATED, NS>()>()
-              : mx_lds_bytes<BM, BN, WM, WN, GATED, NS>();
+              : cmax<mx_lds_bytes<BM, BN, WM, WN, GATED, NS>(),
+                     mx_lds_bytes<192, BN, WM, WN, GATED, 2>()>();
+}
+
+template <int BN, int WM, int WN, bool GATED, bool GATHER>
+__device__ __forceinline__ void mx_short(int q, const FfnGroup& fg, int m0, int n0, int h,
+                                         uint4* __restrict__ smem) {
+  if (q == 2) gemm_mx_body<128, BN, WM, WN, GATED, GATHER, 2>(fg, m0, n0, h, smem);
+  else gemm_mx_body<192, BN, WM, WN, GATED, GATHER, 2>(fg, m0, n0, h, smem);
 }
 
 template <int BM, int BN, int WM, int WN, bool GATED, bool TALL>
@@ -995,6 +1048,13 @@ __device__ __forceinline__ void gemm_mx_tile(const FfnSched* __restrict__ sc, in
   const FfnGroup& fg = sc->g[t.g];
   const int m0 = t.m_tile * BM, n0 = t.n_tile * BNO;
   const int n0t = n0 + (t.tall - 1) * (BNO / TS);
+  if constexpr (!TALL) {
+    if (t.tall) {   // an expert's short last m-tile (128 or 192 rows)
+      if (GATED && fg.gidx) mx_short<BN, WM, WN, GATED, true>(t.tall, fg, m0, n0, h, smem);
+      else mx_short<BN, WM, WN, GATED, false>(t.tall, fg, m0, n0, h, smem);
+      return;
+    }
+  }
   if (GATED && fg.gidx) {
     if (TALL && t.tall)
       gemm_mx_body<TALL ? BMT : BM, TALL ? BNT : BN, WM, WN, GATED, GATED, NS>(fg, m0, n0t, h,
@@ -1118,7 +1178,9 @@ struct Tiling {
 };
 Tiling tiling(Tiles k) {
   switch (k) {
-    case Tiles::Large: return {256, 0, 1};   // its tall parts would cost as much as tiles
+    // 256-row tiles: tall parts would cost as much as tiles; an expert's last m-tile is a
+    // short one instead when its remainder is 65..192 rows (tall_split 0)
+    case Tiles::Large: return {256, 0, 0};
     case Tiles::Medium: return {128, 64, 2};
     default: return {32, 32, 1};
   }

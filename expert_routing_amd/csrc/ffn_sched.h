@@ -39,10 +39,11 @@ struct FfnSched {
   int n_groups;
   int total1;
   int total2;
-  int tall_split[2];
+  int tall_split[2];  // 0: no tall tiles; an expert's last m-tile is a short one instead
+                      // (64, 128 or 192 rows when its remainder fits)
+  int bm[2];          // rows of a full m-tile of each GEMM
   int cu_per_xcd;   // CUs of one XCD (one round of blocks there)
   int split_max;    // 1: no split-K; else the most k-slices a tile may take
-  int pad2_;
   int start1[G_PAD];
   int start2[G_PAD];
   FfnGroup g[G_MAX];
@@ -203,6 +204,8 @@ __device__ inline void ffn_build_sched(const FfnPrepArgs& a, const int32_t* offs
     a.sc->n_groups = G;
     a.sc->tall_split[0] = a.tall_split1;
     a.sc->tall_split[1] = a.tall_split2;
+    a.sc->bm[0] = a.BM1;
+    a.sc->bm[1] = a.BM2;
     a.sc->cu_per_xcd = a.cu_per_xcd;
     a.sc->split_max = a.split_max;
     a.sc->total1 = tot1;

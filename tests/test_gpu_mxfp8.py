@@ -12,7 +12,8 @@ oracle's fp8 module, through the C ABI.
     fp32 accumulation of exact fp8 products, one bf16 rounding, and, where the GPU's fp32
     gated product may fall on the other side of an E4M3 rounding boundary than the fp64
     one (or its block exponent may differ), the change that one code step makes; the
-    layer output y end to end at the bf16 tolerance.
+    layer output y end to end (the oracle's own routing) within those bounds carried
+    through combine, and at the bf16 mean tolerance.
 """
 import numpy as np
 import pytest
@@ -22,7 +23,8 @@ import expert_routing_amd as moe
 import oracle
 from oracle import fp8 as F
 from synth import CONFIGS
-from gpu_cases import TOL, cpu_inputs, gpu_inputs, np_, rel_errors, routing_mismatches
+from gpu_cases import (TOL, W_RTOL, cpu_inputs, gpu_inputs, np_, rel_errors,
+                       routing_mismatches)
 
 pytestmark = pytest.mark.gpu
 
@@ -104,6 +106,8 @@ MX_CASES = {
     "mx_ragged": BASE.with_(T=300, h=256, E=8, K=2, inter=256),
     # capacity drops, three experts per token, ragged rows
     "mx_cap": BASE.with_(T=333, h=384, E=6, K=3, inter=384, capacity_factor=1.0),
+    # ~425 rows per expert: 256-row tiles and short last tiles of 192 rows
+    "mx_short_last": BASE.with_(T=850, h=256, E=4, K=2, inter=256),
     # ~512 rows per expert (the large-tile regime of the bf16 path)
     "mx_big": BASE.with_(T=1024, h=512, E=4, K=2, inter=512),
     # 32-row tiles, a shared expert, remote experts over 4 virtual ranks, group limit
@@ -238,6 +242,7 @@ def test_mx_forward_parity(name):
     xq, xs = F.mx_quantize_rows(inp_c["x"].double().numpy())
     xd = F.mx_dequantize(xq, xs)
     yp = np_(b["yp"])
+    yp_bound = np.zeros_like(yp)
     n_ambig = 0
     worst = 0.0
     for el in range(cfg.E_local):
@@ -248,6 +253,7 @@ def test_mx_forward_parity(name):
         w13d = F.mx_dequantize(q["w13"][el], q["w13_scale"][el])
         w2d = F.mx_dequantize(q["w2"][el], q["w2_scale"][el])
         y, bound, na = expert_rows_bound(xd[toks], w13d, w2d, cfg.h)
+        yp_bound[r0:r1] = bound
         n_ambig += na
         err = np.abs(yp[r0:r1] - y)
         worst = max(worst, float((err / bound).max()))
@@ -261,20 +267,39 @@ def test_mx_forward_parity(name):
         w13d = F.mx_dequantize(q["w13_sh"], q["w13_sh_scale"])
         w2d = F.mx_dequantize(q["w2_sh"], q["w2_sh_scale"])
         y, bound, na = expert_rows_bound(xd[t0:t0 + tpr], w13d, w2d, cfg.h)
+        ysh_bound = bound
         n_ambig += na
         err = np.abs(np_(b["y_sh"]) - y)
         worst = max(worst, float((err / bound).max()))
         assert (err <= bound).all(), "y_sh beyond the bound"
     print(f"[parity] {name}: worst err/bound {worst:.3f}, H elements near a code "
           f"boundary {n_ambig}", flush=True)
-    # end to end: the oracle's MX-FP8 layer on its own routing, at the bf16 tolerance
+    # end to end: the oracle's MX-FP8 layer on its own routing (the same layout off near-
+    # ties). A code step of H moves a row of yp by up to its bound above, which can exceed
+    # the flat bf16 tolerance on rows of small norm, so y is held to those bounds carried
+    # through combine (weights within W_RTOL, one more bf16 rounding), and on average to the
+    # bf16 mean tolerance.
     if near:
         pytest.skip(f"near-tie tokens {near}: end-to-end compare not defined")
     y_ref = mx_layer_reference(cfg, inp_c, rr, q)
-    mx, mean, zexact = rel_errors(np_(b["y"]), y_ref)
-    tmax, tmean = TOL["bf16"]
-    print(f"[parity] {name}: y max_rel {mx:.3e} mean_rel {mean:.3e}", flush=True)
-    assert mx <= tmax and mean <= tmean and zexact, (mx, mean)
+    y = np_(b["y"])
+    wabs = np.abs(rr.weights)
+    dest = d.dest_row
+    y_bound = 2.0 ** -8 * np.abs(y_ref) + 1e-30
+    yp_abs = np.abs(yp)
+    for k in range(cfg.K):
+        live = dest[:, k] >= 0
+        rows = dest[live, k]
+        y_bound[live] += wabs[live, k, None] * (yp_bound[rows] + W_RTOL * yp_abs[rows])
+    if cfg.n_shared:
+        y_bound[t0:t0 + tpr] += ysh_bound
+    err = np.abs(y - y_ref)
+    bad = np.argwhere(err > y_bound)
+    mx, mean, zexact = rel_errors(y, y_ref)
+    print(f"[parity] {name}: y max_rel {mx:.3e} mean_rel {mean:.3e}, worst err/bound "
+          f"{float((err / y_bound).max()):.3f}", flush=True)
+    assert len(bad) == 0, (f"{len(bad)} y elements beyond the bound; first {bad[0].tolist()}")
+    assert mean <= TOL["bf16"][1] and zexact, (mx, mean)
 
 
 def mx_layer_reference(cfg, inp_c, rr, q):

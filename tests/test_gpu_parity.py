@@ -37,6 +37,10 @@ SMALL = {
     "bf16_large_tiles": BASE.with_(T=1100, h=192, E=4, K=2, inter=384),
     # 256-row tiles: two experts end in a short remainder, two do not
     "bf16_tall_large": BASE.with_(T=1080, h=128, E=4, K=2, inter=192),
+    # 256-row tiles whose experts end in 65..192-row remainders: short last tiles of 128 and
+    # 192 rows (gate/up and down), some of them split along K in the last round
+    "bf16_short_last": BASE.with_(T=850, h=128, E=4, K=2, inter=192),
+    "bf16_short_last_q2": BASE.with_(T=720, h=192, E=4, K=2, inter=128),
     # 256-row tiles under skewed routing, including an expert of exactly 64 rows
     "bf16_large_skew": CONFIGS["skew_nodrop"].with_(T=2048, h=128, E=8, K=2, inter=128),
     "bf16_decode": CONFIGS["dsv3_decode"].with_(T=8, h=256, E=64, inter=128),
