@@ -319,7 +319,7 @@ __device__ __forceinline__ void store_tile_parts(const float* __restrict__ part,
 // kernels' full tile): the host compilation pass rejects a second use of the same
 // specialisation of this body from another kernel.
 template <int BM, int BN, int WM, int WN, bool GATED, bool GATHER = false, int NS = 2,
-          int VARIANT = 0>
+          int VARIANT = 0, int NB = NS>
 __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n0, int h,
                                                uint4* __restrict__ smem, int slice,
                                                int nslice, float* __restrict__ part,
@@ -336,6 +336,7 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
   constexpr int A_ST = BM * 8, B_ST = BN * 8;       // uint4 per stage
   constexpr int NMF = TM * TN;                      // MFMAs per k16 phase
   static_assert(NS >= 2 && NS <= 4 && LPS * (NS - 2) < 64, "LDS stages");
+  static_assert(NB == NS || (NS == 2 && NB == 3), "B stages: as A, or 3 with 2 A stages");
   uint4* As = smem;                                 // [NS][BM rows][8 chunks]
   uint4* Bs = smem + NS * A_ST;                     // [NS][BN rows][8 chunks]
 
@@ -392,6 +393,7 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
   const int nk = __builtin_amdgcn_readfirstlane((slice + 1) * (Kd / 64) / nslice) - kb;
   auto issue_one = [&](int step, int stage, int x) __attribute__((always_inline)) {
     const uint32_t soff = (uint32_t)(kb + step) * 128;
+    if (NB != NS && x >= AI) stage = step % NB;
     if (x < AI) {
       if constexpr (GATHER)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -431,9 +433,9 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
     brow[j] = br + (lane & 31);
   }
   bf16x8_t fa[2][TM], fb[2][TN];
-  auto read_frags = [&](int set, int stage, int kk) __attribute__((always_inline)) {
+  auto read_frags = [&](int set, int stage, int kk, int bstage) __attribute__((always_inline)) {
     const uint4* as = As + stage * A_ST;
-    const uint4* bs = Bs + stage * B_ST;
+    const uint4* bs = Bs + bstage * B_ST;
     const int c = kk * 2 + (lane >> 5);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
@@ -448,8 +450,9 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
   // fragments, then its other MFMAs. With `dma`, the next k-step's DMA rides along one
   // instruction every kDmaStride MFMAs: a burst of VMEM issues would block the wave, and
   // one per MFMA (measured) outruns what the address units accept from four waves.
-  auto kstep = [&](int stage, bool dma, int next_step, int dma_stage)
-                   __attribute__((always_inline)) {
+  // dma: A of next_step (and, with NB == NS, its B); dmab: B of bnext (NB != NS only)
+  auto kstep = [&](int stage, bool dma, int next_step, int dma_stage, int bstage, bool dmab,
+                   int bnext) __attribute__((always_inline)) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int cur = kk & 1;
@@ -458,22 +461,64 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
         acc[t / TN][t % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             fb[cur][t % TN], fa[cur][t / TN], acc[t / TN][t % TN], 0, 0, 0);
         const int slot = kk * NMF + t;            // MFMA index within the k-step
-        if (dma && slot >= 1 && (slot - 1) % kDmaStride == 0 && (slot - 1) / kDmaStride < LPS)
-          issue_one(next_step, dma_stage, (slot - 1) / kDmaStride);
+        if (slot >= 1 && (slot - 1) % kDmaStride == 0 && (slot - 1) / kDmaStride < LPS) {
+          const int xx = (slot - 1) / kDmaStride;
+          if (NB == NS || xx < AI) {
+            if (dma) issue_one(next_step, dma_stage, xx);
+          } else if (dmab) {
+            issue_one(bnext, 0, xx);
+          }
+        }
         if (t == 0 && kk < 3) {
           __builtin_amdgcn_sched_barrier(0);
-          read_frags(cur ^ 1, stage, kk + 1);
+          read_frags(cur ^ 1, stage, kk + 1, bstage);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (dma) {   // instructions left over when the k-step has too few MFMAs
+    // instructions left over when the k-step has too few MFMAs
 #pragma unroll
-      for (int x = (4 * NMF - 2) / kDmaStride + 1; x < LPS; ++x)
-        issue_one(next_step, dma_stage, x);
+    for (int x = (4 * NMF - 2) / kDmaStride + 1; x < LPS; ++x) {
+      if (NB == NS || x < AI) {
+        if (dma) issue_one(next_step, dma_stage, x);
+      } else if (dmab) {
+        issue_one(bnext, 0, x);
+      }
     }
   };
 
+  if constexpr (NB != NS) {
+    // two A stages, three B stages: during k-step kt the DMA fetches A of kt + 1 and B of
+    // kt + 2 (A instructions first), so the weights have two k-steps of lead time
+    if (nk > 0) {
+#pragma unroll
+      for (int x = 0; x < LPS; ++x) issue_one(0, 0, x);             // A0, B0
+      if (nk > 1) {
+#pragma unroll
+        for (int x = AI; x < LPS; ++x) issue_one(1, 0, x);          // B1
+        wait_vmcnt<BI>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      lds_barrier();
+      read_frags(0, 0, 0, 0);
+      int kt = 0;
+      for (; kt + 2 < nk; ++kt) {   // A of kt + 1, B of kt + 2
+        kstep(kt % NS, true, kt + 1, (kt + 1) % NS, kt % NB, true, kt + 2);
+        wait_vmcnt<BI>();
+        lds_barrier();
+        read_frags(0, (kt + 1) % NS, 0, (kt + 1) % NB);
+      }
+      if (kt + 1 < nk) {            // A of the last k-step
+        kstep(kt % NS, true, kt + 1, (kt + 1) % NS, kt % NB, false, 0);
+        wait_vmcnt<0>();
+        lds_barrier();
+        read_frags(0, (kt + 1) % NS, 0, (kt + 1) % NB);
+        ++kt;
+      }
+      kstep(kt % NS, false, 0, 0, kt % NB, false, 0);
+    }
+  } else {
   // NS stages: k-step kt lives in stage kt % NS; up to NS - 1 k-steps are in flight.
   if (nk > 0) {
 #pragma unroll
@@ -484,29 +529,30 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
   if (nk >= NS - 1) wait_vmcnt<LPS * (NS - 2)>();   // k-step 0 has landed
   else wait_vmcnt<0>();
   lds_barrier();
-  read_frags(0, 0, 0);
+  read_frags(0, 0, 0, 0);
   int kt = 0;
   for (; kt + NS - 1 < nk; ++kt) {
     // the DMA of k-step kt + NS - 1 refills the stage k-step kt - 1 used: every wave
     // passed the barrier after its last reads there
-    kstep(kt % NS, true, kt + NS - 1, (kt + NS - 1) % NS);
+    kstep(kt % NS, true, kt + NS - 1, (kt + NS - 1) % NS, kt % NS, true, kt + NS - 1);
     // k-step kt+1 has landed (this wave's DMA; the NS - 2 after it may still be in
     // flight) and every wave is past its reads of stage kt % NS; the barrier publishes
     // the DMA of all waves
     wait_vmcnt<LPS * (NS - 2)>();
     lds_barrier();
-    read_frags(0, (kt + 1) % NS, 0);
+    read_frags(0, (kt + 1) % NS, 0, (kt + 1) % NS);
   }
   for (; kt + 1 < nk; ++kt) {   // the last NS - 2 k-steps: nothing left to fetch
-    kstep(kt % NS, false, 0, 0);
+    kstep(kt % NS, false, 0, 0, kt % NS, false, 0);
     const int after = nk - kt - 2;   // k-steps still in flight behind k-step kt+1
     if (NS > 3 && after >= 2) wait_vmcnt<LPS * (NS > 3 ? 2 : 0)>();
     else if (NS > 2 && after >= 1) wait_vmcnt<LPS * (NS > 2 ? 1 : 0)>();
     else wait_vmcnt<0>();
     lds_barrier();
-    read_frags(0, (kt + 1) % NS, 0);
+    read_frags(0, (kt + 1) % NS, 0, (kt + 1) % NS);
   }
-  kstep((nk - 1) % NS, false, 0, 0);
+  kstep((nk - 1) % NS, false, 0, 0, (nk - 1) % NS, false, 0);
+  }
   }
   __syncthreads();
 
@@ -540,9 +586,9 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
   store_tile<BM, BN, WM, WN, GATED>(acc, fg, m0, n0, h, smem);
 }
 
-template <int BM, int BN, bool GATED, int NS = 2>
+template <int BM, int BN, bool GATED, int NS = 2, int NB = NS>
 constexpr size_t bf16_lds_bytes() {
-  constexpr size_t ops = NS * (size_t)(BM + BN) * 8 * 16;
+  constexpr size_t ops = (NS * (size_t)BM + NB * (size_t)BN) * 8 * 16;
   constexpr size_t stg = (size_t)BM * ((GATED ? BN / 2 : BN) * 2 + 16);
   return ops > stg ? ops : stg;
 }
@@ -577,7 +623,7 @@ __device__ __forceinline__ void bf16_short(int q, const FfnGroup& fg, int m0, in
                                                       pstride, arrive);
 }
 
-template <int BM, int BN, int WM, int WN, bool GATED, bool TALL>
+template <int BM, int BN, int WM, int WN, bool GATED, bool TALL, bool DEEP = false>
 __device__ __forceinline__ void gemm_bf16_tile(const FfnSched* __restrict__ sc, int h,
                                                float* __restrict__ part,
                                                int* __restrict__ arrive,
@@ -615,46 +661,49 @@ __device__ __forceinline__ void gemm_bf16_tile(const FfnSched* __restrict__ sc, 
       return;
     }
   }
-  if (GATED && fg.gidx) {   // gate/up reading x through the row -> token map
-    if (TALL && t.tall)
-      gemm_bf16_body<TALL ? BMT : BM, TALL ? BNT : BN, WM, WN, GATED, GATED, NS>(
-          fg, m0, n0t, h, smem, 0, 1, nullptr, 0, nullptr);
-    else
-      gemm_bf16_body<BM, BN, WM, WN, GATED, GATED, NS>(fg, m0, n0, h, smem, t.slice, t.nslice, pt,
-                                                   ps, ar);
-  } else {
-    if (TALL && t.tall)
-      gemm_bf16_body<TALL ? BMT : BM, TALL ? BNT : BN, WM, WN, GATED, false, NS>(
-          fg, m0, n0t, h, smem, 0, 1, nullptr, 0, nullptr);
-    else
-      gemm_bf16_body<BM, BN, WM, WN, GATED, false, NS>(fg, m0, n0, h, smem, t.slice, t.nslice, pt,
-                                                       ps, ar);
+  if constexpr (TALL) {
+    if (t.tall) {   // part of an expert's tall last tile: all of K
+      if (GATED && fg.gidx)   // gate/up reading x through the row -> token map
+        gemm_bf16_body<BMT, BNT, WM, WN, GATED, GATED, NS>(fg, m0, n0t, h, smem, 0, 1, nullptr,
+                                                           0, nullptr);
+      else
+        gemm_bf16_body<BMT, BNT, WM, WN, GATED, false, NS>(fg, m0, n0t, h, smem, 0, 1, nullptr,
+                                                           0, nullptr);
+      return;
+    }
   }
+  constexpr int NB = DEEP ? 3 : NS;   // three weight stages (two-ahead weight prefetch)
+  if (GATED && fg.gidx)
+    gemm_bf16_body<BM, BN, WM, WN, GATED, GATED, NS, 0, NB>(fg, m0, n0, h, smem, t.slice,
+                                                            t.nslice, pt, ps, ar);
+  else
+    gemm_bf16_body<BM, BN, WM, WN, GATED, false, NS, 0, NB>(fg, m0, n0, h, smem, t.slice,
+                                                            t.nslice, pt, ps, ar);
 }
 
-template <int BM, int BN, int WM, int WN, bool GATED, bool TALL>
+template <int BM, int BN, int WM, int WN, bool GATED, bool TALL, bool DEEP = false>
 constexpr size_t tile_lds_bytes() {
   constexpr int NS = kernel_stages<BM>();
   return TALL ? cmax<bf16_lds_bytes<BM, BN, GATED, NS>(),
                      bf16_lds_bytes<BM + 32 * WM, BN / tall_split<WM, WN>(), GATED, NS>()>()
-              : cmax<bf16_lds_bytes<BM, BN, GATED, NS>(),
+              : cmax<bf16_lds_bytes<BM, BN, GATED, NS, DEEP ? 3 : NS>(),
                      cmax<bf16_lds_bytes<128, BN, GATED, 3>(),
                           bf16_lds_bytes<192, BN, GATED, 2>()>()>();
 }
 
-template <int BM, int BN, int WM, int WN, bool TALL>
+template <int BM, int BN, int WM, int WN, bool TALL, bool DEEP = false>
 __global__ __launch_bounds__(64 * WM * WN) void ffn_gate_up_bf16(const FfnSched* __restrict__ sc,
                                                                  int h, float* part,
                                                                  int* arrive) {
-  __shared__ uint4 smem[tile_lds_bytes<BM, BN, WM, WN, true, TALL>() / 16];
-  gemm_bf16_tile<BM, BN, WM, WN, true, TALL>(sc, h, part, arrive, smem);
+  __shared__ uint4 smem[tile_lds_bytes<BM, BN, WM, WN, true, TALL, DEEP>() / 16];
+  gemm_bf16_tile<BM, BN, WM, WN, true, TALL, DEEP>(sc, h, part, arrive, smem);
 }
-template <int BM, int BN, int WM, int WN, bool TALL>
+template <int BM, int BN, int WM, int WN, bool TALL, bool DEEP = false>
 __global__ __launch_bounds__(64 * WM * WN) void ffn_down_bf16(const FfnSched* __restrict__ sc,
                                                               int h, float* part,
                                                               int* arrive) {
-  __shared__ uint4 smem[tile_lds_bytes<BM, BN, WM, WN, false, TALL>() / 16];
-  gemm_bf16_tile<BM, BN, WM, WN, false, TALL>(sc, h, part, arrive, smem);
+  __shared__ uint4 smem[tile_lds_bytes<BM, BN, WM, WN, false, TALL, DEEP>() / 16];
+  gemm_bf16_tile<BM, BN, WM, WN, false, TALL, DEEP>(sc, h, part, arrive, smem);
 }
 
 // fp32 grouped GEMM: 64 x 64 tiles (gated: 32 gate + 32 up columns), 4x4 per thread.
@@ -1186,7 +1235,7 @@ Tiling tiling(Tiles k) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool TALL>
+template <int BM, int BN, int WM, int WN, bool TALL, bool DEEP = false>
 bool launch_bf16_gemm(bool gated, const FfnSched* sc, int h, int64_t ub, int cpx, float* part,
                       int* arrive, hipStream_t st) {
   constexpr int NT = 64 * WM * WN;
@@ -1194,18 +1243,31 @@ bool launch_bf16_gemm(bool gated, const FfnSched* sc, int h, int64_t ub, int cpx
   // per XCD: its share of the tiles plus room for one round of k-slices
   const int64_t g = ((ub + kNumXcd - 1) / kNumXcd + cpx) * kNumXcd;
   if (gated)
-    hipLaunchKernelGGL((ffn_gate_up_bf16<BM, BN, WM, WN, TALL>), dim3((unsigned)g), dim3(NT), 0,
-                       st, sc, h, part, arrive);
+    hipLaunchKernelGGL((ffn_gate_up_bf16<BM, BN, WM, WN, TALL, DEEP>), dim3((unsigned)g),
+                       dim3(NT), 0, st, sc, h, part, arrive);
   else
-    hipLaunchKernelGGL((ffn_down_bf16<BM, BN, WM, WN, TALL>), dim3((unsigned)g), dim3(NT), 0,
-                       st, sc, h, part, arrive);
+    hipLaunchKernelGGL((ffn_down_bf16<BM, BN, WM, WN, TALL, DEEP>), dim3((unsigned)g), dim3(NT),
+                       0, st, sc, h, part, arrive);
   return hipGetLastError() == hipSuccess;
 }
 
+// 256-row tiles stream each weight tile once per 4+ m-tiles; with three weight stages in
+// LDS (two A stages: 160 KB in all) the weights are fetched two k-steps ahead. That helps
+// every GEMM measured except the gate/up GEMM of ~1000-row experts, which is bound by LDS
+// reads rather than fetch latency and runs 3% slower with it (Mixtral: down -1.5%;
+// DeepSeek-V3 share gate/up -4.5%, skewed layers' down -5%).
+bool deep_weight_prefetch(const Dims& d, bool gated) {
+  const double per_expert = d.E > 0 ? (double)d.T * d.K / d.E : 0.0;
+  return !(gated && per_expert >= 1024);
+}
+
 bool launch_bf16(Tiles k, bool gated, const FfnSched* sc, int h, int64_t ub, int cpx,
-                 float* part, int* arrive, hipStream_t st) {
+                 float* part, int* arrive, hipStream_t st, bool deep) {
   switch (k) {
     case Tiles::Large:
+      if (deep)
+        return launch_bf16_gemm<256, 256, 2, 2, false, true>(gated, sc, h, ub, cpx, part, arrive,
+                                                             st);
       return launch_bf16_gemm<256, 256, 2, 2, false>(gated, sc, h, ub, cpx, part, arrive, st);
     case Tiles::Medium:
       return launch_bf16_gemm<128, 256, 2, 2, true>(gated, sc, h, ub, cpx, part, arrive, st);
@@ -1364,9 +1426,12 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
     if (ok && ev) ok = hipEventRecord(ev[1], st) == hipSuccess;
     if (ok) ok = launch_mx(tile_kind(d, false), false, sc, d.h, ub2, st);
   } else if (d.bf16) {
-    ok = launch_bf16(tile_kind(d, true), true, sc, d.h, ub1, cpx, part, a.arrive, st);
+    ok = launch_bf16(tile_kind(d, true), true, sc, d.h, ub1, cpx, part, a.arrive, st,
+                     deep_weight_prefetch(d, true));
     if (ok && ev) ok = hipEventRecord(ev[1], st) == hipSuccess;
-    if (ok) ok = launch_bf16(tile_kind(d, false), false, sc, d.h, ub2, cpx, part, a.arrive, st);
+    if (ok)
+      ok = launch_bf16(tile_kind(d, false), false, sc, d.h, ub2, cpx, part, a.arrive, st,
+                       deep_weight_prefetch(d, false));
   } else {
     const int64_t g1 = (ub1 + kNumXcd - 1) / kNumXcd * kNumXcd;
     const int64_t g2 = (ub2 + kNumXcd - 1) / kNumXcd * kNumXcd;

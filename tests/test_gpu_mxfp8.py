@@ -345,3 +345,68 @@ def test_mx_stage_ffn_is_unsupported():
     with pytest.raises(moe.MoeError):
         moe.moe_expert_ffn(p, b["xp"], b["offsets"], w, w, None, None, None, b["yp"], None,
                            b["ws"])
+
+
+def _mx_tensors(cfg, inp, q, b):
+    t = dict(b)
+    t.update(x=inp["x"], w_router=inp["w_router"], bias=inp["bias"], w13=q["w13"], w2=q["w2"],
+             w13_sh=q["w13_sh"], w2_sh=q["w2_sh"], w13_scale=q["w13_scale"],
+             w2_scale=q["w2_scale"], w13_sh_scale=q["w13_sh_scale"],
+             w2_sh_scale=q["w2_sh_scale"])
+    t["xp"] = None
+    return t
+
+
+def _mx_weights(inp):
+    q = {}
+    for k in ("w13", "w2", "w13_sh", "w2_sh"):
+        if inp.get(k) is None:
+            q[k] = q[k + "_scale"] = None
+            continue
+        w = inp[k]
+        c, s = moe.quantize_mx(w.reshape(-1, w.shape[-1]))
+        q[k] = c.reshape(w.shape)
+        q[k + "_scale"] = s.reshape(w.shape[:-1] + (w.shape[-1] // 32,))
+    return q
+
+
+def test_mx_replicated_forward_equals_plain():
+    """With every expert on this GPU and no capacity, a replica map only regroups rows: the
+    MX-FP8 GEMMs (never split along K) compute each row in the same order, so the layer
+    output must equal the plain forward's bit for bit, each replica running its logical
+    expert's codes and scales."""
+    cfg = BASE.with_(T=600, h=256, E=8, K=2, inter=256)
+    inp = gpu_inputs(cfg)
+    q = _mx_weights(inp)
+    p = moe.problem_from_config(cfg)
+    p.act_dtype = moe.DTYPE["mxfp8"]
+    b = moe.alloc_buffers(p, "cuda")
+    moe.moe_forward(p, _mx_tensors(cfg, inp, q, b), b["ws"])
+    torch.cuda.synchronize()
+    ids = np_(b["topk_ids"]).astype(np.int64)
+    plan = moe.replica_plan(cfg.E, 8, 1, np.bincount(ids.reshape(-1), minlength=cfg.E))
+    assert (plan["counts"] > 1).any()
+    rmap = moe.DeviceReplicaMap(plan)
+    rb = moe.alloc_buffers_replicated(p, rmap.P)
+    moe.moe_forward_replicated(p, rmap, _mx_tensors(cfg, inp, q, rb), rb["ws"])
+    torch.cuda.synchronize()
+    assert torch.equal(rb["topk_ids"], b["topk_ids"])
+    assert torch.equal(rb["y"], b["y"])
+
+
+def test_mx_noalloc_equals_forward():
+    """moe_forward_noalloc on an MX-FP8 problem (x's codes and the gated product's codes
+    live in the library's own array) equals moe_forward, on two calls, the second smaller."""
+    for T in (64, 24):
+        cfg = CONFIGS["dsv3_decode"].with_(T=T, h=512, E=32, inter=256)
+        inp = gpu_inputs(cfg)
+        q = _mx_weights(inp)
+        p = moe.problem_from_config(cfg)
+        p.act_dtype = moe.DTYPE["mxfp8"]
+        want = moe.alloc_buffers(p, "cuda")
+        moe.moe_forward(p, _mx_tensors(cfg, inp, q, want), want["ws"])
+        got = moe.alloc_buffers(p, "cuda")
+        moe.moe_forward_noalloc(p, _mx_tensors(cfg, inp, q, got))
+        torch.cuda.synchronize()
+        for k in ("topk_ids", "topk_w", "offsets", "row_src", "y"):
+            assert torch.equal(want[k], got[k]), (T, k)
