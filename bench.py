@@ -118,13 +118,15 @@ def summarize_traffic(fetch_csv, write_csv, workload):
                     rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"],
                                  float(r["Counter_Value"]) * 1024.0))
         rows.sort()
-        first = min(d for d, n, _ in rows if stage_of(n) is not None)
+        # the layer calls start at the first router kernel; earlier library kernels (the
+        # MX-FP8 weights' one-time quantisation) and the calibration copy come before
+        first = min(d for d, n, _ in rows if stage_of(n) == "route")
         copies = [v for d, n, v in rows if "copyBuffer" in n and d < first]
         tot, kern = {}, {}
         calls = 0
-        for _, n, v in rows:
+        for d, n, v in rows:
             s = stage_of(n)
-            if s is None:
+            if s is None or d < first:
                 continue
             calls += s == "combine"
             tot[s] = tot.get(s, 0.0) + v

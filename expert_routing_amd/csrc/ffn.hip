@@ -2,19 +2,23 @@
 //   GEMM1 (gated):  H[r] = silu(A[r] W_g^T) * (A[r] W_u^T)      -> hbuf (act dtype)
 //   GEMM2 (down):   Y[r] = H[r] W_d^T                             -> yp / y_sh
 // Groups are the local experts (rows from `offsets`, read on the device) plus the
-// optional shared expert over this rank's token block. A one-block prep kernel turns
-// the offsets into a tile table; every GEMM block finds its (group, n-tile, m-tile) by
-// binary search, so the host never waits for the routing result.
+// optional shared expert over this rank's token block. The offsets become a tile table
+// (built by dispatch, or by a one-block prep kernel); every GEMM block finds its (group,
+// n-tile, m-tile) by binary search, so the host never waits for the routing result.
 //
 // bf16 path: 256 threads (4 waves), MFMA 32x32x16 bf16 with fp32 accumulators; operand
-// tiles stream by buffer->LDS DMA into two 64-deep stages of XOR-swizzled 128-byte rows,
-// one k-step ahead of the MFMAs; an LDS-staged epilogue writes 16-byte coalesced rows;
-// an XCD-aware block order keeps consecutive tiles of one expert on one XCD's L2. Tile
-// shapes (256, 128 or 32 rows by 256 weight rows) are chosen per GEMM from the rows per
-// expert; with 128- and 32-row tiles a short remainder rides on an expert's last tile
-// (tall tiles); an XCD's last, partial round of tiles is split along K (fp32 partials,
-// summed in slice order by the last slice to arrive). Without xp the gate/up GEMM reads
-// its A rows straight from x through the row -> token map.
+// tiles stream by buffer->LDS DMA into 64-deep stages of XOR-swizzled 128-byte rows
+// (two for 256-row tiles, or two activation and three weight stages; three for 128-row
+// and four for 32-row tiles); an LDS-staged epilogue writes 16-byte coalesced rows; an
+// XCD-aware block order keeps consecutive tiles of one expert on one XCD's L2. Tile shapes
+// (256, 128 or 32 rows by 256 weight rows) are chosen per GEMM from the rows per expert;
+// with 128- and 32-row tiles a short remainder rides on an expert's last tile (tall
+// tiles), with 256-row tiles a 65..192-row remainder gets a short last tile; an XCD's
+// last, partial round of tiles is split along K (fp32 partials, summed in slice order by
+// the last slice to arrive). Without xp the gate/up GEMM reads its A rows straight from x
+// through the row -> token map.
+//
+// MX-FP8 path: the same tiles and pipeline on scaled FP8 MFMAs (see its section below).
 #include "ffn_sched.h"
 #include "mxfp8.h"
 
