@@ -8,8 +8,8 @@
 //
 // bf16 path: 256 threads (4 waves), MFMA 32x32x16 bf16 with fp32 accumulators; operand
 // tiles stream by buffer->LDS DMA into 64-deep stages of XOR-swizzled 128-byte rows
-// (two for 256-row tiles, or two activation and three weight stages; three for 128-row
-// and four for 32-row tiles); an LDS-staged epilogue writes 16-byte coalesced rows; an
+// (two activation and three weight stages for 256-row tiles, three for 128-row and four
+// for 32-row tiles); an LDS-staged epilogue writes 16-byte coalesced rows; an
 // XCD-aware block order keeps consecutive tiles of one expert on one XCD's L2. Tile shapes
 // (256, 128 or 32 rows by 256 weight rows) are chosen per GEMM from the rows per expert;
 // with 128- and 32-row tiles a short remainder rides on an expert's last tile (tall
@@ -160,7 +160,10 @@ __device__ __forceinline__ global_i32* as_global(const int32_t* p) { return (glo
 // of bank conflicts whether the LDS serves 8 or 16 lanes per cycle.
 __device__ __forceinline__ int row_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-constexpr int kDmaStride = 2;   // MFMAs per interleaved DMA instruction
+constexpr int kDmaStride = 2;   // MFMAs per interleaved DMA instruction (MX-FP8, bf16 gate/up)
+// The bf16 down GEMM spreads its DMA wider: its weights stream from HBM once per four
+// m-tiles, and every third MFMA measured 6% faster than every second at the Mixtral shape.
+constexpr int kDmaStrideDown = 3;
 
 constexpr int kLdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
 
@@ -314,9 +317,12 @@ __device__ __forceinline__ void store_tile_parts(const float* __restrict__ part,
 // bf16 grouped GEMM. Block tile BM x BN (BN counts weight rows: for GATED half gate,
 // half up), k-step 64, WM x WN waves (4 or 8), each wave (BM/WM) x (BN/WN) as 32x32
 // MFMA tiles. With 8 waves two share each SIMD, so one wave's MFMAs keep the matrix
-// core busy while the other waits to issue its memory instructions. Operand tiles stream into two LDS stages by buffer->LDS DMA (no register
-// staging) one k-step ahead of the MFMAs. Every DMA request covers whole 128-byte row
-// segments (half-line requests roughly halve what L2 can deliver per CU). The MFMA takes
+// core busy while the other waits to issue its memory instructions. Operand tiles stream
+// into NS LDS stages by buffer->LDS DMA (no register staging), up to NS - 1 k-steps ahead
+// of the MFMAs; with NB = 3 the weights take three stages and the activations two, so the
+// weights are fetched two k-steps ahead and the activations one. Every DMA request covers
+// whole 128-byte row segments (half-line requests roughly halve what L2 can deliver per
+// CU). The MFMA takes
 // the weight fragment first, so a lane's accumulators hold 4 consecutive output columns.
 // VARIANT only tells apart instantiations that are otherwise identical but reached from
 // different tile kinds (an expert's short last tile in the 256-row kernels and the 128-row
@@ -455,8 +461,20 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
   // instruction every kDmaStride MFMAs: a burst of VMEM issues would block the wave, and
   // one per MFMA (measured) outruns what the address units accept from four waves.
   // dma: A of next_step (and, with NB == NS, its B); dmab: B of bnext (NB != NS only)
+  // Early barrier (the gate/up GEMM with three weight stages): every A instruction of a
+  // k-step is issued before its last phase, so the wait for the next k-step's operands and
+  // the workgroup barrier sit after that phase's first MFMA, and the next k-step's first
+  // fragments are read under the phase's other MFMAs rather than after the k-step. The
+  // barrier also orders every wave's reads of the current stages before the DMA that
+  // refills them (issued from the next k-step on), so the k-steps need no other barrier.
+  // The weight instructions of kt + 2 issued before the barrier (NBB) may stay in flight.
+  constexpr int DS = GATED ? kDmaStride : kDmaStrideDown;
+  constexpr bool EB = GATED && NS == 2 && NB == 3 && (AI - 1) * DS + 1 <= 3 * NMF;
+  constexpr int NBB_RAW = (3 * NMF - 1) / DS + 1 - AI;
+  constexpr int NBB = NBB_RAW < 0 ? 0 : (NBB_RAW > BI ? BI : NBB_RAW);
   auto kstep = [&](int stage, bool dma, int next_step, int dma_stage, int bstage, bool dmab,
-                   int bnext) __attribute__((always_inline)) {
+                   int bnext, bool eb = false, int nstage = 0, int nbstage = 0)
+                   __attribute__((always_inline)) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int cur = kk & 1;
@@ -465,8 +483,8 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
         acc[t / TN][t % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             fb[cur][t % TN], fa[cur][t / TN], acc[t / TN][t % TN], 0, 0, 0);
         const int slot = kk * NMF + t;            // MFMA index within the k-step
-        if (slot >= 1 && (slot - 1) % kDmaStride == 0 && (slot - 1) / kDmaStride < LPS) {
-          const int xx = (slot - 1) / kDmaStride;
+        if (slot >= 1 && (slot - 1) % DS == 0 && (slot - 1) / DS < LPS) {
+          const int xx = (slot - 1) / DS;
           if (NB == NS || xx < AI) {
             if (dma) issue_one(next_step, dma_stage, xx);
           } else if (dmab) {
@@ -477,12 +495,24 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
           __builtin_amdgcn_sched_barrier(0);
           read_frags(cur ^ 1, stage, kk + 1, bstage);
         }
+        if constexpr (EB) {
+          if (t == 0 && kk == 3 && eb) {
+            __builtin_amdgcn_sched_barrier(0);
+            // this wave's reads of the current stages have returned (lgkmcnt(0)), and its
+            // DMA of the next k-step's operands has landed
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            if (dmab) wait_vmcnt<NBB>();
+            else wait_vmcnt<0>();
+            lds_barrier();
+            read_frags(0, nstage, 0, nbstage);
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     // instructions left over when the k-step has too few MFMAs
 #pragma unroll
-    for (int x = (4 * NMF - 2) / kDmaStride + 1; x < LPS; ++x) {
+    for (int x = (4 * NMF - 2) / DS + 1; x < LPS; ++x) {
       if (NB == NS || x < AI) {
         if (dma) issue_one(next_step, dma_stage, x);
       } else if (dmab) {
@@ -508,16 +538,26 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
       read_frags(0, 0, 0, 0);
       int kt = 0;
       for (; kt + 2 < nk; ++kt) {   // A of kt + 1, B of kt + 2
-        kstep(kt % NS, true, kt + 1, (kt + 1) % NS, kt % NB, true, kt + 2);
-        wait_vmcnt<BI>();
-        lds_barrier();
-        read_frags(0, (kt + 1) % NS, 0, (kt + 1) % NB);
+        if constexpr (EB) {
+          kstep(kt % NS, true, kt + 1, (kt + 1) % NS, kt % NB, true, kt + 2, true,
+                (kt + 1) % NS, (kt + 1) % NB);
+        } else {
+          kstep(kt % NS, true, kt + 1, (kt + 1) % NS, kt % NB, true, kt + 2);
+          wait_vmcnt<BI>();
+          lds_barrier();
+          read_frags(0, (kt + 1) % NS, 0, (kt + 1) % NB);
+        }
       }
       if (kt + 1 < nk) {            // A of the last k-step
-        kstep(kt % NS, true, kt + 1, (kt + 1) % NS, kt % NB, false, 0);
-        wait_vmcnt<0>();
-        lds_barrier();
-        read_frags(0, (kt + 1) % NS, 0, (kt + 1) % NB);
+        if constexpr (EB) {
+          kstep(kt % NS, true, kt + 1, (kt + 1) % NS, kt % NB, false, 0, true, (kt + 1) % NS,
+                (kt + 1) % NB);
+        } else {
+          kstep(kt % NS, true, kt + 1, (kt + 1) % NS, kt % NB, false, 0);
+          wait_vmcnt<0>();
+          lds_barrier();
+          read_frags(0, (kt + 1) % NS, 0, (kt + 1) % NB);
+        }
         ++kt;
       }
       kstep(kt % NS, false, 0, 0, kt % NB, false, 0);
@@ -1256,23 +1296,13 @@ bool launch_bf16_gemm(bool gated, const FfnSched* sc, int h, int64_t ub, int cpx
 }
 
 // 256-row tiles stream each weight tile once per 4+ m-tiles; with three weight stages in
-// LDS (two A stages: 160 KB in all) the weights are fetched two k-steps ahead. That helps
-// every GEMM measured except the gate/up GEMM of ~1000-row experts, which is bound by LDS
-// reads rather than fetch latency and runs 3% slower with it (Mixtral: down -1.5%;
-// DeepSeek-V3 share gate/up -4.5%, skewed layers' down -5%).
-bool deep_weight_prefetch(const Dims& d, bool gated) {
-  const double per_expert = d.E > 0 ? (double)d.T * d.K / d.E : 0.0;
-  return !(gated && per_expert >= 1024);
-}
-
+// LDS (two A stages: 160 KB in all) the weights are fetched two k-steps ahead.
 bool launch_bf16(Tiles k, bool gated, const FfnSched* sc, int h, int64_t ub, int cpx,
-                 float* part, int* arrive, hipStream_t st, bool deep) {
+                 float* part, int* arrive, hipStream_t st) {
   switch (k) {
     case Tiles::Large:
-      if (deep)
-        return launch_bf16_gemm<256, 256, 2, 2, false, true>(gated, sc, h, ub, cpx, part, arrive,
-                                                             st);
-      return launch_bf16_gemm<256, 256, 2, 2, false>(gated, sc, h, ub, cpx, part, arrive, st);
+      return launch_bf16_gemm<256, 256, 2, 2, false, true>(gated, sc, h, ub, cpx, part, arrive,
+                                                           st);
     case Tiles::Medium:
       return launch_bf16_gemm<128, 256, 2, 2, true>(gated, sc, h, ub, cpx, part, arrive, st);
     default:
@@ -1430,12 +1460,9 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
     if (ok && ev) ok = hipEventRecord(ev[1], st) == hipSuccess;
     if (ok) ok = launch_mx(tile_kind(d, false), false, sc, d.h, ub2, st);
   } else if (d.bf16) {
-    ok = launch_bf16(tile_kind(d, true), true, sc, d.h, ub1, cpx, part, a.arrive, st,
-                     deep_weight_prefetch(d, true));
+    ok = launch_bf16(tile_kind(d, true), true, sc, d.h, ub1, cpx, part, a.arrive, st);
     if (ok && ev) ok = hipEventRecord(ev[1], st) == hipSuccess;
-    if (ok)
-      ok = launch_bf16(tile_kind(d, false), false, sc, d.h, ub2, cpx, part, a.arrive, st,
-                       deep_weight_prefetch(d, false));
+    if (ok) ok = launch_bf16(tile_kind(d, false), false, sc, d.h, ub2, cpx, part, a.arrive, st);
   } else {
     const int64_t g1 = (ub1 + kNumXcd - 1) / kNumXcd * kNumXcd;
     const int64_t g2 = (ub2 + kNumXcd - 1) / kNumXcd * kNumXcd;
