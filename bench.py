@@ -3,7 +3,7 @@
 on one MI355X, seeded synthetic inputs resident in HBM.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME|all] [--no-cpu-baseline]
-                    [--dtype bf16|mxfp8]
+                    [--dtype bf16|mxfp8] [--weights packed|rows]
 
 Default workload: the Mixtral-shaped prefill layer (T=4096 tokens, h=4096, 8 experts, top-2
 softmax, SwiGLU inter=14336, bf16 with fp32 accumulation, fp32 router, no capacity limit).
@@ -21,6 +21,9 @@ times and the per-stage rates against the HBM / MFMA rooflines. The CPU baseline
 the fp64 oracle on the same workload; its routing result also gives the near-tie count and
 the first-choice skew.
 
+bf16 expert weights are packed once before timing into the MFMA-fragment order the GEMMs
+stream straight into registers (moe_pack_weights, a permutation done at load time, like
+any kernel-specific weight layout); `--weights rows` times the row-major layout instead.
 `--dtype mxfp8` runs the same workload with MX-FP8 expert weights (E4M3 codes and E8M0
 block scales, quantised once on the GPU before timing): x is quantised per token inside
 the step, both GEMMs run on the FP8 matrix cores, and their rates are taken against the
@@ -283,15 +286,26 @@ def route_bound(cfg):
     return "hbm", peak
 
 
+def variant_suffix(args, workload_dtype):
+    """Suffix of a workload's traffic summary: none for the default bf16 run (packed
+    weights), _rows for row-major bf16 weights, _mxfp8 for MX-FP8."""
+    if args.dtype == "mxfp8":
+        return "_mxfp8"
+    return "_rows" if workload_dtype == "bf16" and args.weights == "rows" else ""
+
+
 def run_workload(name, args, moe, torch, np):
     from synth import CONFIGS, make_inputs
 
     cfg = CONFIGS[name]
     mx = args.dtype == "mxfp8"
+    pk = not mx and cfg.dtype == "bf16" and args.weights == "packed"
     inp = make_inputs(cfg, device="cuda")
     p = moe.problem_from_config(cfg)
     if mx:
         p.act_dtype = moe.DTYPE["mxfp8"]
+    if pk:
+        p.act_dtype = moe.DTYPE["bf16_packed"]
     b = moe.alloc_buffers(p, "cuda")
     t = dict(b)
     t.update(x=inp["x"], w_router=inp["w_router"], bias=inp["bias"], w13=inp["w13"],
@@ -306,6 +320,12 @@ def run_workload(name, args, moe, torch, np):
             c, sc = moe.quantize_mx(w.reshape(-1, w.shape[-1]))
             t[k] = c.reshape(w.shape)
             t[k + "_scale"] = sc.reshape(w.shape[:-1] + (w.shape[-1] // 32,))
+        torch.cuda.synchronize()
+    if pk:
+        # the weights in the packed fragment order, once before timing
+        for k in ("w13", "w2", "w13_sh", "w2_sh"):
+            if inp[k] is not None:
+                t[k] = moe.pack_weights(inp[k])
         torch.cuda.synchronize()
     gather = not args.materialize_xp
     if gather:
@@ -386,11 +406,12 @@ def run_workload(name, args, moe, torch, np):
     mfma_peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
     gu_bound = "mfma" if gu["flops"] / gu["bytes"] > mfma_peak * 1e12 / (PEAK_HBM_GBS * 1e9) \
         else "hbm"
-    traffic = load_traffic(name + ("_mxfp8" if mx else ""))
+    traffic = load_traffic(name + variant_suffix(args, cfg.dtype))
     gu_ms = net(steady)["ffn_gate_up"]
     kname = ("ffn_gate_up_mxfp8 (grouped gate/up GEMM on scaled FP8 MFMA, fused silu*mul "
              "and MX quantisation)" if mx else
-             "ffn_gate_up_bf16 (grouped gate/up GEMM, fused silu*mul)")
+             "ffn_gate_up_pk (grouped gate/up GEMM on packed bf16 weights, fused silu*mul)"
+             if pk else "ffn_gate_up_bf16 (grouped gate/up GEMM, fused silu*mul)")
     if gu_bound == "mfma":
         achieved = gu["flops"] / (gu_ms * 1e-3) / 1e12
         roof = {"kernel": kname, "bound": "mfma", "achieved": achieved, "peak": mfma_peak,
@@ -442,7 +463,10 @@ def run_workload(name, args, moe, torch, np):
                    "inter": cfg.inter, "score": cfg.score, "n_groups": cfg.n_groups,
                    "topk_groups": cfg.topk_groups, "capacity_factor": cfg.capacity_factor,
                    "n_ep": cfg.n_ep, "n_shared": cfg.n_shared, "router": "fp32",
-                   "xp": "gathered by the gate/up GEMM" if gather else "materialised"},
+                   "xp": "gathered by the gate/up GEMM" if gather else "materialised",
+                   "expert_weights": ("MX-FP8, quantised before timing" if mx else
+                                      "packed fragment order, packed before timing" if pk
+                                      else "row-major")},
         "roofline": roof,
         "routed_pairs_per_s": (T * K - dropped) / (ms * 1e-3),
         "layer_tflops": (gu["flops"] + work["ffn_down"]["flops"]) / (ms * 1e-3) / 1e12,
@@ -495,13 +519,16 @@ def main():
     ap.add_argument("--dtype", choices=["bf16", "mxfp8"], default="bf16",
                     help="expert weights and GEMM operands: bf16 (the workloads' dtype), or "
                          "MX-FP8 (E4M3 with E8M0 block scales; activations stay bf16)")
+    ap.add_argument("--weights", choices=["packed", "rows"], default="packed",
+                    help="bf16 expert weights in the packed fragment order (packed once "
+                         "before timing) or row-major")
     ap.add_argument("--materialize-xp", action="store_true",
                     help="pass xp, so dispatch copies rows into it (default: no xp; the "
                          "gate/up GEMM reads x through row_src)")
     args = ap.parse_args()
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic,
-                          workload=args.workload + ("_mxfp8" if args.dtype == "mxfp8" else ""))
+                          workload=args.workload + variant_suffix(args, "bf16"))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:

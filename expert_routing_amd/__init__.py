@@ -24,9 +24,9 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 SCORE = {"softmax": 0, "sigmoid": 1}
-DTYPE = {"f32": 0, "bf16": 1, "mxfp8": 2}
-# activations of each act_dtype (MX-FP8 problems keep bf16 activations)
-_TORCH_DTYPE = {0: torch.float32, 1: torch.bfloat16, 2: torch.bfloat16}
+DTYPE = {"f32": 0, "bf16": 1, "mxfp8": 2, "bf16_packed": 3}
+# activations of each act_dtype (MX-FP8 and packed-weight problems keep bf16 activations)
+_TORCH_DTYPE = {0: torch.float32, 1: torch.bfloat16, 2: torch.bfloat16, 3: torch.bfloat16}
 
 
 class Problem(ctypes.Structure):
@@ -105,6 +105,8 @@ _forward_traced = _sig("moe_forward_traced",
 _forward_noalloc = _sig("moe_forward_noalloc", [_P, ctypes.POINTER(Tensors), _V])
 _quantize_mx = _sig("moe_quantize_mx", [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _V, _V,
                                         _V, _V])
+_pack_weights = _sig("moe_pack_weights", [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _V, _V,
+                                          _V])
 _RM = ctypes.POINTER(ReplicaMap)
 _replica_plan = _sig("moe_replica_plan", [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           _V, _V, _V, _V, _V, _V])
@@ -122,7 +124,8 @@ EXPORTED = ["moe_check_problem", "moe_capacity", "moe_max_rows", "moe_workspace_
             "moe_status_string", "moe_route", "moe_select", "moe_dispatch", "moe_expert_ffn",
             "moe_combine", "moe_layout_stats", "moe_forward", "moe_forward_traced",
             "moe_forward_noalloc", "moe_replica_plan", "moe_replicated_sizes",
-            "moe_dispatch_replicated", "moe_forward_replicated", "moe_quantize_mx"]
+            "moe_dispatch_replicated", "moe_forward_replicated", "moe_quantize_mx",
+            "moe_pack_weights"]
 
 
 class MoeError(RuntimeError):
@@ -240,6 +243,25 @@ def quantize_mx(src, stream=None):
     scales = torch.empty((rows, max(cols // 32, 0)), dtype=torch.uint8, device=src.device)
     moe_quantize_mx(src, codes, scales, stream)
     return codes, scales
+
+
+def moe_pack_weights(src, dst, stream=None):
+    """Packs bf16 matrices src [mats][rows][cols] (or one [rows][cols]) into dst (same shape
+    and dtype) in the fragment order MOE_DTYPE_BF16_PACKED problems read."""
+    if src.dtype != torch.bfloat16 or dst.dtype != torch.bfloat16 or src.shape != dst.shape:
+        raise MoeError(-1, "moe_pack_weights: src and dst must be bf16 tensors of one shape")
+    if not (src.is_contiguous() and dst.is_contiguous()) or src.dim() not in (2, 3):
+        raise MoeError(-1, "moe_pack_weights: contiguous [mats][rows][cols] or [rows][cols]")
+    mats, rows, cols = (1, *src.shape) if src.dim() == 2 else tuple(src.shape)
+    _ok(_pack_weights(mats, rows, cols, _ptr(src), _ptr(dst), _stream(stream)),
+        "moe_pack_weights")
+
+
+def pack_weights(src, stream=None):
+    """src packed into a tensor allocated here."""
+    dst = torch.empty_like(src)
+    moe_pack_weights(src, dst, stream)
+    return dst
 
 
 def moe_forward(p, t: dict, ws, stream=None):
@@ -389,10 +411,11 @@ def alloc_buffers(p: Problem, device="cuda", send=True) -> dict:
     return b
 
 
-def problem_from_config(cfg, T=None) -> Problem:
-    """Problem for a workload description with the fields of synth.MoEConfig."""
+def problem_from_config(cfg, T=None, dtype=None) -> Problem:
+    """Problem for a workload description with the fields of synth.MoEConfig (dtype, when
+    given, overrides the workload's: "bf16_packed" for bf16 with packed expert weights)."""
     return Problem(T=cfg.T if T is None else T, h=cfg.h, E=cfg.E, K=cfg.K, score=cfg.score,
                    renorm=cfg.renorm, n_groups=cfg.n_groups, topk_groups=cfg.topk_groups,
                    capacity_factor=cfg.capacity_factor, pad=cfg.pad, n_ep=cfg.n_ep,
                    ep_rank=cfg.ep_rank, inter=cfg.inter, n_shared=cfg.n_shared,
-                   shared_inter=cfg.shared_inter, dtype=cfg.dtype)
+                   shared_inter=cfg.shared_inter, dtype=dtype or cfg.dtype)

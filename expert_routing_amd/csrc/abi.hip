@@ -49,7 +49,7 @@ int make_dims(const moe_problem* p, Dims* d) {
   if (p->topk_groups < 1 || p->topk_groups > p->n_groups) return MOE_ERR_INVALID;
   if ((int64_t)p->topk_groups * (p->E / p->n_groups) < p->K) return MOE_ERR_INVALID;
   if (p->act_dtype != MOE_DTYPE_F32 && p->act_dtype != MOE_DTYPE_BF16 &&
-      p->act_dtype != MOE_DTYPE_MXFP8)
+      p->act_dtype != MOE_DTYPE_MXFP8 && p->act_dtype != MOE_DTYPE_BF16_PACKED)
     return MOE_ERR_INVALID;
   if (p->n_shared != 0 && p->n_shared != 1) return MOE_ERR_INVALID;
   if (p->inter < 0 || p->shared_inter < 0) return MOE_ERR_INVALID;
@@ -59,7 +59,8 @@ int make_dims(const moe_problem* p, Dims* d) {
   if (!cap_exact(p->capacity_factor, p->T, p->K, p->E, &cap)) return MOE_ERR_UNSUPPORTED;
   if (p->pad_to_capacity && cap < 0) return MOE_ERR_INVALID;
   const bool mx = p->act_dtype == MOE_DTYPE_MXFP8;
-  const bool bf16 = p->act_dtype == MOE_DTYPE_BF16 || mx;
+  const bool pk = p->act_dtype == MOE_DTYPE_BF16_PACKED;
+  const bool bf16 = p->act_dtype == MOE_DTYPE_BF16 || mx || pk;
   if (mx && (p->h % 128 != 0 || p->inter % 128 != 0 || p->shared_inter % 128 != 0))
     return MOE_ERR_UNSUPPORTED;   // 128-value k-steps: four scale blocks per row and step
   if (bf16) {
@@ -98,6 +99,7 @@ int make_dims(const moe_problem* p, Dims* d) {
   d->s = bf16 ? 2 : 4;
   d->bf16 = bf16;
   d->mx = mx;
+  d->pk = pk;
   d->route_split = route_split(*d);
   return MOE_OK;
 }
@@ -446,6 +448,21 @@ int moe_quantize_mx(int64_t rows, int32_t cols, int32_t src_dtype, const void* s
   if (rows * (int64_t)cols / 32 >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
   return launch_mx_quant(src, src_dtype == MOE_DTYPE_BF16, rows, cols, codes, scales,
                          (hipStream_t)stream);
+}
+
+int moe_pack_weights(int64_t mats, int32_t rows, int32_t cols, const void* src, void* dst,
+                     void* stream) {
+  if (mats < 0 || rows <= 0 || cols <= 0) return MOE_ERR_INVALID;
+  if (rows % 32 != 0 || cols % 16 != 0) return MOE_ERR_INVALID;
+  if (mats == 0) return MOE_OK;
+  if (!src || !dst) return MOE_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 != 0)
+    return MOE_ERR_INVALID;
+  if ((int64_t)rows * cols >= ((int64_t)1 << 40) / mats) return MOE_ERR_UNSUPPORTED;
+  const uintptr_t bytes = (uintptr_t)(mats * rows * (int64_t)cols * 2);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a < b + bytes && b < a + bytes) return MOE_ERR_INVALID;   // overlapping
+  return launch_pack_weights(mats, rows, cols, src, dst, (hipStream_t)stream);
 }
 
 int moe_replicated_sizes(const moe_problem* p, int32_t P, int64_t* max_rows, size_t* ws_bytes) {

@@ -314,6 +314,47 @@ __device__ __forceinline__ void store_tile_parts(const float* __restrict__ part,
   }
 }
 
+// The end of a tile, once every wave is past its last operand read: the whole tile goes
+// through store_tile; a k-slice of a split tile stores its fp32 partial sums (fragment
+// order, so each store is 1 KB contiguous) and counts itself in, and the last slice to
+// arrive adds all of them in slice order (the same order whichever arrives last) and
+// stores the tile.
+template <int BM, int BN, int WM, int WN, bool GATED>
+__device__ __forceinline__ void finish_tile(const floatx16 (&acc)[BM / WM / 32][BN / WN / 32],
+                                            const FfnGroup& fg, int m0, int n0, int h,
+                                            uint4* __restrict__ smem, int slice, int nslice,
+                                            float* __restrict__ part, size_t pstride,
+                                            int* __restrict__ arrive) {
+  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (part) {
+    const size_t frag = (size_t)wave * TM * TN * 4 * 64 + lane;
+    float4* dst = reinterpret_cast<float4*>(part + (size_t)slice * pstride) + frag;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          dst[((i * TN + j) * 4 + q4) * 64] =
+              make_float4(acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2],
+                          acc[i][j][4 * q4 + 3]);
+    __threadfence();
+    __syncthreads();
+    // the flag lives in the (now idle) operand LDS: a second LDS object would make the
+    // compiler wait for all LDS DMA before every fragment read of the main loop
+    int* last = reinterpret_cast<int*>(smem);
+    if (tid == 0) *last = atomicAdd(arrive, 1) == nslice - 1;
+    __syncthreads();
+    if (!*last) return;
+    __threadfence();
+    store_tile_parts<BM, BN, WM, WN, GATED>(part, pstride, nslice, fg, m0, n0, h, smem);
+    return;
+  }
+  store_tile<BM, BN, WM, WN, GATED>(acc, fg, m0, n0, h, smem);
+}
+
 // bf16 grouped GEMM. Block tile BM x BN (BN counts weight rows: for GATED half gate,
 // half up), k-step 64, WM x WN waves (4 or 8), each wave (BM/WM) x (BN/WN) as 32x32
 // MFMA tiles. With 8 waves two share each SIMD, so one wave's MFMAs keep the matrix
@@ -599,35 +640,229 @@ __device__ __forceinline__ void gemm_bf16_body(const FfnGroup& fg, int m0, int n
   }
   }
   __syncthreads();
+  finish_tile<BM, BN, WM, WN, GATED>(acc, fg, m0, n0, h, smem, slice, nslice, part, pstride,
+                                     arrive);
+}
 
-  if (part) {
-    // Split tile: store this slice's fp32 partial sums (fragment order, so each store is
-    // 1 KB contiguous), then count the slice in. The last slice to arrive adds all of
-    // them in slice order (the same order whichever arrives last) and stores the tile.
-    const size_t frag = (size_t)wave * TM * TN * 4 * 64 + lane;
-    float4* dst = reinterpret_cast<float4*>(part + (size_t)slice * pstride) + frag;
+// ---- bf16 grouped GEMM on packed weights ---------------------------------------------
+// Weights in MFMA-fragment order (moe_pack_weights): 32 weight rows by 16 k values form one
+// 1 KB block in which lane l's 16 bytes are row l % 32, k 8*(l/32) .. +7, exactly the
+// weight operand of one 32x32x16 MFMA. A wave loads its weight fragments straight into
+// registers, one coalesced 1 KB load each, NS - 1 k-steps ahead into a ring of NS
+// k-steps; only the activation tile goes through LDS (buffer->LDS DMA into NS stages,
+// NS - 1 k-steps ahead). Measured on gfx950: a k-step's LDS writes cost more than its
+// reads, and writing the weight tile to LDS (by DMA or by ds_write) was a quarter of the
+// 256-row GEMM's time. The waves sit side by side (WM = 1): each streams its own weight
+// columns, none twice. The workgroup barrier of a k-step follows the first MFMA of its
+// last phase (the wait there is for the next k-step's activations), and the next
+// k-step's first fragments are read under the rest of that phase.
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+
+template <int BM, int BN, int WM, int WN, bool GATED, bool GATHER, int NS, int VARIANT = 0>
+__device__ __forceinline__ void gemm_pk_body(const FfnGroup& fg, int m0, int n0, int h,
+                                             uint4* __restrict__ smem, int slice, int nslice,
+                                             float* __restrict__ part, size_t pstride,
+                                             int* __restrict__ arrive) {
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  static_assert(TM >= 1 && TN >= 1, "tile");
+  static_assert(!GATED || TN % 2 == 0, "gated needs gate/up pairs");
+  static_assert(BM % (8 * NW) == 0, "DMA rows split evenly over waves");
+  constexpr int AI = BM / (8 * NW);     // activation DMA instructions per wave per k-step
+  constexpr int LB = 4 * TN;            // weight loads per wave per k-step
+  constexpr int LPS = AI + LB;          // a k-step's group of instructions
+  constexpr int A_ST = BM * 8;          // uint4 per stage
+  constexpr int NMF = TM * TN;          // MFMAs per k16 phase
+  constexpr int DS = kDmaStride;
+  constexpr int EBS = 3 * NMF;          // the barrier follows MFMA EBS (first of phase 3)
+  static_assert(NS >= 3 && NS <= 4, "stages");
+  // Issue order of the group of k-step kt + NS - 1 during k-step kt: weight loads from
+  // the first MFMA on, one every DS MFMAs; the activation DMA only after the barrier
+  // (into the stage k-step kt - 1 used, whose reads every wave has consumed by then);
+  // weight loads that did not fit before the barrier after the DMA. At the barrier of
+  // k-step kt the activations of kt + 1 (issued during k-step kt + 2 - NS, after its
+  // barrier) have landed once all but the instructions issued after them are done:
+  // that group's remaining weights, the NS - 3 whole groups after it and this k-step's
+  // weights so far, LB + (NS - 3) * LPS in all.
+  constexpr int WB_RAW = (EBS - 1) / DS + 1;        // weight loads up to the barrier
+  constexpr int WB = WB_RAW > LB ? LB : WB_RAW;
+  constexpr int A_SLOTS = (4 * NMF - 1 - EBS - 1) / DS + 1;   // DMA slots after it
+  constexpr int AB = A_SLOTS > AI ? AI : (A_SLOTS < 0 ? 0 : A_SLOTS);
+  constexpr int N_EB = LB + (NS - 3) * LPS;
+  static_assert(N_EB < 64, "vmcnt range");
+  uint4* As = smem;                     // [NS][BM rows][8 chunks]
+
+  const int rows = fg.rows, I = fg.inter;
+  const bf16_t* A = static_cast<const bf16_t*>(GATED ? fg.A1 : fg.C1);
+  const bf16_t* B = static_cast<const bf16_t*>(GATED ? fg.B1 : fg.B2);
+  const int Kd = GATED ? h : I;
+  const uint32_t b_rows = GATED ? 2 * I : h;
+  const uint32_t a_bytes = (uint32_t)(GATHER ? fg.arows : rows) * Kd * 2;
+  const __amdgpu_buffer_rsrc_t ra_rs = make_rsrc(A, a_bytes);
+  const __amdgpu_buffer_rsrc_t rb_rs = make_rsrc(B, b_rows * (uint32_t)Kd * 2);
+  const __amdgpu_buffer_rsrc_t rz_rs = make_rsrc(A, 0);   // every load reads zero
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  // activation DMA: as in gemm_bf16_body
+  const int dr = lane >> 3;
+  const int dc = (lane & 7) ^ dr ^ (wave & 1);
+  const uint32_t a_lane = ((uint32_t)(m0 + 8 * wave + dr) * Kd + dc * 8) * 2;
+  const uint32_t x_stride = (uint32_t)(8 * NW) * Kd * 2;
+  uint32_t a_off[GATHER ? AI : 1];
+  if constexpr (GATHER) {
+    const global_i32* gidx = as_global(fg.gidx);
+    int src[AI];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int x = 0; x < AI; ++x) {
+      const int r = m0 + 8 * (NW * x + wave) + dr;
+      src[x] = gidx[r < rows ? r : rows - 1];
+    }
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          dst[((i * TN + j) * 4 + q4) * 64] =
-              make_float4(acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2],
-                          acc[i][j][4 * q4 + 3]);
-    __threadfence();
-    __syncthreads();
-    // the flag lives in the (now idle) operand LDS: a second LDS object would make the
-    // compiler wait for all LDS DMA before every fragment read of the main loop
-    int* last = reinterpret_cast<int*>(smem);
-    if (tid == 0) *last = atomicAdd(arrive, 1) == nslice - 1;
-    __syncthreads();
-    if (!*last) return;
-    __threadfence();
-    store_tile_parts<BM, BN, WM, WN, GATED>(part, pstride, nslice, fg, m0, n0, h, smem);
-    return;
+    for (int x = 0; x < AI; ++x) {
+      const int r = m0 + 8 * (NW * x + wave) + dr;
+      a_off[x] = (r < rows && src[x] >= 0) ? ((uint32_t)(src[x] / fg.gK) * Kd + dc * 8) * 2
+                                           : a_bytes;
+    }
   }
-  store_tile<BM, BN, WM, WN, GATED>(acc, fg, m0, n0, h, smem);
+  // Weight col-tile j of this wave: 32 weight rows from wr (a multiple of 32), so its
+  // fragment for k16 chunk c sits at byte wr*Kd*2 + c*1024 + lane*16 of the packed
+  // matrix. Gated: gate col-tiles first, then the up rows of the same output columns.
+  // Rows past the matrix read as zero; gate rows past I read up rows, which only feed
+  // output columns past I that are never stored.
+  uint32_t b_off[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    int wr;
+    if (GATED)
+      wr = j < TN / 2 ? n0 + wn * (WTN / 2) + j * 32 : I + n0 + wn * (WTN / 2) + (j - TN / 2) * 32;
+    else
+      wr = n0 + wn * WTN + j * 32;
+    b_off[j] = ((uint32_t)wr * Kd + lane * 8) * 2;
+  }
+
+  const int kb = __builtin_amdgcn_readfirstlane(slice * (Kd / 64) / nslice);
+  const int nk = __builtin_amdgcn_readfirstlane((slice + 1) * (Kd / 64) / nslice) - kb;
+  // k-steps rounded up to whole rounds of NS: the ones past nk load zeros (activations
+  // and weights alike) and add exactly nothing, so the k-loop has no exit inside a round
+  const int nkp = (nk + NS - 1) / NS * NS;
+
+  floatx16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  int arow[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) arow[i] = wm * WTM + i * 32 + (lane & 31);
+  // Activation fragments: one per row-tile, each replaced by the next phase's as soon as
+  // the phase's last MFMA on it is issued (a phase of MFMAs ahead of its use).
+  bf16x8_t fa[TM];
+  bf16x8_t fw[NS][4][TN];   // weight fragments of NS k-steps: [ring slot][k16 phase][col-tile]
+  auto read_a = [&](int i, int stage, int kk) __attribute__((always_inline)) {
+    const uint4* as = As + stage * A_ST;
+    const int c = kk * 2 + (lane >> 5);
+    fa[i] = __builtin_bit_cast(bf16x8_t, as[arow[i] * 8 + (c ^ row_swz(arow[i]))]);
+  };
+  // The group of k-step `step` (stage and ring slot `slot` = step % NS): activation DMA
+  // instruction x, weight load y. k-steps past nk read zeros.
+  auto issue_a = [&](int step, int slot, int x) __attribute__((always_inline)) {
+    const uint32_t soff = (uint32_t)(kb + step) * 128;
+    const __amdgpu_buffer_rsrc_t rs = step < nk ? ra_rs : rz_rs;
+    if constexpr (GATHER)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, LDS_PTR(As + slot * A_ST + 64 * (NW * x + wave)), 16, a_off[x], soff, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, LDS_PTR(As + slot * A_ST + 64 * (NW * x + wave)), 16, a_lane, soff + x * x_stride,
+          0, 0);
+  };
+  auto issue_w = [&](int step, int slot, int y) __attribute__((always_inline)) {
+    const int kk = y / TN, j = y % TN;
+    const uint32_t soff = (uint32_t)(4 * (kb + step) + kk) * 1024;
+    fw[slot][kk][j] = __builtin_bit_cast(
+        bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(step < nk ? rb_rs : rz_rs, b_off[j],
+                                                        soff, 0));
+  };
+
+  // k-step kt (kt % NS == P): four k16 phases of NMF MFMAs, and the group of k-step
+  // kt + NS - 1. Every k-step issues a whole group, so the issue points and the counts
+  // the waits use are fixed and the MFMAs stay one straight run of code.
+  auto step = [&](auto PC, int kt) __attribute__((always_inline)) {
+    constexpr int P = decltype(PC)::value;
+    constexpr int NX = (P + 1) % NS;          // stage of kt + 1
+    constexpr int FS = (P + NS - 1) % NS;     // stage and ring slot of kt + NS - 1
+    const int ft = kt + NS - 1;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int t = 0; t < NMF; ++t) {
+        const int i = t / TN, j = t % TN;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[P][kk][j], fa[i], acc[i][j], 0,
+                                                            0, 0);
+        const int slot = kk * NMF + t;
+        if (slot >= 1 && slot <= EBS && (slot - 1) % DS == 0 && (slot - 1) / DS < WB)
+          issue_w(ft, FS, (slot - 1) / DS);
+        if (slot == EBS) {
+          __builtin_amdgcn_sched_barrier(0);
+          // the next k-step's activations have landed, here and (barrier) in every wave
+          // (after the last k-step this reads a stage nothing uses, which is harmless)
+          wait_vmcnt<N_EB>();
+          lds_barrier();
+        }
+        if (slot > EBS && (slot - EBS - 1) % DS == 0 && (slot - EBS - 1) / DS < AB)
+          issue_a(ft, FS, (slot - EBS - 1) / DS);
+        if (j == TN - 1) {   // last MFMA on fa[i] in this phase
+          __builtin_amdgcn_sched_barrier(0);
+          if (kk < 3) read_a(i, P, kk + 1);
+          else read_a(i, NX, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int x = AB; x < AI; ++x) issue_a(ft, FS, x);
+#pragma unroll
+    for (int y = WB; y < LB; ++y) issue_w(ft, FS, y);
+  };
+
+  if (nk > 0) {
+    // groups of k-steps 0 .. NS - 2, then wait for k-step 0's activations
+    // the groups of k-steps 0 .. NS - 2, each in the order a k-step issues one (weights
+    // up to the barrier, activations, the other weights), so the counts above hold
+#pragma unroll
+    for (int s0 = 0; s0 < NS - 1; ++s0) {
+#pragma unroll
+      for (int y = 0; y < WB; ++y) issue_w(s0, s0, y);
+#pragma unroll
+      for (int x = 0; x < AI; ++x) issue_a(s0, s0, x);
+#pragma unroll
+      for (int y = WB; y < LB; ++y) issue_w(s0, s0, y);
+    }
+    wait_vmcnt<(LB - WB) + (NS - 2) * LPS>();   // k-step 0's activations
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) read_a(i, 0, 0);
+    for (int kt = 0; kt < nkp; kt += NS) {
+      step(IC<0>{}, kt);
+      step(IC<1>{}, kt + 1);
+      if constexpr (NS > 2) step(IC<2>{}, kt + 2);
+      if constexpr (NS > 3) step(IC<3>{}, kt + 3);
+    }
+    wait_vmcnt<0>();   // the zero groups past the end land before the LDS is reused
+  }
+  __syncthreads();
+  finish_tile<BM, BN, WM, WN, GATED>(acc, fg, m0, n0, h, smem, slice, nslice, part, pstride,
+                                     arrive);
 }
 
 template <int BM, int BN, bool GATED, int NS = 2, int NB = NS>
@@ -748,6 +983,127 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_down_bf16(const FfnSched* __
                                                               int* arrive) {
   __shared__ uint4 smem[tile_lds_bytes<BM, BN, WM, WN, false, TALL, DEEP>() / 16];
   gemm_bf16_tile<BM, BN, WM, WN, false, TALL, DEEP>(sc, h, part, arrive, smem);
+}
+
+template <int BM, int BN, bool GATED, int NS>
+constexpr size_t pk_lds_bytes() {
+  constexpr size_t ops = (size_t)NS * BM * 8 * 16;
+  constexpr size_t stg = (size_t)BM * ((GATED ? BN / 2 : BN) * 2 + 16);
+  return ops > stg ? ops : stg;
+}
+
+// Activation stages on packed weights: the LDS holds nothing else, and smaller tiles
+// stream more bytes per MFMA.
+template <int BM>
+constexpr int pk_stages() { return BM >= 128 ? 3 : 4; }
+
+template <int BN, int WM, int WN, bool GATED, bool GATHER>
+__device__ __forceinline__ void pk_short(int q, const FfnGroup& fg, int m0, int n0, int h,
+                                         uint4* __restrict__ smem, int slice, int nslice,
+                                         float* part, size_t pstride, int* arrive) {
+  if (q == 2)
+    gemm_pk_body<128, BN, WM, WN, GATED, GATHER, 3, 1>(fg, m0, n0, h, smem, slice, nslice, part,
+                                                       pstride, arrive);
+  else
+    gemm_pk_body<192, BN, WM, WN, GATED, GATHER, 3>(fg, m0, n0, h, smem, slice, nslice, part,
+                                                    pstride, arrive);
+}
+
+// The tile of a block on packed weights: as gemm_bf16_tile.
+template <int BM, int BN, int WM, int WN, bool GATED, bool TALL>
+__device__ __forceinline__ void gemm_pk_tile(const FfnSched* __restrict__ sc, int h,
+                                             float* __restrict__ part, int* __restrict__ arrive,
+                                             uint4* __restrict__ smem) {
+  constexpr int BMT = BM + 32 * WM, TS = tall_split<WM, WN>(), BNT = BN / TS;
+  constexpr int BNO = GATED ? BN / 2 : BN;
+  constexpr int NS = pk_stages<BM>();
+  TileRef t;
+  if (!find_tile(sc, GATED, t)) return;
+  t.g = __builtin_amdgcn_readfirstlane(t.g);
+  t.m_tile = __builtin_amdgcn_readfirstlane(t.m_tile);
+  t.n_tile = __builtin_amdgcn_readfirstlane(t.n_tile);
+  t.tall = __builtin_amdgcn_readfirstlane(t.tall);
+  t.slice = __builtin_amdgcn_readfirstlane(t.slice);
+  t.nslice = __builtin_amdgcn_readfirstlane(t.nslice);
+  t.piece = __builtin_amdgcn_readfirstlane(t.piece);
+  t.pstride = __builtin_amdgcn_readfirstlane(t.pstride);
+  t.tid_x = __builtin_amdgcn_readfirstlane(t.tid_x);
+  const FfnGroup& fg = sc->g[t.g];
+  const int m0 = t.m_tile * BM, n0 = t.n_tile * BNO;
+  float* pt = t.piece >= 0 ? part + (size_t)t.piece * BM * BN : nullptr;
+  int* ar = arrive + (GATED ? 0 : kArriveSlots) + (t.tid_x >= 0 ? t.tid_x : 0);
+  const size_t ps = (size_t)t.pstride * BM * BN;
+  const int n0t = n0 + (t.tall - 1) * (BNO / TS);
+  if constexpr (!TALL) {
+    if (t.tall) {   // an expert's short last m-tile (128 or 192 rows)
+      if (GATED && fg.gidx)
+        pk_short<BN, WM, WN, GATED, GATED>(t.tall, fg, m0, n0, h, smem, t.slice, t.nslice, pt, ps,
+                                           ar);
+      else
+        pk_short<BN, WM, WN, GATED, false>(t.tall, fg, m0, n0, h, smem, t.slice, t.nslice, pt, ps,
+                                           ar);
+      return;
+    }
+  }
+  if constexpr (TALL) {
+    if (t.tall) {   // part of an expert's tall last tile: all of K
+      if (GATED && fg.gidx)
+        gemm_pk_body<BMT, BNT, WM, WN, GATED, GATED, NS>(fg, m0, n0t, h, smem, 0, 1, nullptr, 0,
+                                                         nullptr);
+      else
+        gemm_pk_body<BMT, BNT, WM, WN, GATED, false, NS>(fg, m0, n0t, h, smem, 0, 1, nullptr, 0,
+                                                         nullptr);
+      return;
+    }
+  }
+  if (GATED && fg.gidx)
+    gemm_pk_body<BM, BN, WM, WN, GATED, GATED, NS>(fg, m0, n0, h, smem, t.slice, t.nslice, pt, ps,
+                                                   ar);
+  else
+    gemm_pk_body<BM, BN, WM, WN, GATED, false, NS>(fg, m0, n0, h, smem, t.slice, t.nslice, pt, ps,
+                                                   ar);
+}
+
+template <int BM, int BN, int WM, int WN, bool GATED, bool TALL>
+constexpr size_t pk_tile_lds_bytes() {
+  constexpr int NS = pk_stages<BM>();
+  return TALL ? cmax<pk_lds_bytes<BM, BN, GATED, NS>(),
+                     pk_lds_bytes<BM + 32 * WM, BN / tall_split<WM, WN>(), GATED, NS>()>()
+              : cmax<pk_lds_bytes<BM, BN, GATED, NS>(),
+                     cmax<pk_lds_bytes<128, BN, GATED, 3>(), pk_lds_bytes<192, BN, GATED, 3>()>()>();
+}
+
+template <int BM, int BN, int WM, int WN, bool TALL>
+__global__ __launch_bounds__(64 * WM * WN) void ffn_gate_up_pk(const FfnSched* __restrict__ sc,
+                                                               int h, float* part, int* arrive) {
+  __shared__ uint4 smem[pk_tile_lds_bytes<BM, BN, WM, WN, true, TALL>() / 16];
+  gemm_pk_tile<BM, BN, WM, WN, true, TALL>(sc, h, part, arrive, smem);
+}
+template <int BM, int BN, int WM, int WN, bool TALL>
+__global__ __launch_bounds__(64 * WM * WN) void ffn_down_pk(const FfnSched* __restrict__ sc,
+                                                            int h, float* part, int* arrive) {
+  __shared__ uint4 smem[pk_tile_lds_bytes<BM, BN, WM, WN, false, TALL>() / 16];
+  gemm_pk_tile<BM, BN, WM, WN, false, TALL>(sc, h, part, arrive, smem);
+}
+
+// Weights in the packed order the GEMMs above read: one thread per 16-byte output chunk o
+// = ((m * rows/32 + b) * cols/16 + k) * 64 + l, holding row 32b + l%32, columns
+// 16k + 8(l/32) .. +7 of matrix m.
+__global__ __launch_bounds__(256) void pack_weights(const uint4* __restrict__ src,
+                                                    uint4* __restrict__ dst, int64_t chunks,
+                                                    int rows, int cols) {
+  const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (o >= chunks) return;
+  const int l = (int)(o & 63);
+  int64_t rest = o >> 6;
+  const int kblocks = cols / 16, rblocks = rows / 32;
+  const int k = (int)(rest % kblocks);
+  rest /= kblocks;
+  const int b = (int)(rest % rblocks);
+  const int64_t m = rest / rblocks;
+  const int64_t row = (int64_t)b * 32 + (l & 31);
+  const int64_t col = (int64_t)k * 16 + 8 * (l >> 5);
+  dst[o] = src[((m * rows + row) * cols + col) / 8];
 }
 
 // fp32 grouped GEMM: 64 x 64 tiles (gated: 32 gate + 32 up columns), 4x4 per thread.
@@ -1269,12 +1625,12 @@ Tiles tile_kind(const Dims& d, bool gate_up) {
 struct Tiling {
   int BM, tall_extra, tall_split;   // tall: 32 rows per wave row; halves when WM = 2
 };
-Tiling tiling(Tiles k) {
+Tiling tiling(Tiles k, bool waves_side_by_side) {
   switch (k) {
     // 256-row tiles: tall parts would cost as much as tiles; an expert's last m-tile is a
     // short one instead when its remainder is 65..192 rows (tall_split 0)
     case Tiles::Large: return {256, 0, 0};
-    case Tiles::Medium: return {128, 64, 2};
+    case Tiles::Medium: return waves_side_by_side ? Tiling{128, 32, 1} : Tiling{128, 64, 2};
     default: return {32, 32, 1};
   }
 }
@@ -1307,6 +1663,34 @@ bool launch_bf16(Tiles k, bool gated, const FfnSched* sc, int h, int64_t ub, int
       return launch_bf16_gemm<128, 256, 2, 2, true>(gated, sc, h, ub, cpx, part, arrive, st);
     default:
       return launch_bf16_gemm<32, 256, 1, 4, true>(gated, sc, h, ub, cpx, part, arrive, st);
+  }
+}
+
+template <int BM, int BN, int WM, int WN, bool TALL>
+bool launch_pk_gemm(bool gated, const FfnSched* sc, int h, int64_t ub, int cpx, float* part,
+                    int* arrive, hipStream_t st) {
+  constexpr int NT = 64 * WM * WN;
+  if (ub <= 0) return true;
+  const int64_t g = ((ub + kNumXcd - 1) / kNumXcd + cpx) * kNumXcd;
+  if (gated)
+    hipLaunchKernelGGL((ffn_gate_up_pk<BM, BN, WM, WN, TALL>), dim3((unsigned)g), dim3(NT), 0,
+                       st, sc, h, part, arrive);
+  else
+    hipLaunchKernelGGL((ffn_down_pk<BM, BN, WM, WN, TALL>), dim3((unsigned)g), dim3(NT), 0, st,
+                       sc, h, part, arrive);
+  return hipGetLastError() == hipSuccess;
+}
+
+// Packed weights: every tile kind with its four waves side by side.
+bool launch_pk(Tiles k, bool gated, const FfnSched* sc, int h, int64_t ub, int cpx,
+               float* part, int* arrive, hipStream_t st) {
+  switch (k) {
+    case Tiles::Large:
+      return launch_pk_gemm<256, 256, 1, 4, false>(gated, sc, h, ub, cpx, part, arrive, st);
+    case Tiles::Medium:
+      return launch_pk_gemm<128, 256, 1, 4, true>(gated, sc, h, ub, cpx, part, arrive, st);
+    default:
+      return launch_pk_gemm<32, 256, 1, 4, true>(gated, sc, h, ub, cpx, part, arrive, st);
   }
 }
 
@@ -1366,8 +1750,8 @@ int ffn_prep_args(const moe_problem* p, const Dims& d, const void* xp, const voi
   int BN1 = F_BN / 2, BN2 = F_BN, split_max = 1;
   const int has_sh = (p->n_shared && d.sh_rows > 0) ? 1 : 0;
   if (d.bf16) {
-    t1 = tiling(d.mx ? mx_tiles(tile_kind(d, true)) : tile_kind(d, true));
-    t2 = tiling(d.mx ? mx_tiles(tile_kind(d, false)) : tile_kind(d, false));
+    t1 = tiling(d.mx ? mx_tiles(tile_kind(d, true)) : tile_kind(d, true), d.pk);
+    t2 = tiling(d.mx ? mx_tiles(tile_kind(d, false)) : tile_kind(d, false), d.pk);
     int min_k = d.h < p->inter ? d.h : p->inter;
     if (has_sh && p->shared_inter < min_k) min_k = p->shared_inter;
     split_max = min_k / 64 < kMaxSplit ? min_k / 64 : kMaxSplit;
@@ -1460,9 +1844,10 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
     if (ok && ev) ok = hipEventRecord(ev[1], st) == hipSuccess;
     if (ok) ok = launch_mx(tile_kind(d, false), false, sc, d.h, ub2, st);
   } else if (d.bf16) {
-    ok = launch_bf16(tile_kind(d, true), true, sc, d.h, ub1, cpx, part, a.arrive, st);
+    auto run = d.pk ? launch_pk : launch_bf16;
+    ok = run(tile_kind(d, true), true, sc, d.h, ub1, cpx, part, a.arrive, st);
     if (ok && ev) ok = hipEventRecord(ev[1], st) == hipSuccess;
-    if (ok) ok = launch_bf16(tile_kind(d, false), false, sc, d.h, ub2, cpx, part, a.arrive, st);
+    if (ok) ok = run(tile_kind(d, false), false, sc, d.h, ub2, cpx, part, a.arrive, st);
   } else {
     const int64_t g1 = (ub1 + kNumXcd - 1) / kNumXcd * kNumXcd;
     const int64_t g2 = (ub2 + kNumXcd - 1) / kNumXcd * kNumXcd;
@@ -1475,6 +1860,15 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
   }
   if (ok && ev) ok = hipEventRecord(ev[2], st) == hipSuccess;
   return ok ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+int launch_pack_weights(int64_t mats, int rows, int cols, const void* src, void* dst,
+                        hipStream_t st) {
+  const int64_t chunks = mats * rows * (int64_t)cols / 8;
+  if (chunks <= 0) return MOE_OK;
+  hipLaunchKernelGGL(pack_weights, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st,
+                     static_cast<const uint4*>(src), static_cast<uint4*>(dst), chunks, rows, cols);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
 }  // namespace moe

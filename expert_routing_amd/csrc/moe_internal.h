@@ -41,6 +41,7 @@ struct Dims {
   int s;            // activation bytes
   bool bf16;        // bf16 activations (also with MX-FP8 expert weights)
   bool mx;          // MX-FP8 expert weights and GEMM operands
+  bool pk;          // bf16 expert weights in the packed fragment order
   int route_split;  // K-slices of the router GEMM (partial logits summed in order)
 };
 
@@ -121,6 +122,8 @@ int launch_combine(const moe_problem* p, const Dims& d, const void* yp, const in
 
 // MX-FP8 quantisation of a rows x cols matrix (cols % 32 == 0): codes [rows][cols],
 // scale bytes [rows][cols / 32].
+int launch_pack_weights(int64_t mats, int rows, int cols, const void* src, void* dst,
+                        hipStream_t st);
 int launch_mx_quant(const void* src, bool bf16, int64_t rows, int cols, uint8_t* codes,
                     uint8_t* scales, hipStream_t st);
 

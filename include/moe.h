@@ -46,7 +46,12 @@ enum moe_status {
 };
 
 enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
-enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1, MOE_DTYPE_MXFP8 = 2 };
+enum moe_dtype {
+  MOE_DTYPE_F32 = 0,
+  MOE_DTYPE_BF16 = 1,
+  MOE_DTYPE_MXFP8 = 2,
+  MOE_DTYPE_BF16_PACKED = 3
+};
 
 /*
  * The problem statement of one MoE layer call, in the pages' own quantities: T tokens
@@ -94,6 +99,11 @@ enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1, MOE_DTYPE_MXFP8 = 2 };
  *               关键观察 observation 3: quantise / dequantise passes cost as much as the
  *               GEMMs unless fused). Only moe_forward and its variants take it; the
  *               stage call moe_expert_ffn returns MOE_ERR_UNSUPPORTED.
+ *               MOE_DTYPE_BF16_PACKED: bf16 throughout, as MOE_DTYPE_BF16, with the
+ *               routed and shared expert weights (w13, w2, w13_sh, w2_sh) in the order
+ *               moe_pack_weights writes. The GEMMs then load weight fragments straight
+ *               into registers and keep the LDS for the token rows; results are the same
+ *               as with MOE_DTYPE_BF16 on the unpacked weights up to fp32 summation order.
  */
 typedef struct moe_problem {
   int64_t T;
@@ -298,6 +308,18 @@ int moe_forward_traced(const moe_problem* p, const moe_tensors* t, void* ws, siz
  *   codes   [rows][cols] uint8 out;  scales [rows][cols/32] uint8 out                   */
 int moe_quantize_mx(int64_t rows, int32_t cols, int32_t src_dtype, const void* src,
                     uint8_t* codes, uint8_t* scales, void* stream);
+
+/* Weight packing for MOE_DTYPE_BF16_PACKED (a one-time transform, like loading a
+ * checkpoint into the kernels' layout). src holds `mats` row-major bf16 matrices
+ * [mats][rows][cols]; dst (same size, caller-owned, not overlapping src) receives them
+ * as [mats][rows/32][cols/16][64][8]: the 1 KB block (b, k) of a matrix holds, for lane
+ * l = 0..63, row 32*b + l%32, columns 16*k + 8*(l/32) .. +7. That is the operand
+ * fragment of one 32x32x16 bf16 MFMA, so a GEMM reads each fragment as one coalesced
+ * 1 KB load. Pack w13 with (E_l, 2*inter, h), w2 with (E_l, h, inter) and the shared
+ * expert's with mats = 1. Requires rows % 32 == 0, cols % 16 == 0, 16-byte aligned
+ * pointers (else MOE_ERR_INVALID); enqueued on `stream`. */
+int moe_pack_weights(int64_t mats, int32_t rows, int32_t cols, const void* src, void* dst,
+                     void* stream);
 
 /* ---- redundant experts ---------------------------------------------------------------
  * A logical -> physical replica map: P = E + R physical experts (replicas), P a multiple of

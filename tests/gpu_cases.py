@@ -9,9 +9,18 @@ import expert_routing_amd as moe
 from synth import make_inputs
 
 
-def run_stages(cfg, inp, p=None):
-    """route -> dispatch -> expert FFN -> combine, one ABI call per stage."""
-    p = p or moe.problem_from_config(cfg, T=inp["T"])
+def packed_weights(inp):
+    """The expert weights of a bf16 workload in the packed order (moe_pack_weights)."""
+    return {k: (None if inp[k] is None else moe.pack_weights(inp[k]))
+            for k in ("w13", "w2", "w13_sh", "w2_sh")}
+
+
+def run_stages(cfg, inp, p=None, packed=False):
+    """route -> dispatch -> expert FFN -> combine, one ABI call per stage (packed: bf16
+    with packed expert weights)."""
+    p = p or moe.problem_from_config(cfg, T=inp["T"], dtype="bf16_packed" if packed else None)
+    if packed:
+        inp = dict(inp, **packed_weights(inp))
     b = moe.alloc_buffers(p, "cuda")
     if cfg.keys == "uniform":
         moe.moe_select(p, inp["keys"], inp["bias"], b["topk_ids"], b["topk_w"])
@@ -28,9 +37,12 @@ def run_stages(cfg, inp, p=None):
     return p, b
 
 
-def run_forward(cfg, inp, p=None, gather=False):
-    """moe_forward; gather=True passes no xp, so the gate/up GEMM reads x through row_src."""
-    p = p or moe.problem_from_config(cfg, T=inp["T"])
+def run_forward(cfg, inp, p=None, gather=False, packed=False):
+    """moe_forward; gather=True passes no xp, so the gate/up GEMM reads x through row_src;
+    packed: bf16 with packed expert weights."""
+    p = p or moe.problem_from_config(cfg, T=inp["T"], dtype="bf16_packed" if packed else None)
+    if packed:
+        inp = dict(inp, **packed_weights(inp))
     b = moe.alloc_buffers(p, "cuda")
     t = dict(b)
     t.update(x=inp["x"], w_router=inp["w_router"], bias=inp["bias"], w13=inp["w13"],

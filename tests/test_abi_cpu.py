@@ -153,3 +153,25 @@ def test_noalloc_refuses_problems_beyond_its_scratch():
     # invalid problems are reported as such first
     bad = moe.Problem(T=32, h=64, E=8, K=9, inter=64)
     assert moe._forward_noalloc(moe.ctypes.byref(bad), None, None) == -1
+
+
+def test_pack_weights_argument_checks():
+    fake, other = 0x10000, 0x20000000   # never dereferenced: validation fails first
+    pk = moe._pack_weights
+    assert pk(0, 32, 16, None, None, None) == 0                 # nothing to pack
+    assert pk(-1, 32, 16, fake, other, None) == -1
+    assert pk(1, 48, 16, fake, other, None) == -1               # rows % 32
+    assert pk(1, 32, 24, fake, other, None) == -1               # cols % 16
+    assert pk(1, 32, 16, None, other, None) == -1
+    assert pk(1, 32, 16, fake + 8, other, None) == -1           # 16-byte alignment
+    assert pk(2, 64, 64, fake, fake + 4096, None) == -1         # overlapping
+    assert pk(1, 32, 16, fake, fake, None) == -1                # in place
+
+
+def test_packed_dtype_is_a_bf16_problem():
+    ok = dict(T=64, h=128, E=8, K=2, inter=128)
+    assert moe.check_problem(moe.Problem(**ok, dtype="bf16_packed")) == 0
+    assert moe.check_problem(moe.Problem(**dict(ok, h=96), dtype="bf16_packed")) == -2
+    p = moe.Problem(**ok, dtype="bf16_packed")
+    assert p.torch_dtype == moe.torch.bfloat16
+    assert moe.workspace_bytes(p) == moe.workspace_bytes(moe.Problem(**ok))
