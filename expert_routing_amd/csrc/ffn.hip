@@ -18,6 +18,10 @@
 // the last slice to arrive). Without xp the gate/up GEMM reads its A rows straight from x
 // through the row -> token map.
 //
+// Packed bf16 weights (MOE_DTYPE_BF16_PACKED): the same tiles with the weights stored in
+// MFMA-fragment order, loaded straight into registers; only the token rows go through LDS
+// (see its section below).
+//
 // MX-FP8 path: the same tiles and pipeline on scaled FP8 MFMAs (see its section below).
 #include "ffn_sched.h"
 #include "mxfp8.h"
