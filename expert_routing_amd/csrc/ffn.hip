@@ -57,11 +57,10 @@ struct XcdPlan {
 };
 
 __device__ __forceinline__ XcdPlan xcd_plan(const FfnSched* sc, bool first, int xcd) {
-  const int total = first ? sc->total1 : sc->total2;
-  const int per = (total + kNumXcd - 1) / kNumXcd;
+  const int* xb = sc->xb[first ? 0 : 1];
   XcdPlan q;
-  q.base = xcd * per;
-  q.cnt = max(0, min(per, total - q.base));
+  q.base = xb[xcd];
+  q.cnt = xb[xcd + 1] - xb[xcd];
   const int cpx = sc->cu_per_xcd;
   q.full = q.cnt / cpx * cpx;
   q.rem = q.cnt - q.full;
@@ -93,12 +92,12 @@ __device__ __forceinline__ void locate(const FfnSched* sc, bool first, int L, Ti
     t.n_tile = local / mt;
     t.tall = 0;
     if (sc->tall_split[gi] == 0 && t.m_tile == mt - 1) {
-      // short last m-tile: a remainder of 65..192 rows rounded up to 128 or 192 rows (a
-      // 64-row tile streams the same weight bytes per k-step as a full one and was measured
-      // no faster, so smaller remainders keep the full tile)
+      // short last m-tile: a remainder of up to 192 rows rounded up to 64, 128 or 192 rows
+      // (64 only on packed weights: with both operands in LDS a 64-row tile writes as many
+      // weight bytes to LDS per k-step as a full one and was measured no faster)
       const int rem = sc->g[lo].rows - t.m_tile * sc->bm[gi];
       const int q64 = (rem + 63) >> 6;
-      t.tall = q64 >= 2 && q64 <= 3 && rem < sc->bm[gi] ? q64 : 0;
+      t.tall = q64 >= sc->short_min[gi] && q64 <= 3 && rem < sc->bm[gi] ? q64 : 0;
     }
   }
 }
@@ -1005,7 +1004,10 @@ template <int BN, int WM, int WN, bool GATED, bool GATHER>
 __device__ __forceinline__ void pk_short(int q, const FfnGroup& fg, int m0, int n0, int h,
                                          uint4* __restrict__ smem, int slice, int nslice,
                                          float* part, size_t pstride, int* arrive) {
-  if (q == 2)
+  if (q == 1)
+    gemm_pk_body<64, BN, WM, WN, GATED, GATHER, 3, 2>(fg, m0, n0, h, smem, slice, nslice, part,
+                                                      pstride, arrive);
+  else if (q == 2)
     gemm_pk_body<128, BN, WM, WN, GATED, GATHER, 3, 1>(fg, m0, n0, h, smem, slice, nslice, part,
                                                        pstride, arrive);
   else
@@ -1740,6 +1742,21 @@ size_t ffn_splitk_bytes(const Dims& d) {
   return (size_t)kNumXcd * kCuPerXcdMax * tile * 4;
 }
 
+// Upper bounds on each GEMM's tiles, which the launches size their grids by:
+// sum_e ceil(rows_e / BM) <= R_max / BM + E_l m-tiles (an expert with a tall last tile has
+// mt - 1 + tall_split <= ceil(rows_e / BM) tiles per n-tile), plus the shared expert's.
+void ffn_tile_bounds(const moe_problem* p, const Dims& d, const FfnPrepArgs& a, int64_t* ub1,
+                     int64_t* ub2) {
+  const int has_sh = a.has_shared;
+  auto m_ub = [&](int BM) { return d.R_max / BM + d.El; };
+  auto m_sh = [&](int BM) { return has_sh ? (d.sh_rows + BM - 1) / BM : (int64_t)0; };
+  const int64_t nt1 = (p->inter + a.BN1 - 1) / a.BN1;
+  const int64_t nt1s = has_sh ? (p->shared_inter + a.BN1 - 1) / a.BN1 : 0;
+  const int64_t nt2 = (d.h + a.BN2 - 1) / a.BN2;
+  *ub1 = m_ub(a.BM1) * nt1 + m_sh(a.BM1) * nt1s;
+  *ub2 = (m_ub(a.BM2) + m_sh(a.BM2)) * nt2;
+}
+
 int ffn_prep_args(const moe_problem* p, const Dims& d, const void* xp, const void* w13,
                   const void* w2, const void* x, const void* w13_sh, const void* w2_sh, void* yp,
                   void* y_sh, char* ws, const WsLayout& L, const int32_t* gather_rows,
@@ -1804,6 +1821,11 @@ int ffn_prep_args(const moe_problem* p, const Dims& d, const void* xp, const voi
   a->BN1 = BN1; a->BN2 = BN2;
   a->cu_per_xcd = cpx;
   a->split_max = split_max;
+  a->short_min = d.pk ? 1 : 2;
+  int64_t ub1 = 0, ub2 = 0;
+  ffn_tile_bounds(p, d, *a, &ub1, &ub2);
+  a->ub1 = (int)(ub1 < INT32_MAX ? ub1 : INT32_MAX);
+  a->ub2 = (int)(ub2 < INT32_MAX ? ub2 : INT32_MAX);
   return MOE_OK;
 }
 
@@ -1830,18 +1852,9 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
   if (ev && hipEventRecord(ev[0], st) != hipSuccess) return MOE_ERR_LAUNCH;
   const FfnSched* sc = a.sc;
   float* part = reinterpret_cast<float*>(ws + L.splitk);
-  const int has_sh = a.has_shared;
   const int cpx = a.cu_per_xcd;
-  const int BN1 = a.BN1, BN2 = a.BN2;
-  // Upper bound on m-tiles: sum_e ceil(rows_e / BM) <= R_max / BM + E_l (an expert with a
-  // tall last tile has mt - 1 + tall_split <= ceil(rows_e / BM) tiles per n-tile).
-  auto m_ub = [&](int BM) { return d.R_max / BM + d.El; };
-  auto m_sh = [&](int BM) { return has_sh ? (d.sh_rows + BM - 1) / BM : (int64_t)0; };
-  const int64_t nt1 = (p->inter + BN1 - 1) / BN1;
-  const int64_t nt1s = has_sh ? (p->shared_inter + BN1 - 1) / BN1 : 0;
-  const int64_t nt2 = (d.h + BN2 - 1) / BN2;
-  const int64_t ub1 = m_ub(a.BM1) * nt1 + m_sh(a.BM1) * nt1s;
-  const int64_t ub2 = (m_ub(a.BM2) + m_sh(a.BM2)) * nt2;
+  int64_t ub1 = 0, ub2 = 0;
+  ffn_tile_bounds(p, d, a, &ub1, &ub2);
   bool ok = true;
   if (d.mx) {
     ok = launch_mx(tile_kind(d, true), true, sc, d.h, ub1, st);

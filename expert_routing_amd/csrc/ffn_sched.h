@@ -41,7 +41,9 @@ struct FfnSched {
   int total2;
   int tall_split[2];  // 0: no tall tiles; an expert's last m-tile is a short one instead
                       // (64, 128 or 192 rows when its remainder fits)
+  int short_min[2];   // smallest short tile of each GEMM, in 64-row units (1 or 2)
   int bm[2];          // rows of a full m-tile of each GEMM
+  int xb[2][kNumXcd + 1];   // XCD x takes tiles [xb[k][x], xb[k][x + 1]) of GEMM k
   int cu_per_xcd;   // CUs of one XCD (one round of blocks there)
   int split_max;    // 1: no split-K; else the most k-slices a tile may take
   int start1[G_PAD];
@@ -81,6 +83,8 @@ struct FfnPrepArgs {
   int sy;   // bytes per element of yp / y_sh
   int BM1, BM2, tall_extra1, tall_extra2, tall_split1, tall_split2, BN1, BN2;
   int cu_per_xcd, split_max;
+  int short_min;
+  int ub1, ub2;   // tiles the launches have blocks for (per XCD: (ub + 7) / 8)
 };
 
 // Inclusive scan of one int per thread over a block of NT threads: wave scans by shuffles,
@@ -109,6 +113,20 @@ __device__ inline int block_inclusive_scan(int v, int* wsum, int* total) {
   return v + before;
 }
 
+// Work of one n-column of a group's tiles, for splitting the tiles among the XCDs: one unit
+// a tile, except with 256-row tiles (tall_split 0), where a full tile counts BM/64 + 1 and
+// an expert's short last tile of q 64-row units q + 1. wf: a full tile's work.
+__device__ inline int column_work(int rows, int mt, int per_n, int BM, int TS, int short_min,
+                                  int* wf) {
+  *wf = 1;
+  if (TS != 0 || mt <= 0) return per_n;
+  *wf = BM / 64 + 1;
+  const int rem = rows - (mt - 1) * BM;
+  const int q64 = (rem + 63) >> 6;
+  const int wl = (q64 >= short_min && q64 <= 3 && rem < BM) ? q64 + 1 : *wf;
+  return (per_n - 1) * *wf + wl;
+}
+
 // Builds a.sc from offsets[0..El] (any address space) with the calling block's NT threads;
 // every thread of the block must call it. Thread i takes groups [i*PER, (i+1)*PER): per
 // group the m-tiles of each GEMM (a short remainder of at most tall_extra rows rides on the
@@ -119,13 +137,16 @@ __device__ inline void ffn_build_sched(const FfnPrepArgs& a, const int32_t* offs
   constexpr int PER = (G_MAX + 1 + NT - 1) / NT;   // covers index G (the end of the table)
   const int tid = threadIdx.x;
   const int G = a.El + a.has_shared;
-  int c1[PER], c2[PER];
+  __shared__ int xbs[2][kNumXcd + 1];
+  __shared__ int cst[2][G_PAD];   // work before each group, per GEMM
+  __shared__ int colw_s[2][G_PAD], pern_s[2][G_PAD];   // work and tiles of one n-column
+  __shared__ int sst[2][G_PAD];   // first tile of each group, per GEMM
+  int c1[PER], c2[PER], rows_g[PER], mt1[PER], mt2[PER], pn1[PER], pn2[PER];
   int s1 = 0, s2 = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int g = tid * PER + i;
-    c1[i] = 0;
-    c2[i] = 0;
+    c1[i] = c2[i] = rows_g[i] = mt1[i] = mt2[i] = pn1[i] = pn2[i] = 0;
     if (g < G) {
       FfnGroup fg;
       fg.A1s = fg.B1s = fg.B2s = nullptr;
@@ -180,8 +201,14 @@ __device__ inline void ffn_build_sched(const FfnPrepArgs& a, const int32_t* offs
       fg.arows = fg.gidx ? (int)a.T : rows;
       fg.gK = a.K;
       a.sc->g[g] = fg;
-      c1[i] = per_n[0] * ((I + a.BN1 - 1) / a.BN1);
-      c2[i] = per_n[1] * ((a.h + a.BN2 - 1) / a.BN2);
+      const int ncol1 = (I + a.BN1 - 1) / a.BN1, ncol2 = (a.h + a.BN2 - 1) / a.BN2;
+      c1[i] = per_n[0] * ncol1;
+      c2[i] = per_n[1] * ncol2;
+      rows_g[i] = rows;
+      mt1[i] = fg.mt[0];
+      mt2[i] = fg.mt[1];
+      pn1[i] = per_n[0];
+      pn2[i] = per_n[1];
     }
     s1 += c1[i];
     s2 += c2[i];
@@ -195,15 +222,88 @@ __device__ inline void ffn_build_sched(const FfnPrepArgs& a, const int32_t* offs
     if (g <= G) {          // start[G] = the total: the binary search's upper end
       a.sc->start1[g] = e1;
       a.sc->start2[g] = e2;
+      sst[0][g] = e1;
+      sst[1][g] = e2;
     }
     e1 += c1[i];
     e2 += c2[i];
+  }
+  // The tiles of a GEMM are split among the XCDs by work where that pays: 8 or more rounds
+  // of blocks (the last round's imbalance is then small against the work moved), else by
+  // count, as it is when the launches have no blocks for a split by work.
+  const int rounds8 = 8 * kNumXcd * a.cu_per_xcd;
+  const bool bw1 = tot1 >= rounds8, bw2 = tot2 >= rounds8;   // block-uniform
+  if (tid < 2 * (kNumXcd + 1)) {
+    const int k = tid / (kNumXcd + 1), x = tid % (kNumXcd + 1);
+    xbs[k][x] = x == 0 ? 0 : (k == 0 ? tot1 : tot2);
+  }
+  if (bw1 || bw2) {
+    int cl1[PER], cl2[PER], w1 = 0, w2 = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      int wf;
+      cl1[i] = column_work(rows_g[i], mt1[i], pn1[i], a.BM1, a.tall_split1, a.short_min, &wf);
+      cl2[i] = column_work(rows_g[i], mt2[i], pn2[i], a.BM2, a.tall_split2, a.short_min, &wf);
+      w1 += c1[i] / max(pn1[i], 1) * cl1[i];   // n-columns x work of one
+      w2 += c2[i] / max(pn2[i], 1) * cl2[i];
+    }
+    int wt1 = 0, wt2 = 0;
+    int f1 = block_inclusive_scan<NT>(w1, wsum, &wt1) - w1;
+    int f2 = block_inclusive_scan<NT>(w2, wsum, &wt2) - w2;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int g = tid * PER + i;
+      if (g <= G) {
+        cst[0][g] = f1;
+        cst[1][g] = f2;
+        colw_s[0][g] = cl1[i];
+        colw_s[1][g] = cl2[i];
+        pern_s[0][g] = pn1[i];
+        pern_s[1][g] = pn2[i];
+      }
+      f1 += c1[i] / max(pn1[i], 1) * cl1[i];
+      f2 += c2[i] / max(pn2[i], 1) * cl2[i];
+    }
+    __syncthreads();
+    // XCD x of GEMM k starts at the tile that holds work offset x*W/8 (one thread each)
+    if (tid < 2 * (kNumXcd + 1)) {
+      const int k = tid / (kNumXcd + 1), x = tid % (kNumXcd + 1);
+      const int wt = k == 0 ? wt1 : wt2;
+      if ((k == 0 ? bw1 : bw2) && x > 0 && x < kNumXcd && wt > 0) {
+        const int target = (int)((int64_t)x * wt / kNumXcd);
+        int lo = 0, hi = G;          // cst[k][lo] <= target < cst[k][hi]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (cst[k][mid] <= target) lo = mid; else hi = mid;
+        }
+        const int colw = colw_s[k][lo], per_n = pern_s[k][lo];
+        const int wf = ((k == 0 ? a.tall_split1 : a.tall_split2) == 0)
+                           ? (k == 0 ? a.BM1 : a.BM2) / 64 + 1 : 1;
+        const int off = target - cst[k][lo];
+        const int m = min((off % colw) / wf, per_n - 1);
+        xbs[k][x] = sst[k][lo] + off / colw * per_n + m;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < 2) {
+    const int k = tid, tot = k == 0 ? tot1 : tot2;
+    const int budget = ((k == 0 ? a.ub1 : a.ub2) + kNumXcd - 1) / kNumXcd;
+    bool by_work = k == 0 ? bw1 : bw2;
+    for (int x = 0; x < kNumXcd; ++x) by_work = by_work && xbs[k][x + 1] - xbs[k][x] <= budget;
+    const int per = (tot + kNumXcd - 1) / kNumXcd;
+    for (int x = 0; x <= kNumXcd; ++x)
+      a.sc->xb[k][x] = by_work ? xbs[k][x] : (x * per < tot ? x * per : tot);
   }
   for (int i = tid; i < 2 * kArriveSlots; i += NT) a.arrive[i] = 0;
   if (tid == 0) {
     a.sc->n_groups = G;
     a.sc->tall_split[0] = a.tall_split1;
     a.sc->tall_split[1] = a.tall_split2;
+    // 64-row short tiles only where the XCDs split the tiles by work: under a split by
+    // count the XCDs without them set the time, and the GEMM measured slower with them
+    a.sc->short_min[0] = bw1 ? a.short_min : 2;
+    a.sc->short_min[1] = bw2 ? a.short_min : 2;
     a.sc->bm[0] = a.BM1;
     a.sc->bm[1] = a.BM2;
     a.sc->cu_per_xcd = a.cu_per_xcd;
