@@ -33,7 +33,8 @@ namespace {
 __global__ __launch_bounds__(1024) void ffn_prep(FfnPrepArgs a,
                                                  const int32_t* __restrict__ offsets) {
   __shared__ int wsum[16];
-  ffn_build_sched<1024>(a, offsets, wsum);
+  __shared__ int lds[kSchedLdsInts];
+  ffn_build_sched<1024>(a, offsets, wsum, lds);
 }
 
 // Tile lookup shared by the GEMM kernels. The tile list is dealt to the XCDs in
@@ -1826,6 +1827,7 @@ int ffn_prep_args(const moe_problem* p, const Dims& d, const void* xp, const voi
   ffn_tile_bounds(p, d, *a, &ub1, &ub2);
   a->ub1 = (int)(ub1 < INT32_MAX ? ub1 : INT32_MAX);
   a->ub2 = (int)(ub2 < INT32_MAX ? ub2 : INT32_MAX);
+  a->by_work = (ub1 > ub2 ? ub1 : ub2) >= 8 * kNumXcd * cpx;
   return MOE_OK;
 }
 

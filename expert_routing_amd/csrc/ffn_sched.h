@@ -85,6 +85,7 @@ struct FfnPrepArgs {
   int cu_per_xcd, split_max;
   int short_min;
   int ub1, ub2;   // tiles the launches have blocks for (per XCD: (ub + 7) / 8)
+  int by_work;    // 0: no GEMM can reach the size where its tiles are split by work
 };
 
 // Inclusive scan of one int per thread over a block of NT threads: wave scans by shuffles,
@@ -132,15 +133,19 @@ __device__ inline int column_work(int rows, int mt, int per_n, int BM, int TS, i
 // group the m-tiles of each GEMM (a short remainder of at most tall_extra rows rides on the
 // last full tile) and its tiles; the groups' starting tile indices are an exclusive scan.
 // wsum: NT/64 ints of LDS.
+// LDS ints the builder takes besides wsum (the caller's, free while it runs)
+constexpr int kSchedLdsInts = 2 * (kNumXcd + 1) + 6 * G_PAD;
+
 template <int NT>
-__device__ inline void ffn_build_sched(const FfnPrepArgs& a, const int32_t* offsets, int* wsum) {
+__device__ inline void ffn_build_sched(const FfnPrepArgs& a, const int32_t* offsets, int* wsum,
+                                       int* lds) {
   constexpr int PER = (G_MAX + 1 + NT - 1) / NT;   // covers index G (the end of the table)
   const int tid = threadIdx.x;
   const int G = a.El + a.has_shared;
-  __shared__ int xbs[2][kNumXcd + 1];
-  __shared__ int cst[2][G_PAD];   // work before each group, per GEMM
-  __shared__ int colw_s[2][G_PAD], pern_s[2][G_PAD];   // work and tiles of one n-column
-  __shared__ int sst[2][G_PAD];   // first tile of each group, per GEMM
+  int(*xbs)[kNumXcd + 1] = reinterpret_cast<int(*)[kNumXcd + 1]>(lds);
+  int(*cst)[G_PAD] = reinterpret_cast<int(*)[G_PAD]>(lds + 2 * (kNumXcd + 1));   // work
+  int(*colw_s)[G_PAD] = cst + 2;   // work of one n-column (before each group: cst)
+  int(*pern_s)[G_PAD] = cst + 4;   // tiles of one n-column
   int c1[PER], c2[PER], rows_g[PER], mt1[PER], mt2[PER], pn1[PER], pn2[PER];
   int s1 = 0, s2 = 0;
 #pragma unroll
@@ -222,8 +227,6 @@ __device__ inline void ffn_build_sched(const FfnPrepArgs& a, const int32_t* offs
     if (g <= G) {          // start[G] = the total: the binary search's upper end
       a.sc->start1[g] = e1;
       a.sc->start2[g] = e2;
-      sst[0][g] = e1;
-      sst[1][g] = e2;
     }
     e1 += c1[i];
     e2 += c2[i];
@@ -232,12 +235,13 @@ __device__ inline void ffn_build_sched(const FfnPrepArgs& a, const int32_t* offs
   // of blocks (the last round's imbalance is then small against the work moved), else by
   // count, as it is when the launches have no blocks for a split by work.
   const int rounds8 = 8 * kNumXcd * a.cu_per_xcd;
-  const bool bw1 = tot1 >= rounds8, bw2 = tot2 >= rounds8;   // block-uniform
+  const bool bw1 = a.by_work && tot1 >= rounds8;   // block-uniform
+  const bool bw2 = a.by_work && tot2 >= rounds8;
   if (tid < 2 * (kNumXcd + 1)) {
     const int k = tid / (kNumXcd + 1), x = tid % (kNumXcd + 1);
     xbs[k][x] = x == 0 ? 0 : (k == 0 ? tot1 : tot2);
   }
-  if (bw1 || bw2) {
+  if (a.by_work && (bw1 || bw2)) {   // (a kernel argument: a scalar branch)
     int cl1[PER], cl2[PER], w1 = 0, w2 = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -281,7 +285,7 @@ __device__ inline void ffn_build_sched(const FfnPrepArgs& a, const int32_t* offs
                            ? (k == 0 ? a.BM1 : a.BM2) / 64 + 1 : 1;
         const int off = target - cst[k][lo];
         const int m = min((off % colw) / wf, per_n - 1);
-        xbs[k][x] = sst[k][lo] + off / colw * per_n + m;
+        xbs[k][x] = (k == 0 ? a.sc->start1[lo] : a.sc->start2[lo]) + off / colw * per_n + m;
       }
     }
   }
