@@ -423,9 +423,7 @@ __global__ __launch_bounds__(CH) void disp_place(
   // (f) the expert FFN's tile table from the offsets (block-uniform branch)
   if (do_ffn && c == ffn_block) {
     __syncthreads();
-    // the builder's LDS: the (now idle) rank masks
-    static_assert(sizeof(masks) >= kSchedLdsInts * sizeof(int), "builder scratch");
-    ffn_build_sched<CH>(ffn, off_s, wsum, reinterpret_cast<int*>(masks));
+    ffn_build_sched<CH>(ffn, off_s, wsum);
   }
 }
 

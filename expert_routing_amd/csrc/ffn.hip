@@ -33,8 +33,13 @@ namespace {
 __global__ __launch_bounds__(1024) void ffn_prep(FfnPrepArgs a,
                                                  const int32_t* __restrict__ offsets) {
   __shared__ int wsum[16];
-  __shared__ int lds[kSchedLdsInts];
-  ffn_build_sched<1024>(a, offsets, wsum, lds);
+  ffn_build_sched<1024>(a, offsets, wsum);
+}
+
+// One block of 1024 threads: the XCD split by work of the table built before.
+__global__ __launch_bounds__(1024) void ffn_split(FfnPrepArgs a) {
+  __shared__ int wsum[16];
+  ffn_split_by_work<1024>(a, wsum);
 }
 
 // Tile lookup shared by the GEMM kernels. The tile list is dealt to the XCDs in
@@ -1850,6 +1855,10 @@ int launch_ffn(const moe_problem* p, const Dims& d, const void* xp, const int32_
                             &a)) != MOE_OK)
       return rc;
     if ((rc = launch_ffn_prep(a, offsets, st)) != MOE_OK) return rc;
+  }
+  if (a.by_work) {   // a GEMM may be large enough to split its tiles by work
+    hipLaunchKernelGGL(ffn_split, dim3(1), dim3(1024), 0, st, a);
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
   }
   if (ev && hipEventRecord(ev[0], st) != hipSuccess) return MOE_ERR_LAUNCH;
   const FfnSched* sc = a.sc;

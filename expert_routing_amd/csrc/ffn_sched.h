@@ -133,25 +133,17 @@ __device__ inline int column_work(int rows, int mt, int per_n, int BM, int TS, i
 // group the m-tiles of each GEMM (a short remainder of at most tall_extra rows rides on the
 // last full tile) and its tiles; the groups' starting tile indices are an exclusive scan.
 // wsum: NT/64 ints of LDS.
-// LDS ints the builder takes besides wsum (the caller's, free while it runs)
-constexpr int kSchedLdsInts = 2 * (kNumXcd + 1) + 6 * G_PAD;
-
 template <int NT>
-__device__ inline void ffn_build_sched(const FfnPrepArgs& a, const int32_t* offsets, int* wsum,
-                                       int* lds) {
+__device__ inline void ffn_build_sched(const FfnPrepArgs& a, const int32_t* offsets, int* wsum) {
   constexpr int PER = (G_MAX + 1 + NT - 1) / NT;   // covers index G (the end of the table)
   const int tid = threadIdx.x;
   const int G = a.El + a.has_shared;
-  int(*xbs)[kNumXcd + 1] = reinterpret_cast<int(*)[kNumXcd + 1]>(lds);
-  int(*cst)[G_PAD] = reinterpret_cast<int(*)[G_PAD]>(lds + 2 * (kNumXcd + 1));   // work
-  int(*colw_s)[G_PAD] = cst + 2;   // work of one n-column (before each group: cst)
-  int(*pern_s)[G_PAD] = cst + 4;   // tiles of one n-column
-  int c1[PER], c2[PER], rows_g[PER], mt1[PER], mt2[PER], pn1[PER], pn2[PER];
+  int c1[PER], c2[PER];
   int s1 = 0, s2 = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int g = tid * PER + i;
-    c1[i] = c2[i] = rows_g[i] = mt1[i] = mt2[i] = pn1[i] = pn2[i] = 0;
+    c1[i] = c2[i] = 0;
     if (g < G) {
       FfnGroup fg;
       fg.A1s = fg.B1s = fg.B2s = nullptr;
@@ -209,11 +201,6 @@ __device__ inline void ffn_build_sched(const FfnPrepArgs& a, const int32_t* offs
       const int ncol1 = (I + a.BN1 - 1) / a.BN1, ncol2 = (a.h + a.BN2 - 1) / a.BN2;
       c1[i] = per_n[0] * ncol1;
       c2[i] = per_n[1] * ncol2;
-      rows_g[i] = rows;
-      mt1[i] = fg.mt[0];
-      mt2[i] = fg.mt[1];
-      pn1[i] = per_n[0];
-      pn2[i] = per_n[1];
     }
     s1 += c1[i];
     s2 += c2[i];
@@ -231,89 +218,109 @@ __device__ inline void ffn_build_sched(const FfnPrepArgs& a, const int32_t* offs
     e1 += c1[i];
     e2 += c2[i];
   }
-  // The tiles of a GEMM are split among the XCDs by work where that pays: 8 or more rounds
-  // of blocks (the last round's imbalance is then small against the work moved), else by
-  // count, as it is when the launches have no blocks for a split by work.
-  const int rounds8 = 8 * kNumXcd * a.cu_per_xcd;
-  const bool bw1 = a.by_work && tot1 >= rounds8;   // block-uniform
-  const bool bw2 = a.by_work && tot2 >= rounds8;
-  if (tid < 2 * (kNumXcd + 1)) {
-    const int k = tid / (kNumXcd + 1), x = tid % (kNumXcd + 1);
-    xbs[k][x] = x == 0 ? 0 : (k == 0 ? tot1 : tot2);
-  }
-  if (a.by_work && (bw1 || bw2)) {   // (a kernel argument: a scalar branch)
-    int cl1[PER], cl2[PER], w1 = 0, w2 = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      int wf;
-      cl1[i] = column_work(rows_g[i], mt1[i], pn1[i], a.BM1, a.tall_split1, a.short_min, &wf);
-      cl2[i] = column_work(rows_g[i], mt2[i], pn2[i], a.BM2, a.tall_split2, a.short_min, &wf);
-      w1 += c1[i] / max(pn1[i], 1) * cl1[i];   // n-columns x work of one
-      w2 += c2[i] / max(pn2[i], 1) * cl2[i];
-    }
-    int wt1 = 0, wt2 = 0;
-    int f1 = block_inclusive_scan<NT>(w1, wsum, &wt1) - w1;
-    int f2 = block_inclusive_scan<NT>(w2, wsum, &wt2) - w2;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int g = tid * PER + i;
-      if (g <= G) {
-        cst[0][g] = f1;
-        cst[1][g] = f2;
-        colw_s[0][g] = cl1[i];
-        colw_s[1][g] = cl2[i];
-        pern_s[0][g] = pn1[i];
-        pern_s[1][g] = pn2[i];
-      }
-      f1 += c1[i] / max(pn1[i], 1) * cl1[i];
-      f2 += c2[i] / max(pn2[i], 1) * cl2[i];
-    }
-    __syncthreads();
-    // XCD x of GEMM k starts at the tile that holds work offset x*W/8 (one thread each)
-    if (tid < 2 * (kNumXcd + 1)) {
-      const int k = tid / (kNumXcd + 1), x = tid % (kNumXcd + 1);
-      const int wt = k == 0 ? wt1 : wt2;
-      if ((k == 0 ? bw1 : bw2) && x > 0 && x < kNumXcd && wt > 0) {
-        const int target = (int)((int64_t)x * wt / kNumXcd);
-        int lo = 0, hi = G;          // cst[k][lo] <= target < cst[k][hi]
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (cst[k][mid] <= target) lo = mid; else hi = mid;
-        }
-        const int colw = colw_s[k][lo], per_n = pern_s[k][lo];
-        const int wf = ((k == 0 ? a.tall_split1 : a.tall_split2) == 0)
-                           ? (k == 0 ? a.BM1 : a.BM2) / 64 + 1 : 1;
-        const int off = target - cst[k][lo];
-        const int m = min((off % colw) / wf, per_n - 1);
-        xbs[k][x] = (k == 0 ? a.sc->start1[lo] : a.sc->start2[lo]) + off / colw * per_n + m;
-      }
-    }
-  }
-  __syncthreads();
+  // XCD split by count; ffn_split_by_work may replace it (a launch of its own)
   if (tid < 2) {
     const int k = tid, tot = k == 0 ? tot1 : tot2;
-    const int budget = ((k == 0 ? a.ub1 : a.ub2) + kNumXcd - 1) / kNumXcd;
-    bool by_work = k == 0 ? bw1 : bw2;
-    for (int x = 0; x < kNumXcd; ++x) by_work = by_work && xbs[k][x + 1] - xbs[k][x] <= budget;
     const int per = (tot + kNumXcd - 1) / kNumXcd;
-    for (int x = 0; x <= kNumXcd; ++x)
-      a.sc->xb[k][x] = by_work ? xbs[k][x] : (x * per < tot ? x * per : tot);
+    for (int x = 0; x <= kNumXcd; ++x) a.sc->xb[k][x] = x * per < tot ? x * per : tot;
+    a.sc->short_min[k] = 2;
   }
   for (int i = tid; i < 2 * kArriveSlots; i += NT) a.arrive[i] = 0;
   if (tid == 0) {
     a.sc->n_groups = G;
     a.sc->tall_split[0] = a.tall_split1;
     a.sc->tall_split[1] = a.tall_split2;
-    // 64-row short tiles only where the XCDs split the tiles by work: under a split by
-    // count the XCDs without them set the time, and the GEMM measured slower with them
-    a.sc->short_min[0] = bw1 ? a.short_min : 2;
-    a.sc->short_min[1] = bw2 ? a.short_min : 2;
     a.sc->bm[0] = a.BM1;
     a.sc->bm[1] = a.BM2;
     a.sc->cu_per_xcd = a.cu_per_xcd;
     a.sc->split_max = a.split_max;
     a.sc->total1 = tot1;
     a.sc->total2 = tot2;
+  }
+}
+
+// Splits the tiles of each GEMM with 8 or more rounds of blocks among the XCDs by work
+// instead of by count (the last round's imbalance is then small against the work moved),
+// where the launches have blocks for it, and lets those GEMMs take 64-row short tiles
+// (under a split by count the XCDs without them set the time: measured slower). Reads
+// the table ffn_build_sched wrote; one block of NT threads.
+template <int NT>
+__device__ inline void ffn_split_by_work(const FfnPrepArgs& a, int* wsum) {
+  constexpr int PER = (G_MAX + 1 + NT - 1) / NT;
+  __shared__ int xbs[2][kNumXcd + 1];
+  __shared__ int cst[2][G_PAD];                          // work before each group
+  __shared__ int colw_s[2][G_PAD], pern_s[2][G_PAD];   // work and tiles of one n-column
+  const int tid = threadIdx.x;
+  const int G = a.El + a.has_shared;
+  const FfnSched* sc = a.sc;
+  const int tot[2] = {sc->total1, sc->total2};
+  const int rounds8 = 8 * kNumXcd * a.cu_per_xcd;
+  const bool bw[2] = {tot[0] >= rounds8, tot[1] >= rounds8};
+  const int BM[2] = {a.BM1, a.BM2}, TS[2] = {a.tall_split1, a.tall_split2};
+  int cl[2][PER], pn[2][PER], cw[2][PER], w[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int g = tid * PER + i;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      cl[k][i] = pn[k][i] = cw[k][i] = 0;
+      if (g < G) {
+        const FfnGroup& fg = sc->g[g];
+        pn[k][i] = fg.tall[k] ? fg.mt[k] - 1 + TS[k] : fg.mt[k];
+        int wf;
+        cl[k][i] = column_work(fg.rows, fg.mt[k], pn[k][i], BM[k], TS[k], a.short_min, &wf);
+        const int ncol = k == 0 ? (fg.inter + a.BN1 - 1) / a.BN1 : (a.h + a.BN2 - 1) / a.BN2;
+        cw[k][i] = pn[k][i] > 0 ? cl[k][i] * ncol : 0;
+      }
+      w[k] += cw[k][i];
+    }
+  }
+  int wt[2], f[2];
+  f[0] = block_inclusive_scan<NT>(w[0], wsum, &wt[0]) - w[0];
+  f[1] = block_inclusive_scan<NT>(w[1], wsum, &wt[1]) - w[1];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int g = tid * PER + i;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (g <= G) {
+        cst[k][g] = f[k];
+        colw_s[k][g] = cl[k][i];
+        pern_s[k][g] = pn[k][i];
+      }
+      f[k] += cw[k][i];
+    }
+  }
+  __syncthreads();
+  // XCD x of GEMM k starts at the tile that holds work offset x*W/8 (one thread each)
+  if (tid < 2 * (kNumXcd + 1)) {
+    const int k = tid / (kNumXcd + 1), x = tid % (kNumXcd + 1);
+    int b = x == 0 ? 0 : tot[k];
+    if (x > 0 && x < kNumXcd && wt[k] > 0) {
+      const int target = (int)((int64_t)x * wt[k] / kNumXcd);
+      int lo = 0, hi = G;          // cst[k][lo] <= target < cst[k][hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cst[k][mid] <= target) lo = mid; else hi = mid;
+      }
+      const int colw = colw_s[k][lo], per_n = pern_s[k][lo];
+      const int wf = TS[k] == 0 ? BM[k] / 64 + 1 : 1;
+      const int off = target - cst[k][lo];
+      const int m = min((off % colw) / wf, per_n - 1);
+      b = (k == 0 ? sc->start1[lo] : sc->start2[lo]) + off / colw * per_n + m;
+    }
+    xbs[k][x] = b;
+  }
+  __syncthreads();
+  if (tid < 2) {
+    const int k = tid;
+    const int budget = ((k == 0 ? a.ub1 : a.ub2) + kNumXcd - 1) / kNumXcd;
+    bool by_work = bw[k];
+    for (int x = 0; x < kNumXcd; ++x) by_work = by_work && xbs[k][x + 1] - xbs[k][x] <= budget;
+    if (by_work) {
+      for (int x = 0; x <= kNumXcd; ++x) a.sc->xb[k][x] = xbs[k][x];
+      a.sc->short_min[k] = a.short_min;
+    }
   }
 }
 
