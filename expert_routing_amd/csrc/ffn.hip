@@ -1832,7 +1832,9 @@ int ffn_prep_args(const moe_problem* p, const Dims& d, const void* xp, const voi
   ffn_tile_bounds(p, d, *a, &ub1, &ub2);
   a->ub1 = (int)(ub1 < INT32_MAX ? ub1 : INT32_MAX);
   a->ub2 = (int)(ub2 < INT32_MAX ? ub2 : INT32_MAX);
-  a->by_work = (ub1 > ub2 ? ub1 : ub2) >= 8 * kNumXcd * cpx;
+  // (the split differs from one by count only with 256-row tiles: others all weigh one)
+  const int64_t rounds8 = 8 * kNumXcd * cpx;
+  a->by_work = (t1.tall_split == 0 && ub1 >= rounds8) || (t2.tall_split == 0 && ub2 >= rounds8);
   return MOE_OK;
 }
 
