@@ -23,6 +23,11 @@ __device__ __forceinline__ void unpack(const uint4& v, float* f, bool bf16) {
   }
 }
 
+// The token's rows are read in batches of CB_KB: every load of a batch is issued before
+// the batch's accumulations, so a wave keeps CB_KB * CB_CH 16-byte loads in flight per lane.
+// Dropped pairs (dest_row < 0) load nothing; the sum runs in k order either way.
+constexpr int CB_KB = 4;   // rows per batch
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ yp,
                                                       const int32_t* __restrict__ dest_row,
@@ -34,68 +39,76 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  int rows[16];
-  float wk[16];
-  int nk = 0;
-  for (int k = 0; k < K; ++k) {
-    const int d = dest_row[t * K + k];
-    if (d >= 0) { rows[nk] = d; wk[nk] = w[t * K + k]; ++nk; }
-  }
   const bool has_sh = ysh && t >= t0 && t < t1;
-  {
-    const int base = blockIdx.y * 64 * CB_CH;
-    float acc[CB_CH][EPC];
+  const int base = blockIdx.y * 64 * CB_CH;
+  float acc[CB_CH][EPC];
 #pragma unroll
-    for (int u = 0; u < CB_CH; ++u)
+  for (int u = 0; u < CB_CH; ++u)
 #pragma unroll
-      for (int i = 0; i < EPC; ++i) acc[u][i] = 0.f;
-    for (int j = 0; j < nk; ++j) {
-      const uint4* src = yp + (int64_t)rows[j] * row_chunks;
-      uint4 v[CB_CH];
+    for (int i = 0; i < EPC; ++i) acc[u][i] = 0.f;
+  for (int k0 = 0; k0 < K; k0 += CB_KB) {
+    int d[CB_KB];
+    float wk[CB_KB];
+    uint4 v[CB_KB][CB_CH];
 #pragma unroll
-      for (int u = 0; u < CB_CH; ++u) {
-        const int i = base + u * 64 + lane;
-        v[u] = i < row_chunks ? src[i] : uint4{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int u = 0; u < CB_CH; ++u) {
-        float f[EPC];
-        unpack(v[u], f, BF16);
-#pragma unroll
-        for (int i = 0; i < EPC; ++i) acc[u][i] = fmaf(wk[j], f[i], acc[u][i]);
-      }
+    for (int j = 0; j < CB_KB; ++j) {
+      d[j] = k0 + j < K ? dest_row[t * K + k0 + j] : -1;
+      wk[j] = k0 + j < K ? w[t * K + k0 + j] : 0.f;
     }
-    if (has_sh) {
-      const uint4* src = ysh + (t - t0) * row_chunks;
 #pragma unroll
-      for (int u = 0; u < CB_CH; ++u) {
-        const int i = base + u * 64 + lane;
-        if (i < row_chunks) {
-          float f[EPC];
-          unpack(src[i], f, BF16);
+    for (int j = 0; j < CB_KB; ++j) {
+      if (d[j] >= 0) {
+        const uint4* src = yp + (int64_t)d[j] * row_chunks;
 #pragma unroll
-          for (int q = 0; q < EPC; ++q) acc[u][q] += f[q];
+        for (int u = 0; u < CB_CH; ++u) {
+          const int i = base + u * 64 + lane;
+          v[j][u] = i < row_chunks ? src[i] : uint4{0, 0, 0, 0};
         }
       }
     }
 #pragma unroll
+    for (int j = 0; j < CB_KB; ++j) {
+      if (d[j] >= 0) {
+#pragma unroll
+        for (int u = 0; u < CB_CH; ++u) {
+          float f[EPC];
+          unpack(v[j][u], f, BF16);
+#pragma unroll
+          for (int i = 0; i < EPC; ++i) acc[u][i] = fmaf(wk[j], f[i], acc[u][i]);
+        }
+      }
+    }
+  }
+  if (has_sh) {
+    const uint4* src = ysh + (t - t0) * row_chunks;
+#pragma unroll
     for (int u = 0; u < CB_CH; ++u) {
       const int i = base + u * 64 + lane;
-      if (i >= row_chunks) continue;
-      uint4 o;
-      if (BF16) {
-        uint32_t p[4];
+      if (i < row_chunks) {
+        float f[EPC];
+        unpack(src[i], f, BF16);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          p[q] = (uint32_t)f32_to_bf16(acc[u][2 * q]) |
-                 ((uint32_t)f32_to_bf16(acc[u][2 * q + 1]) << 16);
-        o = uint4{p[0], p[1], p[2], p[3]};
-      } else {
-        o = uint4{__float_as_uint(acc[u][0]), __float_as_uint(acc[u][1]),
-                  __float_as_uint(acc[u][2]), __float_as_uint(acc[u][3])};
+        for (int q = 0; q < EPC; ++q) acc[u][q] += f[q];
       }
-      y[t * row_chunks + i] = o;
     }
+  }
+#pragma unroll
+  for (int u = 0; u < CB_CH; ++u) {
+    const int i = base + u * 64 + lane;
+    if (i >= row_chunks) continue;
+    uint4 o;
+    if (BF16) {
+      uint32_t p[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        p[q] = (uint32_t)f32_to_bf16(acc[u][2 * q]) |
+               ((uint32_t)f32_to_bf16(acc[u][2 * q + 1]) << 16);
+      o = uint4{p[0], p[1], p[2], p[3]};
+    } else {
+      o = uint4{__float_as_uint(acc[u][0]), __float_as_uint(acc[u][1]),
+                __float_as_uint(acc[u][2]), __float_as_uint(acc[u][3])};
+    }
+    y[t * row_chunks + i] = o;
   }
 }
 
