@@ -48,6 +48,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (the MX-FP8 GEMMs)
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+NUM_XCD = 8                 # MI355X: 8 XCDs of 32 CUs (GRBM_GUI_ACTIVE sums over them)
 RIDGE_BF16 = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per byte
 ALL = ["mixtral_prefill", "dsv3_ep8", "skew_cap1", "skew_nodrop", "dsv3_decode"]
 FLUSH_BYTES = 1 << 30       # written before each flushed step: > L2 (8 x 4 MB) + 256 MB MALL
@@ -57,7 +58,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 # kernel name prefix -> stage of the layer
 STAGE_OF = [("router_", "route"), ("select_", "route"), ("logits_", "route"),
             ("disp_", "dispatch"), ("mx_quant", "dispatch"), ("ffn_prep", "ffn_prep"),
-            ("ffn_gate_up", "ffn_gate_up"),
+            ("ffn_split", "ffn_prep"), ("ffn_gate_up", "ffn_gate_up"),
             ("ffn_down", "ffn_down"), ("combine", "combine")]
 
 
@@ -156,6 +157,118 @@ def summarize_traffic(fetch_csv, write_csv, workload):
     with open(traffic_file(workload), "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
+
+
+PROFILE_SQ = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_LDS SQ_LDS_IDX_ACTIVE "
+              "SQ_LDS_BANK_CONFLICT SQ_WAVE_CYCLES SQ_WAIT_INST_LDS GRBM_GUI_ACTIVE")
+
+
+def summarize_profile(kt_trace_csv, kt_bench_log, sq_csv, workload, dtype, suffix):
+    """profiles/<workload>_<dtype>.md from three rocprofv3 runs of this script: the kernel
+    trace (--kernel-trace --stats; its kernel_trace.csv and the bench line the profiled run
+    printed), and the MFMA / LDS counters of the two GEMMs (PROFILE_SQ, one --pmc run);
+    the HBM traffic table comes from profiles/traffic_<workload><suffix>.json
+    (--summarize-traffic on the same source)."""
+    import csv
+
+    args = f"--workload {workload} --dtype {dtype} --no-cpu-baseline --no-flush"
+    cmds = [
+        f"rocprofv3 --kernel-trace --stats -f csv -d <out>/kt -o kt -- python3 <repo>/bench.py "
+        f"{args} --steps 10 --warmup 3",
+        f"rocprofv3 --pmc FETCH_SIZE -f csv -d <out>/fetch -o fetch -- python3 <repo>/bench.py "
+        f"{args} --steps 2 --warmup 1 --calibrate-copy",
+        f"rocprofv3 --pmc WRITE_SIZE -f csv -d <out>/write -o write -- python3 <repo>/bench.py "
+        f"{args} --steps 2 --warmup 1 --calibrate-copy",
+        f"rocprofv3 --pmc {PROFILE_SQ} --kernel-include-regex \"ffn_gate_up|ffn_down\" -f csv "
+        f"-d <out>/sq -o sq -- python3 <repo>/bench.py {args} --steps 2 --warmup 1",
+        f"python3 <repo>/bench.py --summarize-traffic <out>/fetch/fetch_counter_collection.csv "
+        f"<out>/write/write_counter_collection.csv --workload {workload} --dtype {dtype}",
+        f"python3 <repo>/bench.py --summarize-profile <out>/kt/kt_kernel_trace.csv "
+        f"<kernel-trace run's stdout> <out>/sq/sq_counter_collection.csv --workload {workload} "
+        f"--dtype {dtype}",
+    ]
+    # per-dispatch durations from the first router kernel on (the MX-FP8 weights' one-time
+    # quantisation and the input generation come before the layer calls)
+    disp = []
+    with open(kt_trace_csv) as fh:
+        for r in csv.DictReader(fh):
+            if stage_of(r["Kernel_Name"]) is not None:
+                disp.append((int(r["Dispatch_Id"]), kernel_base_name(r["Kernel_Name"]),
+                             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    first = min(d for d, n, _ in disp if stage_of(n) == "route")
+    per = {}
+    for d, n, us in disp:
+        if d >= first:
+            per.setdefault(n, []).append(us)
+    kern = [(n, len(v), sum(v) / len(v), min(v), max(v)) for n, v in per.items()]
+    kern.sort(key=lambda k: -k[1] * k[2])
+    mean_us = {k[0]: k[2] for k in kern}
+    line = None
+    with open(kt_bench_log) as fh:
+        for ln in fh:
+            if ln.startswith("{"):
+                line = json.loads(ln)
+    sq = {}
+    with open(sq_csv) as fh:
+        for r in csv.DictReader(fh):
+            n = kernel_base_name(r["Kernel_Name"])
+            sq.setdefault(n, {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    calls = max((k[1] for k in kern if stage_of(k[0]) == "combine"), default=0)
+    out = [f"# Kernel times and counters: {workload} ({dtype})", "",
+           "Commands (GPU box, from the repository root; output directory of your choice;",
+           "`cd /tmp && export TMPDIR=/tmp` first):", "", "```", *cmds, "```", ""]
+    out.append("The bench passes no xp (dispatch builds only the layout; the gate/up GEMM reads "
+               "x through row_src); " + ("the expert weights are MX-FP8, quantised once before "
+                                         "timing (quantize_mx, omitted below)." if dtype == "mxfp8"
+                                         else "bf16 expert weights are packed once before timing "
+                                         "(pack_weights, omitted below)."))
+    out.append(f"The kernel-trace run makes {calls} layer calls (3 warm-up, 10 timed, 10 traced). "
+               "Library kernels of the layer calls (from the first router launch on):")
+    out += ["", "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    out += [f"| {n} | {c} | {a:.2f} | {lo:.2f} | {hi:.2f} |" for n, c, a, lo, hi in kern]
+    if line:
+        out += ["", "bench.py's own HIP-event stage times in the same profiled process (us, "
+                f"event-pair overhead of {line['event_pair_us']} us removed): "
+                f"{json.dumps(line['stages_us'])}; ms_per_step {line['ms_per_step']:.4f}, "
+                f"value {line['value']:.4g} tokens/s.",
+                f"Roofline object ({line['roofline']['kernel'].split(' (')[0]}): achieved "
+                f"{line['roofline']['achieved']:.1f} {line['roofline']['unit']} of "
+                f"{line['roofline']['peak']} ({line['roofline']['frac']:.3f})."]
+    out += ["", "## MFMA and LDS counters (per launch, averaged over the run's launches)", "",
+            "| kernel | GRBM_GUI_ACTIVE (sum of 8 XCDs) | SQ_VALU_MFMA_BUSY_CYCLES | MFMA busy "
+            "fraction | SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE | clock under load (GHz) |",
+            "|---|---|---|---|---|---|"]
+    for n in sorted(sq):
+        c = {k: sum(v) / len(v) for k, v in sq[n].items()}
+        grbm, busy = c.get("GRBM_GUI_ACTIVE", 0.0), c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        frac = busy / (1024 * grbm / NUM_XCD) if grbm else 0.0
+        conf = (c.get("SQ_LDS_BANK_CONFLICT", 0.0) / c["SQ_LDS_IDX_ACTIVE"]
+                if c.get("SQ_LDS_IDX_ACTIVE") else 0.0)
+        ghz = grbm / NUM_XCD / (mean_us[n] * 1e3) if n in mean_us and mean_us[n] else 0.0
+        out.append(f"| {n} | {grbm:.4g} | {busy:.4g} | {frac:.3f} | {conf:.3f} | {ghz:.2f} |")
+    out += ["", "MFMA busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / "
+            "8 XCDs); the clock is GRBM_GUI_ACTIVE / 8 over the kernel's mean trace duration."]
+    try:
+        with open(traffic_file(workload + suffix)) as fh:
+            t = json.load(fh)
+    except OSError:
+        t = None
+    if t:
+        cal = t["calibration"]
+        out += ["", "## HBM traffic per layer call (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled)", "",
+                f"Each counter is scaled by its reading for a {cal['copy_bytes'] >> 20} MiB "
+                f"device copy in the same run: FETCH_SIZE reads {cal['fetch_scale']:.4f} of the "
+                f"copy's bytes, WRITE_SIZE {cal['write_scale']:.4f}. Layer calls per run: "
+                f"{t['layer_calls_per_run']}. Source hash: {t['source_sha']} (bench.py reports "
+                "roofline.traffic only while it matches).", "",
+                "| stage | fetched (MB) | written (MB) |", "|---|---|---|"]
+        out += [f"| {s} | {v['fetch_bytes'] / 1e6:.2f} | {v['write_bytes'] / 1e6:.2f} |"
+                for s, v in sorted(t["stages"].items())]
+    path = os.path.join(PROFILES, f"{workload}_{dtype}.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(out) + "\n")
+    print("wrote", path)
 
 
 def cpu_baseline(cfg, inp, ids_gpu, min_seconds=10.0):
@@ -516,6 +629,8 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one device copy of a known size (counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-profile", nargs=3,
+                    metavar=("KERNEL_TRACE_CSV", "BENCH_LOG", "SQ_CSV"))
     ap.add_argument("--dtype", choices=["bf16", "mxfp8"], default="bf16",
                     help="expert weights and GEMM operands: bf16 (the workloads' dtype), or "
                          "MX-FP8 (E4M3 with E8M0 block scales; activations stay bf16)")
@@ -529,6 +644,10 @@ def main():
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic,
                           workload=args.workload + variant_suffix(args, "bf16"))
+        return
+    if args.summarize_profile:
+        summarize_profile(*args.summarize_profile, workload=args.workload, dtype=args.dtype,
+                          suffix=variant_suffix(args, "bf16"))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
