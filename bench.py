@@ -271,6 +271,46 @@ def summarize_profile(kt_trace_csv, kt_bench_log, sq_csv, workload, dtype, suffi
     print("wrote", path)
 
 
+def measure_peaks(torch, reps=20):
+    """Practical ceilings of this GPU, for context beside the published peaks the roofline
+    fractions use: a plain bf16 GEMM through torch.matmul (hipBLASLt) at the Mixtral gate/up
+    shape (all 8192 routed rows against one 28672 x 4096 weight), the same GEMM per 1024-row
+    expert, and a 1 GiB device-to-device copy. Medians of `reps` runs, each timed with HIP
+    events."""
+    dev = "cuda"
+
+    def timed(fn):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        fn()
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in ev)[reps // 2] * 1e-3   # s
+
+    out = {}
+    g = torch.Generator(device=dev).manual_seed(0)
+    for name, M in (("gemm_8192x28672x4096", 8192), ("gemm_1024x28672x4096", 1024)):
+        a = torch.randn(M, 4096, device=dev, dtype=torch.bfloat16, generator=g)
+        w = torch.randn(4096, 28672, device=dev, dtype=torch.bfloat16, generator=g)
+        t = timed(lambda: torch.matmul(a, w))
+        out[name] = {"TFLOPs": 2.0 * M * 28672 * 4096 / t / 1e12,
+                     "frac_of_published": 2.0 * M * 28672 * 4096 / t / 1e12 / PEAK_BF16_TFLOPS}
+        del a, w
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    t = timed(lambda: dst.copy_(src))
+    out["copy_1GiB"] = {"GBps": 2.0 * (1 << 30) / t / 1e9,
+                        "frac_of_published": 2.0 * (1 << 30) / t / 1e9 / PEAK_HBM_GBS}
+    del src, dst
+    return {"practical_peaks": out, "published": {"bf16_TFLOPs": PEAK_BF16_TFLOPS,
+                                                   "hbm_GBps": PEAK_HBM_GBS}}
+
+
 def cpu_baseline(cfg, inp, ids_gpu, min_seconds=10.0):
     """The fp64 oracle, untuned, on the whole workload, called repeatedly until at least
     min_seconds have passed; its routing also gives the near-tie count, the number of
@@ -629,6 +669,9 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one device copy of a known size (counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--measure-peaks", action="store_true",
+                    help="print one JSON line of this GPU's practical ceilings (a hipBLASLt "
+                         "bf16 GEMM, a device copy) and exit")
     ap.add_argument("--summarize-profile", nargs=3,
                     metavar=("KERNEL_TRACE_CSV", "BENCH_LOG", "SQ_CSV"))
     ap.add_argument("--dtype", choices=["bf16", "mxfp8"], default="bf16",
@@ -662,6 +705,9 @@ def main():
     import expert_routing_amd as moe
 
     torch.cuda.set_device(0)
+    if args.measure_peaks:
+        print(json.dumps(measure_peaks(torch)), flush=True)
+        return
     names = ALL if args.workload == "all" else [args.workload]
     for name in names:
         print(json.dumps(run_workload(name, args, moe, torch, np)), flush=True)
