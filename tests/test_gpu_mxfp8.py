@@ -410,3 +410,72 @@ def test_mx_noalloc_equals_forward():
         torch.cuda.synchronize()
         for k in ("topk_ids", "topk_w", "offsets", "row_src", "y"):
             assert torch.equal(want[k], got[k]), (T, k)
+
+
+@pytest.mark.parametrize("name", ["mixtral_prefill", "dsv3_ep8", "skew_nodrop", "dsv3_decode"])
+def test_mx_full_config(name):
+    """The workloads' full sizes on MX-FP8 expert weights, as bench.py runs them (weights
+    quantised on the GPU by moe_quantize_mx, bit-exact to the oracle's quantiser above; no
+    xp): the layout equals the oracle's dispatch of the GPU's ids, and the first, middle and
+    last rows of a spread of experts (and of the shared expert's block) meet the per-element
+    bound against the fp64 FFN on the dequantised operands."""
+    cfg = CONFIGS[name]
+    print(f"[case] mx full {name}", flush=True)
+    inp = gpu_inputs(cfg)
+    p = moe.problem_from_config(cfg)
+    p.act_dtype = moe.DTYPE["mxfp8"]
+    b = moe.alloc_buffers(p, "cuda")
+    q = {}
+    for k in ("w13", "w2", "w13_sh", "w2_sh"):
+        w = inp[k]
+        if w is None:
+            q[k] = q[k + "_scale"] = None
+            continue
+        c, s = moe.quantize_mx(w.reshape(-1, w.shape[-1]))
+        q[k] = c.reshape(w.shape)
+        q[k + "_scale"] = s.reshape(w.shape[:-1] + (w.shape[-1] // 32,))
+    t = dict(b)
+    t.update(x=inp["x"], w_router=inp["w_router"], bias=inp["bias"], xp=None,
+             **{k: q[k] for k in q})
+    moe.moe_forward(p, t, b["ws"])
+    torch.cuda.synchronize()
+    ids = np_(b["topk_ids"]).astype(np.int64)
+    d = oracle.dispatch(ids, E=cfg.E, n_ep=cfg.n_ep, ep_rank=cfg.ep_rank,
+                        capacity_factor=cfg.capacity_factor, pad=cfg.pad,
+                        h=cfg.h + cfg.h // 32, dtype_size=1)
+    np.testing.assert_array_equal(np_(b["offsets"]), d.offsets)
+    np.testing.assert_array_equal(np_(b["dest_row"]), d.dest_row)
+    if b["send_bytes"] is not None:
+        np.testing.assert_array_equal(np_(b["send_bytes"]), d.send_bytes)
+
+    def dq(k, e=None):
+        c, s = (q[k], q[k + "_scale"]) if e is None else (q[k][e], q[k + "_scale"][e])
+        return F.mx_dequantize(c.cpu().numpy(), s.cpu().numpy())
+
+    def x_dq(toks):
+        xq, xs = F.mx_quantize_rows(inp["x"][torch.as_tensor(toks).cuda()].cpu().double().numpy())
+        return F.mx_dequantize(xq, xs)
+
+    off = d.offsets
+    experts = [e for e in range(cfg.E_local) if off[e + 1] > off[e]]
+    rng = np.random.default_rng(2)
+    pick = sorted(rng.choice(experts, size=min(4, len(experts)), replace=False).tolist())
+    worst = 0.0
+    for e in pick:
+        lo, hi = int(off[e]), int(off[e + 1])
+        rows = sorted({lo, (lo + hi) // 2, hi - 1})
+        y, bound, _ = expert_rows_bound(x_dq(d.row_src[rows] // cfg.K), dq("w13", e),
+                                        dq("w2", e), cfg.h)
+        err = np.abs(np_(b["yp"][rows]).astype(np.float64) - y)
+        worst = max(worst, float((err / bound).max()))
+        assert (err <= bound).all(), f"expert {e}: yp beyond the bound"
+    if cfg.n_shared:
+        tpr = cfg.T // cfg.n_ep
+        t0 = cfg.ep_rank * tpr
+        rows = [0, tpr // 2, tpr - 1]
+        y, bound, _ = expert_rows_bound(x_dq([t0 + r for r in rows]), dq("w13_sh"), dq("w2_sh"),
+                                        cfg.h)
+        err = np.abs(np_(b["y_sh"][rows]).astype(np.float64) - y)
+        worst = max(worst, float((err / bound).max()))
+        assert (err <= bound).all(), "y_sh beyond the bound"
+    print(f"[parity] mx full {name}: experts {pick}, worst err/bound {worst:.3f}", flush=True)

@@ -116,7 +116,8 @@ def _f64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-@pytest.mark.parametrize("name", ["mixtral_prefill", "dsv3_ep8", "skew_nodrop", "dsv3_decode"])
+@pytest.mark.parametrize("name", ["mixtral_prefill", "dsv3_ep8", "skew_cap1", "skew_nodrop",
+                                  "dsv3_decode"])
 def test_packed_full_config(name):
     """The workloads' full sizes: sampled rows of a spread of experts and the whole block
     of the largest one against fp64, and the bench's gathered run bit-identical."""
