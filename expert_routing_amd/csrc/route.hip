@@ -562,6 +562,7 @@ __global__ __launch_bounds__(64 * RS_NW) void router_small_e(
 // in slab order.
 constexpr int GV_EB = 16;
 constexpr int GV_MAXI = 16;   // float4 steps per thread: kslice <= 16 * 64 = 1024
+constexpr int GV_XB = 8;      // x chunks per thread loaded together when staging
 
 template <int TB>
 __global__ __launch_bounds__(256) void router_gemv(const bf16_t* __restrict__ x,
@@ -587,13 +588,25 @@ __global__ __launch_bounds__(256) void router_gemv(const bf16_t* __restrict__ x,
     const int k0 = 4 * kl + 64 * i;
     wv[i] = *reinterpret_cast<const float4*>(wr + (k0 < klen ? k0 : 4 * kl));
   }
-  // stage x[0..T)[kb, kb + klen) as 16-byte chunks; rows past T are zero
-  const int cpr = klen / 8;
-  for (int i = tid; i < TB * cpr; i += 256) {
-    const int t = i / cpr, c = i % cpr;
-    uint4 v = uint4{0, 0, 0, 0};
-    if (t < T) v = *reinterpret_cast<const uint4*>(x + (size_t)t * h + kb + c * 8);
-    *reinterpret_cast<uint4*>(xs + (size_t)t * kslice + c * 8) = v;
+  // stage x[0..T)[kb, kb + klen) as 16-byte chunks; rows past T are zero. A thread's
+  // chunks are loaded in batches of GV_XB, every load of a batch issued before its LDS
+  // stores (one memory round trip per batch rather than per chunk)
+  const int cpr = klen / 8, nchunk = TB * cpr;
+  for (int base = tid; base < nchunk; base += 256 * GV_XB) {
+    uint4 v[GV_XB];
+#pragma unroll
+    for (int j = 0; j < GV_XB; ++j) {
+      const int i = base + 256 * j;
+      v[j] = uint4{0, 0, 0, 0};
+      if (i < nchunk && i / cpr < T)
+        v[j] = *reinterpret_cast<const uint4*>(x + (size_t)(i / cpr) * h + kb + (i % cpr) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < GV_XB; ++j) {
+      const int i = base + 256 * j;
+      if (i < nchunk)
+        *reinterpret_cast<uint4*>(xs + (size_t)(i / cpr) * kslice + (i % cpr) * 8) = v[j];
+    }
   }
   __syncthreads();
   float acc[TB];
@@ -654,14 +667,15 @@ __global__ __launch_bounds__(256) void select_topk(const float* __restrict__ log
   const bool active = t < T;
   // partial logits of the nsplit slabs added in slab order; every load of a chunk of 8
   // slabs is issued before the additions (lanes past E read a valid address)
+  constexpr int SB = 8;
   const int64_t tr = active ? t : 0;
   float L[KPL];
 #pragma unroll
   for (int j = 0; j < KPL; ++j) L[j] = 0.f;
-  for (int z0 = 0; z0 < nsplit; z0 += 8) {
-    float v[8][KPL];
+  for (int z0 = 0; z0 < nsplit; z0 += SB) {
+    float v[SB][KPL];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < SB; ++u)
 #pragma unroll
       for (int j = 0; j < KPL; ++j) {
         const int e = j * 64 + lane;
@@ -670,7 +684,7 @@ __global__ __launch_bounds__(256) void select_topk(const float* __restrict__ log
                       : 0.f;
       }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < SB; ++u)
 #pragma unroll
       for (int j = 0; j < KPL; ++j)
         if (z0 + u < nsplit) L[j] = (z0 + u == 0) ? v[u][j] : L[j] + v[u][j];

@@ -59,6 +59,12 @@ SMALL = {
     "bf16_e16_fused": CONFIGS["skew_nodrop"].with_(T=333, h=320, E=16, K=3, inter=64),
     # the small-batch router with 64-token accumulators, group-limited sigmoid scoring
     "bf16_gemv_t64": CONFIGS["dsv3_decode"].with_(T=64, h=512, E=32, inter=64),
+    # the small-batch router leaving 16 slabs of partial logits, which selection loads as
+    # one chunk (one and two keys per lane)
+    "bf16_gemv_slabs16": CONFIGS["dsv3_decode"].with_(T=20, h=1024, E=32, K=4, n_groups=4,
+                                                      topk_groups=2, inter=64),
+    "bf16_gemv_slabs16_e128": CONFIGS["dsv3_decode"].with_(T=16, h=1024, E=128, K=8,
+                                                           inter=64),
 }
 
 
