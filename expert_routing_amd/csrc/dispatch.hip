@@ -22,6 +22,17 @@ namespace {
 
 constexpr int CH = kDispatchChunk;   // tokens per chunk (= threads per block)
 
+// The K expert ids of token t (K <= 16; -1 past T, past K and for ids outside [0, E)), every
+// load issued before any is used, so they share one memory round trip.
+__device__ __forceinline__ void load_pair_ids(const int32_t* __restrict__ ids, int64_t t,
+                                              int64_t T, int K, int E, int (&ev)[16]) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) ev[k] = (k < K && t < T) ? ids[t * K + k] : -1;
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    if (ev[k] < 0 || ev[k] >= E) ev[k] = -1;
+}
+
 __global__ __launch_bounds__(CH) void disp_hist(const int32_t* __restrict__ ids,
                                                 int32_t* __restrict__ chunk_counts, int T,
                                                 int K, int E) {
@@ -30,12 +41,11 @@ __global__ __launch_bounds__(CH) void disp_hist(const int32_t* __restrict__ ids,
   for (int e = threadIdx.x; e < E; e += CH) cnt[e] = 0;
   __syncthreads();
   const int64_t t = (int64_t)c * CH + threadIdx.x;
-  if (t < T) {
-    for (int k = 0; k < K; ++k) {
-      const int e = ids[t * K + k];
-      if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
-    }
-  }
+  int ev[16];
+  load_pair_ids(ids, t, T, K, E, ev);
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    if (ev[k] >= 0) atomicAdd(&cnt[ev[k]], 1);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += CH) chunk_counts[(size_t)c * E + e] = cnt[e];
 }
@@ -109,12 +119,10 @@ __global__ __launch_bounds__(CH) void disp_layout(
     for (int i = tid; i < lds_span * N; i += CH) ncount[i] = 0;
   __syncthreads();
   int ev[16];
-  for (int k = 0; k < K; ++k) {
-    int e = t < T ? ids[t * K + k] : -1;
-    if (e < 0 || e >= E) e = -1;
-    ev[k] = e;
-    if (e >= 0) atomicOr(&masks[wave][e], 1ull << lane);
-  }
+  load_pair_ids(ids, t, T, K, E, ev);
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    if (k < K && ev[k] >= 0) atomicOr(&masks[wave][ev[k]], 1ull << lane);
   __syncthreads();
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int64_t src_rank = (send_bytes && tpr > 0) ? t / tpr : 0;
@@ -171,12 +179,11 @@ __global__ __launch_bounds__(CH) void disp_count(const int32_t* __restrict__ ids
   for (int e = threadIdx.x; e < E; e += CH) cnt[e] = 0;
   __syncthreads();
   const int64_t t = (int64_t)c * CH + threadIdx.x;
-  if (t < T) {
-    for (int k = 0; k < K; ++k) {
-      const int e = ids[t * K + k];
-      if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
-    }
-  }
+  int ev[16];
+  load_pair_ids(ids, t, T, K, E, ev);
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    if (ev[k] >= 0) atomicAdd(&cnt[ev[k]], 1);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += CH) chunk_counts[(size_t)c * E + e] = cnt[e];
 }
@@ -318,12 +325,10 @@ __global__ __launch_bounds__(CH) void disp_place(
   const int64_t tfirst = (int64_t)c * CH;
   const int64_t t = tfirst + tid;
   int ev[16];
-  for (int k = 0; k < K; ++k) {
-    int e = t < T ? ids[t * K + k] : -1;
-    if (e < 0 || e >= E) e = -1;
-    ev[k] = e;
-    if (e >= 0) atomicOr(&masks[wave][e], 1ull << lane);
-  }
+  load_pair_ids(ids, t, T, K, E, ev);
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    if (k < K && ev[k] >= 0) atomicOr(&masks[wave][ev[k]], 1ull << lane);
   __syncthreads();
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int64_t src_rank = (send_mode == kSendAtomic && tpr > 0) ? t / tpr : 0;
@@ -388,8 +393,17 @@ __global__ __launch_bounds__(CH) void disp_place(
       const int r0 = (int)((int64_t)p * n_rows / LPE);
       const int r1 = (int)((int64_t)(p + 1) * n_rows / LPE);
       int sum = 0;
-      if (ok)
-        for (int r = r0; r < r1; ++r) sum += chunk_counts[(size_t)r * E + e];
+      if (ok) {
+        int r = r0;
+        for (; r + 8 <= r1; r += 8) {   // eight loads in flight
+          int v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = chunk_counts[(size_t)(r + u) * E + e];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) sum += v[u];
+        }
+        for (; r < r1; ++r) sum += chunk_counts[(size_t)r * E + e];
+      }
       int incl = sum;
       for (int off = 1; off < LPE; off <<= 1) {
         const int v = __shfl_up(incl, off, LPE);
@@ -398,21 +412,30 @@ __global__ __launch_bounds__(CH) void disp_place(
       if (ok) {
         int before = incl - sum, cur = -1, acc = 0;
         const int dst = e / El;
-        for (int r = r0; r < r1; ++r) {
-          const int v = chunk_counts[(size_t)r * E + e];
-          int kept = v;
-          if (cap >= 0) {
-            const int64_t room = cap - before;
-            kept = room <= 0 ? 0 : (room < v ? (int)room : v);
+        for (int rb = r0; rb < r1; rb += 8) {   // rows in chunks of eight loads in flight
+          int vb[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            vb[u] = rb + u < r1 ? chunk_counts[(size_t)(rb + u) * E + e] : 0;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int r = rb + u;
+            if (r >= r1) break;
+            const int v = vb[u];
+            int kept = v;
+            if (cap >= 0) {
+              const int64_t room = cap - before;
+              kept = room <= 0 ? 0 : (room < v ? (int)room : v);
+            }
+            before += v;
+            const int src = (int)(((int64_t)r * gtok) / tpr);
+            if (src != cur) {
+              if (acc > 0) atomicAdd(&ncount[cur * N + dst], acc);
+              cur = src;
+              acc = 0;
+            }
+            acc += kept;
           }
-          before += v;
-          const int src = (int)(((int64_t)r * gtok) / tpr);
-          if (src != cur) {
-            if (acc > 0) atomicAdd(&ncount[cur * N + dst], acc);
-            cur = src;
-            acc = 0;
-          }
-          acc += kept;
         }
         if (acc > 0) atomicAdd(&ncount[cur * N + dst], acc);
       }
@@ -503,12 +526,10 @@ __global__ __launch_bounds__(CH) void disp_stats(
   for (int i = tid; i < (CH / 64) * E; i += CH) masks[i / E][i % E] = 0ull;
   __syncthreads();
   int ev[16];
-  for (int k = 0; k < K; ++k) {
-    int e = t < T ? ids[t * K + k] : -1;
-    if (e < 0 || e >= E) e = -1;
-    ev[k] = e;
-    if (e >= 0) atomicOr(&masks[wave][e], 1ull << lane);
-  }
+  load_pair_ids(ids, t, T, K, E, ev);
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    if (k < K && ev[k] >= 0) atomicOr(&masks[wave][ev[k]], 1ull << lane);
   __syncthreads();
   if (t >= T) return;
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
